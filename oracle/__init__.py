@@ -1,0 +1,177 @@
+"""CPU oracle for 8-bit quantized attention — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product (the HIP library and its
+binding) never does.  The arithmetic lives in ``oracle.c`` (plain loops, float64
+except where a quantisation decision is defined on float32), built here with
+gcc and loaded with ctypes.  Nothing in this package is shared with the HIP
+path.
+
+Every function follows the method as the SageAttention pages describe it
+(K smoothing, per-block INT8 Q/K, FP8 E4M3 P and V with two-level
+accumulation); the readings taken where the pages are silent are listed in the
+header of ``oracle.c``.  All functions here are pinned by ``tests/test_oracle_*``
+against facts fixed by the mathematics or by independent libraries.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+# Block parameters of the spec (one INT8 scale per BQ query rows and per BK
+# keys; one P scale per row per BN keys).
+BQ, BK, BN = 128, 64, 128
+# Relative distance to an E4M3 rounding midpoint within which both codes of P
+# count as correct: the HIP path evaluates 2^x with a hardware exp2 whose error
+# is about one float32 ulp (2^-23); 2^-20 leaves a factor 8 of margin.
+TAU = 2.0 ** -20
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc, OpenMP, no fast-math)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-fPIC", "-shared", SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i, f, dd, l = ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_long
+        lib.oracle_e4m3_decode.restype = dd
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [dd]
+        lib.oracle_e4m3_encode_array.argtypes = [P, l, P]
+        lib.oracle_e4m3_decode_array.argtypes = [P, l, P]
+        lib.oracle_quantize.argtypes = [P, P, P, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
+        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, f, dd, P, l,
+                                      P, P, P, P]
+        lib.oracle_attn_f64.argtypes = [P, P, P, i, i, i, i, i, i, dd, P, l, P]
+        lib.oracle_num_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def to_f32(t) -> np.ndarray:
+    """Exact up-conversion of an fp16/bf16 tensor to a float32 numpy array."""
+    if isinstance(t, torch.Tensor):
+        return np.ascontiguousarray(t.detach().cpu().to(torch.float32).numpy())
+    return np.ascontiguousarray(np.asarray(t, dtype=np.float32))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, np.uint8)
+    _load().oracle_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(c, dtype=np.uint8))
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True) -> dict:
+    """The prep step on [B,H,N,d] inputs.  Returns codes in the plain logical
+    layout [B,H,N,d] and the scales (see oracle_quantize in oracle.c)."""
+    q, k, v = to_f32(q), to_f32(k), to_f32(v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    r = dict(
+        q_i8=np.empty((B, Hq, N, d), np.int8), q_scale=np.empty((B, Hq, nqb), np.float32),
+        k_i8=np.empty((B, Hkv, N, d), np.int8), k_scale=np.empty((B, Hkv, nkb), np.float32),
+        k_mean=np.empty((B, Hkv, d), np.float32), v_fp8=np.empty((B, Hkv, N, d), np.uint8),
+        v_scale=np.empty((B, Hkv, d), np.float32))
+    _load().oracle_quantize(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, bq, bk, int(smooth),
+                            _ptr(r["q_i8"]), _ptr(r["q_scale"]), _ptr(r["k_i8"]),
+                            _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(r["v_fp8"]),
+                            _ptr(r["v_scale"]))
+    r.update(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, bq=bq, bk=bk)
+    return r
+
+
+def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
+           tau: float = TAU, interval: bool = True):
+    """Quantized attention from the prep outputs `qz` for the given flattened
+    rows (None = all).  Returns (out, lo, hi, flagged), float64 [nrows, d]."""
+    B, Hq, Hkv, N, d = qz["B"], qz["Hq"], qz["Hkv"], qz["N"], qz["d"]
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows.size
+    else:
+        nrows = B * Hq * N
+    out = np.empty((nrows, d), np.float64)
+    lo = np.empty((nrows, d), np.float64) if interval else None
+    hi = np.empty((nrows, d), np.float64) if interval else None
+    flagged = np.empty(nrows, np.int64) if interval else None
+    _load().oracle_attn_q(_ptr(qz["q_i8"]), _ptr(qz["q_scale"]), _ptr(qz["k_i8"]),
+                          _ptr(qz["k_scale"]), _ptr(qz["v_fp8"]), _ptr(qz["v_scale"]),
+                          B, Hq, Hkv, N, d, qz["bq"], qz["bk"], bn, int(causal),
+                          float(sm_scale), float(tau), _ptr(rows), nrows,
+                          _ptr(out), _ptr(lo), _ptr(hi), _ptr(flagged))
+    return out, lo, hi, flagged
+
+
+def attn_f64(q, k, v, causal: bool, sm_scale: float, rows=None) -> np.ndarray:
+    """Full-precision softmax(QK^T*sm_scale)V in float64 for the given rows."""
+    q = np.ascontiguousarray(np.asarray(to_f32(q) if isinstance(q, torch.Tensor) else q,
+                                        dtype=np.float64))
+    k = np.ascontiguousarray(np.asarray(to_f32(k) if isinstance(k, torch.Tensor) else k,
+                                        dtype=np.float64))
+    v = np.ascontiguousarray(np.asarray(to_f32(v) if isinstance(v, torch.Tensor) else v,
+                                        dtype=np.float64))
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows.size
+    else:
+        nrows = B * Hq * N
+    out = np.empty((nrows, d), np.float64)
+    _load().oracle_attn_f64(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, int(causal),
+                            float(sm_scale), _ptr(rows), nrows, _ptr(out))
+    return out
+
+
+def accuracy(out, ref) -> dict:
+    """Cosine similarity and relative L1 of `out` against `ref`."""
+    a = np.asarray(out, np.float64).ravel()
+    b = np.asarray(ref, np.float64).ravel()
+    cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+    rel_l1 = float(np.abs(a - b).sum() / np.abs(b).sum())
+    return {"cos": cos, "rel_l1": rel_l1}
+
+
+def interval_distance(gpu, lo, hi) -> np.ndarray:
+    """Distance of each GPU value from the oracle interval [lo, hi]."""
+    g = np.asarray(gpu, np.float64)
+    return np.maximum(0.0, np.maximum(lo - g, g - hi))

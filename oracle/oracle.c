@@ -1,0 +1,389 @@
+/*
+ * CPU oracle for the forward pass of 8-bit quantized attention (SageAttention
+ * with the FP8 P.V of SageAttention2).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or constant generator with the HIP library; it is written from
+ * the method's description alone, as plain loops in a fixed order, in float64
+ * except where a quantisation decision is defined on float32 values.
+ *
+ * Sources (SageAttention article, "对 K 进行平滑处理" / "对 Q, K 进行分块 INT8
+ * 量化" paragraphs; SageAttention2 summary on the INT4-quantisation search page,
+ * item (4) on P and V; the Berkeley news brief's technique checklist):
+ *   - K is smoothed by subtracting its mean over tokens, per channel; softmax
+ *     is unchanged because the subtracted term is constant along each row.
+ *   - Q and K are quantised to INT8 per block of rows (the flash tile), QK^T
+ *     is an INT8 product with INT32 accumulation.
+ *   - P and V are quantised to FP8 E4M3; V per channel, P per block, and P.V
+ *     is accumulated in two levels (within a block, then across blocks).
+ *
+ * Readings where the pages are silent (each is a parameter of the spec the
+ * HIP path implements too):
+ *   - INT8 is symmetric, range +-127, round-to-nearest-even of x*(127/absmax)
+ *     evaluated in float32; an all-zero block gets scale 0 and codes 0.
+ *   - E4M3 is OCP E4M3FN (bias 7, max 448, subnormal step 2^-9), RNE,
+ *     saturating at +-448; V codes are e4m3(v * (448/absmax_c)) in float32.
+ *   - The P block is one query row by `bn` keys.  Its scale is the block
+ *     maximum over 448: with mt the block's largest score (log2 units,
+ *     float32), P8 = e4m3(2^x), x = fmaf(acc, c, log2(448) - mt), so the
+ *     largest element codes to exactly 448, and the block enters the second
+ *     accumulation level with weight 2^(mt - M), M the row maximum.  The row
+ *     sum l uses the unquantised 2^x values.  See oracle_attn_q.
+ *   - The exponent argument x is defined on float32 exactly as above so that
+ *     both sides take the P8 decision on the same number; only 2^x itself is
+ *     evaluated differently (float64 here).  Codes whose 2^x lies within a
+ *     relative `tau` of a rounding midpoint have two correct values; the
+ *     oracle returns the interval spanned by both choices.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- E4M3 codec */
+
+/* OCP E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent 0 is
+ * subnormal (m * 2^-9); exponent 15 with mantissa 7 is NaN; no infinities. */
+double oracle_e4m3_decode(uint8_t code) {
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even to E4M3FN, saturating at +-448. */
+uint8_t oracle_e4m3_encode(double x) {
+    uint8_t s = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (isnan(x)) return (uint8_t)(s | 0x7F);
+    if (a >= 448.0) return (uint8_t)(s | 0x7E);
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: multiples of 2^-9; rint is round-half-even.  A
+         * result of 8 is the smallest normal, whose code is also 8. */
+        double r = rint(ldexp(a, 9));
+        return (uint8_t)(s | (uint8_t)r);
+    }
+    int ex;
+    frexp(a, &ex);          /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;          /* a in [2^e, 2^(e+1)) */
+    double r = rint(ldexp(a, 3 - e)); /* mantissa with 3 fraction bits, in [8,16] */
+    if (r == 16.0) {
+        r = 8.0;
+        e += 1;
+    }
+    return (uint8_t)(s | (uint8_t)(((e + 7) << 3) | ((int)r - 8)));
+}
+
+void oracle_e4m3_encode_array(const double* x, long n, uint8_t* out) {
+    for (long i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+}
+
+void oracle_e4m3_decode_array(const uint8_t* c, long n, double* out) {
+    for (long i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+
+/* ------------------------------------------------------------ quantisation */
+
+/* Symmetric INT8 of one block of `count` float32 values. */
+static void quant_block_i8(const float* x, long count, int8_t* out, float* scale) {
+    float a = 0.0f;
+    for (long i = 0; i < count; ++i) {
+        float m = fabsf(x[i]);
+        if (m > a) a = m;
+    }
+    if (a == 0.0f) {
+        *scale = 0.0f;
+        memset(out, 0, (size_t)count);
+        return;
+    }
+    float inv = 127.0f / a;
+    *scale = a / 127.0f;
+    for (long i = 0; i < count; ++i) {
+        float t = rintf(x[i] * inv);
+        if (t > 127.0f) t = 127.0f;
+        if (t < -127.0f) t = -127.0f;
+        out[i] = (int8_t)t;
+    }
+}
+
+/*
+ * The prep step: K mean and smoothing, per-block INT8 of Q and smoothed K,
+ * per-channel E4M3 of V.  Inputs are float32 copies of the fp16/bf16 tensors
+ * (the up-conversion is exact), layout [B, H, N, d].
+ *
+ * Outputs (all caller-allocated):
+ *   q_i8 [B,Hq,N,d], q_scale [B,Hq,ceil(N/bq)]
+ *   k_i8 [B,Hkv,N,d], k_scale [B,Hkv,ceil(N/bk)], k_mean [B,Hkv,d]
+ *   v_fp8 [B,Hkv,N,d] (E4M3 codes), v_scale [B,Hkv,d]
+ * smooth = 0 skips the K mean (ablation only; k_mean is then all zero).
+ */
+void oracle_quantize(const float* q, const float* k, const float* v,
+                     int B, int Hq, int Hkv, int N, int d, int bq, int bk, int smooth,
+                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                     float* k_mean, uint8_t* v_fp8, float* v_scale) {
+    const long nd = (long)N * d;
+    const int nqb = (N + bq - 1) / bq, nkb = (N + bk - 1) / bk;
+
+    /* Q: one scale per (b, h, block of bq rows). */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int bh = 0; bh < B * Hq; ++bh)
+        for (int t = 0; t < nqb; ++t) {
+            long r0 = (long)t * bq, r1 = r0 + bq < N ? r0 + bq : N;
+            quant_block_i8(q + bh * nd + r0 * d, (r1 - r0) * d, q_i8 + bh * nd + r0 * d,
+                           q_scale + (long)bh * nqb + t);
+        }
+
+#pragma omp parallel for schedule(static)
+    for (int bg = 0; bg < B * Hkv; ++bg) {
+        const float* kh = k + bg * nd;
+        const float* vh = v + bg * nd;
+        float* mean = k_mean + (long)bg * d;
+        /* K mean over all N tokens, per channel: float64 sum, one rounding. */
+        for (int c = 0; c < d; ++c) {
+            double s = 0.0;
+            for (long n = 0; n < N; ++n) s += (double)kh[n * d + c];
+            mean[c] = smooth ? (float)(s / (double)N) : 0.0f;
+        }
+        /* Smoothed K in float32, then per-block INT8 over bk rows. */
+        float* ks = (float*)malloc(sizeof(float) * (size_t)nd);
+        for (long n = 0; n < N; ++n)
+            for (int c = 0; c < d; ++c) ks[n * d + c] = kh[n * d + c] - mean[c];
+        for (int t = 0; t < nkb; ++t) {
+            long r0 = (long)t * bk, r1 = r0 + bk < N ? r0 + bk : N;
+            quant_block_i8(ks + r0 * d, (r1 - r0) * d, k_i8 + bg * nd + r0 * d,
+                           k_scale + (long)bg * nkb + t);
+        }
+        free(ks);
+        /* V per channel: absmax over tokens, E4M3 of v * (448/absmax). */
+        for (int c = 0; c < d; ++c) {
+            float a = 0.0f;
+            for (long n = 0; n < N; ++n) {
+                float m = fabsf(vh[n * d + c]);
+                if (m > a) a = m;
+            }
+            float* sv = v_scale + (long)bg * d + c;
+            if (a == 0.0f) {
+                *sv = 0.0f;
+                for (long n = 0; n < N; ++n) v_fp8[bg * nd + n * d + c] = 0;
+                continue;
+            }
+            float inv = 448.0f / a;
+            *sv = a / 448.0f;
+            for (long n = 0; n < N; ++n) {
+                float t = vh[n * d + c] * inv;
+                v_fp8[bg * nd + n * d + c] = oracle_e4m3_encode((double)t);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------- quantised attention */
+
+/*
+ * Quantised attention for a list of query rows (flattened (b*Hq + h)*N + i;
+ * rows == NULL means every row).  For each row, with g = h / (Hq/Hkv) and the
+ * allowed keys j <= i (causal) or all j < N:
+ *
+ *   acc_j = sum_c q_i8[i,c] * k_i8[j,c]                       (exact integer)
+ *   c_j   = f32( f32(sq * sk[j/bk]) * f32(sm_scale*log2 e) )   (float32)
+ *   blocks t of bn keys; s_j = f32(acc_j * c_j); m_t = max over the block's
+ *   allowed keys; bias_t = f32(f32(log2 448) - m_t)
+ *   x_j   = fmaf(acc_j, c_j, bias_t);  y_j = 2^x_j (float64)
+ *   P8_j  = e4m3(y_j)                  (the block maximum codes to 448)
+ *   level 1: A_t[c] = sum_{j in t} P8_j * V8[j,c];  r_t = sum_{j in t} y_j
+ *   level 2: with M = max_t m_t and w_t = 2^(m_t - M) (float64),
+ *            O[c] = sum_t w_t A_t[c],  l = sum_t w_t r_t
+ *   out[c] = O[c] * sv[c] / l
+ *
+ * out_lo/out_hi (optional) bound the output over every choice of the P8 codes
+ * whose y lies within relative distance tau of a rounding midpoint; flagged
+ * (optional) receives the number of such codes per row.
+ */
+void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                   const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                   int B, int Hq, int Hkv, int N, int d, int bq, int bk, int bn, int causal,
+                   float sm_scale, double tau, const int64_t* rows, long nrows,
+                   double* out, double* out_lo, double* out_hi, int64_t* flagged) {
+    const long nd = (long)N * d;
+    const int G = Hq / Hkv;
+    const int nqb = (N + bq - 1) / bq, nkb = (N + bk - 1) / bk;
+    const float qk = (float)((double)sm_scale * 1.4426950408889634); /* log2(e) */
+    const float l448 = (float)log2(448.0);
+    double dec[256];
+    for (int i = 0; i < 256; ++i) dec[i] = oracle_e4m3_decode((uint8_t)i);
+    if (rows == NULL) nrows = (long)B * Hq * N;
+
+#pragma omp parallel
+    {
+        int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+        float* cj = (float*)malloc(sizeof(float) * (size_t)N);
+        float* mblk = (float*)malloc(sizeof(float) * (size_t)(N / bn + 2));
+        double* A = (double*)malloc(sizeof(double) * (size_t)d);
+        double* O = (double*)malloc(sizeof(double) * (size_t)d);
+        double* lo = (double*)malloc(sizeof(double) * (size_t)d);
+        double* hi = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (long ri = 0; ri < nrows; ++ri) {
+            long row = rows ? (long)rows[ri] : ri;
+            long bh = row / N;
+            int i = (int)(row % N);
+            int b = (int)(bh / Hq), h = (int)(bh % Hq);
+            int g = h / G;
+            const int8_t* qrow = q_i8 + bh * nd + (long)i * d;
+            const int8_t* kh = k_i8 + ((long)b * Hkv + g) * nd;
+            const uint8_t* vh = v_fp8 + ((long)b * Hkv + g) * nd;
+            const float* svh = v_scale + ((long)b * Hkv + g) * d;
+            const float sq = q_scale[bh * nqb + i / bq];
+            const float* skh = k_scale + ((long)b * Hkv + g) * nkb;
+            int jmax = causal ? i : N - 1;
+            int nt = jmax / bn + 1;
+
+            /* scores */
+            for (int j = 0; j <= jmax; ++j) {
+                int32_t s = 0;
+                const int8_t* kr = kh + (long)j * d;
+                for (int c = 0; c < d; ++c) s += (int32_t)qrow[c] * (int32_t)kr[c];
+                acc[j] = s;
+                float sqk = sq * skh[j / bk];
+                cj[j] = sqk * qk;
+            }
+            /* per-block maximum score: the P scale of the block */
+            float M = -INFINITY;
+            for (int t = 0; t < nt; ++t) {
+                int j0 = t * bn, j1 = j0 + bn - 1 < jmax ? j0 + bn - 1 : jmax;
+                float mt = -INFINITY;
+                for (int j = j0; j <= j1; ++j) {
+                    float s = (float)acc[j] * cj[j];
+                    if (s > mt) mt = s;
+                }
+                mblk[t] = mt;
+                if (mt > M) M = mt;
+            }
+            /* P quantisation and the two-level accumulation */
+            double l = 0.0;
+            int64_t nflag = 0;
+            for (int c = 0; c < d; ++c) O[c] = lo[c] = hi[c] = 0.0;
+            for (int t = 0; t < nt; ++t) {
+                int j0 = t * bn, j1 = j0 + bn - 1 < jmax ? j0 + bn - 1 : jmax;
+                float bias = l448 - mblk[t];
+                double w = exp2((double)mblk[t] - (double)M);
+                double r = 0.0;
+                for (int c = 0; c < d; ++c) A[c] = 0.0;
+                for (int j = j0; j <= j1; ++j) {
+                    float x = fmaf((float)acc[j], cj[j], bias);
+                    double y = exp2((double)x);
+                    uint8_t code = oracle_e4m3_encode(y);
+                    double p = dec[code];
+                    r += y;
+                    const uint8_t* vr = vh + (long)j * d;
+                    for (int c = 0; c < d; ++c) A[c] += p * dec[vr[c]];
+                    if (out_lo || flagged) {
+                        /* the other code is also correct when y sits within
+                         * tau of the midpoint to a neighbouring code */
+                        double alt = p;
+                        if (code < 0x7E) {
+                            double up = dec[code + 1], mid = 0.5 * (p + up);
+                            if (fabs(y - mid) <= tau * mid) alt = up;
+                        }
+                        if (code > 0 && alt == p) {
+                            double dn = dec[code - 1], mid = 0.5 * (p + dn);
+                            if (fabs(y - mid) <= tau * mid) alt = dn;
+                        }
+                        if (alt != p) {
+                            ++nflag;
+                            if (out_lo)
+                                for (int c = 0; c < d; ++c) {
+                                    double delta = w * (alt - p) * dec[vr[c]];
+                                    if (delta < 0) lo[c] += delta;
+                                    else hi[c] += delta;
+                                }
+                        }
+                    }
+                }
+                for (int c = 0; c < d; ++c) O[c] += w * A[c];
+                l += w * r;
+            }
+            for (int c = 0; c < d; ++c) {
+                double sv = (double)svh[c];
+                out[ri * d + c] = O[c] * sv / l;
+                if (out_lo) {
+                    out_lo[ri * d + c] = (O[c] + lo[c]) * sv / l;
+                    out_hi[ri * d + c] = (O[c] + hi[c]) * sv / l;
+                }
+            }
+            if (flagged) flagged[ri] = nflag;
+        }
+        free(acc);
+        free(cj);
+        free(mblk);
+        free(A);
+        free(O);
+        free(lo);
+        free(hi);
+    }
+}
+
+/* ------------------------------------------- full-precision attention */
+
+/*
+ * softmax(Q K^T * sm_scale) V in float64 for a list of rows (same row
+ * indexing as oracle_attn_q), with the causal mask j <= i when asked.
+ * Inputs are float64 [B,H,N,d].
+ */
+void oracle_attn_f64(const double* q, const double* k, const double* v, int B, int Hq,
+                     int Hkv, int N, int d, int causal, double sm_scale,
+                     const int64_t* rows, long nrows, double* out) {
+    const long nd = (long)N * d;
+    const int G = Hq / Hkv;
+    if (rows == NULL) nrows = (long)B * Hq * N;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (long ri = 0; ri < nrows; ++ri) {
+            long row = rows ? (long)rows[ri] : ri;
+            long bh = row / N;
+            int i = (int)(row % N);
+            int b = (int)(bh / Hq), h = (int)(bh % Hq);
+            int g = h / G;
+            const double* qr = q + bh * nd + (long)i * d;
+            const double* kh = k + ((long)b * Hkv + g) * nd;
+            const double* vh = v + ((long)b * Hkv + g) * nd;
+            int jmax = causal ? i : N - 1;
+            double m = -INFINITY;
+            for (int j = 0; j <= jmax; ++j) {
+                double t = 0.0;
+                for (int c = 0; c < d; ++c) t += qr[c] * kh[(long)j * d + c];
+                s[j] = t * sm_scale;
+                if (s[j] > m) m = s[j];
+            }
+            double l = 0.0;
+            double* o = out + ri * d;
+            for (int c = 0; c < d; ++c) o[c] = 0.0;
+            for (int j = 0; j <= jmax; ++j) {
+                double p = exp(s[j] - m);
+                l += p;
+                for (int c = 0; c < d; ++c) o[c] += p * vh[(long)j * d + c];
+            }
+            for (int c = 0; c < d; ++c) o[c] /= l;
+        }
+        free(s);
+    }
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
