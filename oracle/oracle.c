@@ -29,7 +29,8 @@
  *     float32), P8 = e4m3(2^x), x = fmaf(acc, c, log2(448) - mt), so the
  *     largest element codes to exactly 448, and the block enters the second
  *     accumulation level with weight 2^(mt - M), M the row maximum.  The row
- *     sum l uses the unquantised 2^x values.  See oracle_attn_q.
+ *     sum l is the same two-level sum over the quantised P, so the quantised
+ *     weights are normalised exactly.  See oracle_attn_q.
  *   - The exponent argument x is defined on float32 exactly as above so that
  *     both sides take the P8 decision on the same number; only 2^x itself is
  *     evaluated differently (float64 here).  Codes whose 2^x lies within a
@@ -199,14 +200,17 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  *   allowed keys; bias_t = f32(f32(log2 448) - m_t)
  *   x_j   = fmaf(acc_j, c_j, bias_t);  y_j = 2^x_j (float64)
  *   P8_j  = e4m3(y_j)                  (the block maximum codes to 448)
- *   level 1: A_t[c] = sum_{j in t} P8_j * V8[j,c];  r_t = sum_{j in t} y_j
+ *   level 1: A_t[c] = sum_{j in t} P8_j * V8[j,c];  R_t = sum_{j in t} P8_j
  *   level 2: with M = max_t m_t and w_t = 2^(m_t - M) (float64),
- *            O[c] = sum_t w_t A_t[c],  l = sum_t w_t r_t
+ *            O[c] = sum_t w_t A_t[c],  l = sum_t w_t R_t
  *   out[c] = O[c] * sv[c] / l
  *
  * out_lo/out_hi (optional) bound the output over every choice of the P8 codes
- * whose y lies within relative distance tau of a rounding midpoint; flagged
- * (optional) receives the number of such codes per row.
+ * whose y lies within relative distance tau of a rounding midpoint: changing
+ * code j by delta moves out[c] by w delta (V8[j,c] sv[c] - out[c]) / (l + w
+ * delta); the bounds add these moves' negative and positive parts, widened by
+ * their relative interaction (sum |w delta| / l).  flagged (optional)
+ * receives the number of such codes per row.
  */
 void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                    const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
@@ -229,8 +233,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
         float* mblk = (float*)malloc(sizeof(float) * (size_t)(N / bn + 2));
         double* A = (double*)malloc(sizeof(double) * (size_t)d);
         double* O = (double*)malloc(sizeof(double) * (size_t)d);
-        double* lo = (double*)malloc(sizeof(double) * (size_t)d);
-        double* hi = (double*)malloc(sizeof(double) * (size_t)d);
+        int32_t* fj = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);   /* flagged keys */
+        double* fwd = (double*)malloc(sizeof(double) * (size_t)N);     /* their w * delta */
 #pragma omp for schedule(dynamic, 1)
         for (long ri = 0; ri < nrows; ++ri) {
             long row = rows ? (long)rows[ri] : ri;
@@ -271,19 +275,19 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
             /* P quantisation and the two-level accumulation */
             double l = 0.0;
             int64_t nflag = 0;
-            for (int c = 0; c < d; ++c) O[c] = lo[c] = hi[c] = 0.0;
+            for (int c = 0; c < d; ++c) O[c] = 0.0;
             for (int t = 0; t < nt; ++t) {
                 int j0 = t * bn, j1 = j0 + bn - 1 < jmax ? j0 + bn - 1 : jmax;
                 float bias = l448 - mblk[t];
                 double w = exp2((double)mblk[t] - (double)M);
-                double r = 0.0;
+                double R = 0.0;
                 for (int c = 0; c < d; ++c) A[c] = 0.0;
                 for (int j = j0; j <= j1; ++j) {
                     float x = fmaf((float)acc[j], cj[j], bias);
                     double y = exp2((double)x);
                     uint8_t code = oracle_e4m3_encode(y);
                     double p = dec[code];
-                    r += y;
+                    R += p;
                     const uint8_t* vr = vh + (long)j * d;
                     for (int c = 0; c < d; ++c) A[c] += p * dec[vr[c]];
                     if (out_lo || flagged) {
@@ -299,25 +303,30 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                             if (fabs(y - mid) <= tau * mid) alt = dn;
                         }
                         if (alt != p) {
+                            fj[nflag] = j;
+                            fwd[nflag] = w * (alt - p);
                             ++nflag;
-                            if (out_lo)
-                                for (int c = 0; c < d; ++c) {
-                                    double delta = w * (alt - p) * dec[vr[c]];
-                                    if (delta < 0) lo[c] += delta;
-                                    else hi[c] += delta;
-                                }
                         }
                     }
                 }
                 for (int c = 0; c < d; ++c) O[c] += w * A[c];
-                l += w * r;
+                l += w * R;
             }
-            for (int c = 0; c < d; ++c) {
-                double sv = (double)svh[c];
-                out[ri * d + c] = O[c] * sv / l;
-                if (out_lo) {
-                    out_lo[ri * d + c] = (O[c] + lo[c]) * sv / l;
-                    out_hi[ri * d + c] = (O[c] + hi[c]) * sv / l;
+            for (int c = 0; c < d; ++c) out[ri * d + c] = O[c] * (double)svh[c] / l;
+            if (out_lo) {
+                double inter = 0.0;
+                for (int64_t e = 0; e < nflag; ++e) inter += fabs(fwd[e]) / l;
+                for (int c = 0; c < d; ++c) {
+                    double o = out[ri * d + c], neg = 0.0, pos = 0.0;
+                    for (int64_t e = 0; e < nflag; ++e) {
+                        double vjc = dec[vh[(long)fj[e] * d + c]] * (double)svh[c];
+                        double mv = fwd[e] * (vjc - o) / (l + fwd[e]);
+                        if (mv < 0) neg += mv;
+                        else pos += mv;
+                    }
+                    double slack = 2.0 * inter * (pos - neg);
+                    out_lo[ri * d + c] = o + neg - slack;
+                    out_hi[ri * d + c] = o + pos + slack;
                 }
             }
             if (flagged) flagged[ri] = nflag;
@@ -327,8 +336,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
         free(mblk);
         free(A);
         free(O);
-        free(lo);
-        free(hi);
+        free(fj);
+        free(fwd);
     }
 }
 
