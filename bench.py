@@ -1,0 +1,148 @@
+#!/usr/bin/env python3
+"""Throughput of the 8-bit quantized attention forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: the prep kernels (K mean, smoothing, INT8 Q/K, FP8 V)
+followed by the fused attention kernel, i.e. one sage_attn_fwd call.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu]
+
+Prints one JSON line.  `value` is TOPS = 4*B*Hq*N^2*d / t (halved for causal)
+for the whole step; `roofline` prices the attention kernel alone (its average
+duration measured with HIP events on the stream it runs on) against the dense
+INT8/FP8 matrix-core peak; `cpu_baseline` times the CPU oracle on a bounded
+sample of query rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized attention fwd TOPS (4·B·H·N²·d/t) and % of INT8/FP8 MFMA peak, 1 GPU"
+PEAK_TOPS = 5000.0        # MI355X dense INT8 = dense FP8 matrix-core peak (ops/s / 1e12)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=3,
+                   help="1..5; 3 is the non-causal N=17550 video-diffusion shape")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
+    return p.parse_args()
+
+
+def timed(fn, iters, torch):
+    """Average milliseconds per call of fn() measured with HIP events on the
+    current stream (the stream every library call is launched on)."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(iters):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(w, q, k, v, rows_wanted):
+    """The oracle as it stands: its prep over the whole input, pro-rated to the
+    sampled rows, plus its attention over the sampled rows."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    oracle.build()
+    t0 = time.perf_counter()
+    oz = oracle.quantize(q, k, v)
+    t_prep = time.perf_counter() - t0
+    total_rows = w.B * w.Hq * w.N
+    if rows_wanted <= 0:
+        # ~15 s of attention work at the box's thread count, measured first on 64 rows
+        probe = workloads.sample_rows(w, 64, seed=1)
+        t0 = time.perf_counter()
+        oracle.attn_q(oz, w.causal, w.sm_scale, rows=probe, interval=False)
+        per_row = (time.perf_counter() - t0) / len(probe)
+        rows_wanted = int(max(64, min(total_rows, 15.0 / max(per_row, 1e-9))))
+    rows = workloads.sample_rows(w, rows_wanted, seed=2)
+    t0 = time.perf_counter()
+    oracle.attn_q(oz, w.causal, w.sm_scale, rows=rows, interval=False)
+    t_attn = time.perf_counter() - t0
+    frac = len(rows) / total_rows
+    t = t_attn + t_prep * frac
+    ops = w.ops * frac  # causal rows are sampled uniformly, so the average row cost matches
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} of {total_rows} query rows (uniform, seeded) of the same workload; "
+                      f"oracle prep over the full input pro-rated by that fraction "
+                      f"(prep {t_prep:.2f} s, attention {t_attn:.2f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_quantized_attention_02_amd as sage
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    q, k, v = workloads.generate(w)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    ws = sage.workspace_for(qd, kd)
+    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d)
+
+    def step():
+        sage.sage_attn_fwd(qd, kd, vd, out, w.causal, w.sm_scale, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = timed(step, args.steps, torch)
+    wall = time.perf_counter() - t0
+
+    # per-kernel averages on the same stream
+    ms_prep = timed(lambda: sage.sage_quantize(qd, kd, vd, z), args.steps, torch)
+    ms_attn = timed(lambda: sage.sage_attn_fwd_quantized(z, out, w.B, w.Hq, w.Hkv, w.N, w.d,
+                                                         w.causal, w.sm_scale), args.steps, torch)
+    tops = w.ops / (ms_step * 1e-3) / 1e12
+    attn_tops = w.ops / (ms_attn * 1e-3) / 1e12
+    elems = (w.B * w.Hq + 2 * w.B * w.Hkv) * w.N * w.d
+    prep_gbs = 3.0 * elems / (ms_prep * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8xi8->i32 + e4m3xe4m3->f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "input_dtype": w.dtype, "sm_scale": w.sm_scale,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd", "ms_per_launch": round(ms_attn, 4)},
+        "prep": {"ms_per_launch": round(ms_prep, 4), "alg_GBps": round(prep_gbs, 1),
+                 "frac_hbm": round(prep_gbs / HBM_PEAK_GBS, 4)},
+        "timed_wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,274 @@
+// The prep step of 8-bit quantized attention: K channel mean and smoothing,
+// per-block INT8 of Q and smoothed K, per-channel E4M3 of V (SageAttention
+// article: smoothing K and per-block INT8 Q/K; SageAttention2 summary: E4M3
+// for V).  Memory-bound: every kernel streams 16-byte loads and does its
+// reductions in registers, wavefront shuffles and LDS.
+//
+//   prep_stats_q  per (kv head, 512-row chunk): partial K channel sums
+//                 (float64) and V channel absmax; per (q head, 128-row block):
+//                 Q absmax, scale and INT8 codes.
+//   prep_finalize per kv head: K mean and V scales from the partials, summed
+//                 in a fixed order (deterministic).
+//   prep_pack     per (kv head, 64-row block) K - mean, absmax, scale, codes;
+//                 per (kv head, 128-key block) V codes, transposed to the
+//                 attention kernel's channel-major, permuted-key layout.
+//                 Heads are visited in the reverse order of prep_stats_q so
+//                 the second read of K and V finds the most recent heads
+//                 still in the last-level cache.
+#include "sage_internal.h"
+
+namespace sage {
+
+// ------------------------------------------------------------ statistics + Q
+template <typename In, int D>
+__global__ __launch_bounds__(kThreads) void prep_stats_q(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, Shape s, int8_t* __restrict__ q_i8,
+    float* __restrict__ q_scale, double* __restrict__ k_part, float* __restrict__ v_part) {
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
+    constexpr int RPI = kThreads / CPR;   // rows per iteration
+    __shared__ double ssum[RPI][D];
+    __shared__ float smax[RPI][D];
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int nstat = s.B * s.Hkv * s.nchunk;
+    const int bid = blockIdx.x;
+
+    if (bid < nstat) {
+        const int bg = bid / s.nchunk, chunk = bid % s.nchunk;
+        const int cg = tid % CPR, rr = tid / CPR;
+        const long long head = (long long)bg * s.N * D;
+        const int r0 = chunk * kStatRows;
+        const int r1 = min(s.N, r0 + kStatRows);
+        double sum[8];
+        float mx[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sum[i] = 0.0;
+            mx[i] = 0.0f;
+        }
+        for (int r = r0 + rr; r < r1; r += RPI) {
+            const long long off = head + (long long)r * D + cg * 8;
+            const uint4 uk = *reinterpret_cast<const uint4*>(k + off);
+            const uint4 uv = *reinterpret_cast<const uint4*>(v + off);
+            float fk[8], fv[8];
+            unpack8<In>(uk, fk);
+            unpack8<In>(uv, fv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sum[i] += (double)fk[i];
+                mx[i] = fmaxf(mx[i], fabsf(fv[i]));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ssum[rr][cg * 8 + i] = sum[i];
+            smax[rr][cg * 8 + i] = mx[i];
+        }
+        __syncthreads();
+        if (tid < D) {
+            double t = 0.0;
+            float m = 0.0f;
+            for (int r = 0; r < RPI; ++r) {
+                t += ssum[r][tid];
+                m = fmaxf(m, smax[r][tid]);
+            }
+            const long long o = ((long long)bg * s.nchunk + chunk) * D + tid;
+            k_part[o] = t;
+            v_part[o] = m;
+        }
+        return;
+    }
+
+    // Q block: rows [t*BQ, t*BQ+BQ) of head bh; rows >= N are zero padding.
+    const int qb = bid - nstat;
+    const int nqt = s.Np / SAGE_BQ;
+    const int bh = qb / nqt, t = qb % nqt;
+    constexpr int NCH = SAGE_BQ * CPR / kThreads;  // chunks per thread
+    const long long src_head = (long long)bh * s.N * D;
+    const long long dst_head = (long long)bh * s.Np * D;
+    float x[NCH][8];
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = tid + c * kThreads;
+        const int row = t * SAGE_BQ + e / CPR, col = (e % CPR) * 8;
+        if (row < s.N) {
+            const uint4 u = *reinterpret_cast<const uint4*>(q + src_head + (long long)row * D + col);
+            unpack8<In>(u, x[c]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[c][i] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[c][i]));
+    }
+    a = block_max(a, red);
+    const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+    if (tid == 0) q_scale[(long long)bh * nqt + t] = a / 127.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = tid + c * kThreads;
+        const int row = t * SAGE_BQ + e / CPR, col = (e % CPR) * 8;
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = __builtin_rintf(x[c][i] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (i & 3));
+        }
+        *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = make_uint2(w[0], w[1]);
+    }
+}
+
+// ------------------------------------------------------------ finalisation
+template <int D>
+__global__ __launch_bounds__(D) void prep_finalize(Shape s, const double* __restrict__ k_part,
+                                                   const float* __restrict__ v_part,
+                                                   float* __restrict__ k_mean,
+                                                   float* __restrict__ v_scale,
+                                                   float* __restrict__ v_inv) {
+    const int bg = blockIdx.x, c = threadIdx.x;
+    double sum = 0.0;
+    float m = 0.0f;
+    for (int ch = 0; ch < s.nchunk; ++ch) {
+        const long long o = ((long long)bg * s.nchunk + ch) * D + c;
+        sum += k_part[o];
+        m = fmaxf(m, v_part[o]);
+    }
+    const long long o = (long long)bg * D + c;
+    k_mean[o] = (float)(sum / (double)s.N);
+    v_scale[o] = m / 448.0f;
+    v_inv[o] = m > 0.0f ? 448.0f / m : 0.0f;
+}
+
+// ------------------------------------------------------------ K and V packing
+template <typename In, int D>
+__global__ __launch_bounds__(kThreads) void prep_pack(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s,
+    const float* __restrict__ k_mean, const float* __restrict__ v_inv,
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint8_t* __restrict__ v_fp8) {
+    constexpr int CPR = D / 8;
+    __shared__ float red[4];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[D * SAGE_BN];
+    const int tid = threadIdx.x;
+    const int nkb = s.Np / SAGE_BK, nvb = s.Np / SAGE_BN;
+    const int per_head = nkb + nvb;
+    // reverse head order relative to prep_stats_q
+    const int bg = s.B * s.Hkv - 1 - (int)(blockIdx.x / per_head);
+    const int j = blockIdx.x % per_head;
+    const long long src_head = (long long)bg * s.N * D;
+
+    if (j < nkb) {
+        const int t = j;
+        constexpr int NCH = SAGE_BK * CPR / kThreads;
+        const long long dst_head = (long long)bg * s.Np * D;
+        float x[NCH][8];
+        float a = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int e = tid + c * kThreads;
+            const int row = t * SAGE_BK + e / CPR, col = (e % CPR) * 8;
+            if (row < s.N) {
+                const uint4 u = *reinterpret_cast<const uint4*>(k + src_head + (long long)row * D + col);
+                unpack8<In>(u, x[c]);
+                const float* mean = k_mean + (long long)bg * D + col;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[c][i] = x[c][i] - mean[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[c][i] = 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[c][i]));
+        }
+        a = block_max(a, red);
+        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        if (tid == 0) k_scale[(long long)bg * nkb + t] = a / 127.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int e = tid + c * kThreads;
+            const int row = t * SAGE_BK + e / CPR, col = (e % CPR) * 8;
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float r = __builtin_rintf(x[c][i] * inv);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (i & 3));
+            }
+            *reinterpret_cast<uint2*>(k_i8 + dst_head + (long long)row * D + col) = make_uint2(w[0], w[1]);
+        }
+        return;
+    }
+
+    // V block T: codes of 128 keys x D channels, transposed through LDS.
+    const int T = j - nkb;
+    constexpr int NCH = SAGE_BN * CPR / kThreads;
+    const float* inv = v_inv + (long long)bg * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = tid + c * kThreads;
+        const int key = e / CPR, col = (e % CPR) * 8;
+        const int row = T * SAGE_BN + key;
+        float x[8];
+        if (row < s.N) {
+            const uint4 u = *reinterpret_cast<const uint4*>(v + src_head + (long long)row * D + col);
+            unpack8<In>(u, x);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+        }
+        const int pos = v_key_position(key);
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            // |v * inv| <= 448 (1 + 2^-23); the clamp keeps the hardware
+            // conversion (which gives NaN above 464) in range regardless.
+            const float y0 = fminf(fmaxf(x[i] * inv[col + i], -448.0f), 448.0f);
+            const float y1 = fminf(fmaxf(x[i + 1] * inv[col + i + 1], -448.0f), 448.0f);
+            const uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+            vt[(col + i) * SAGE_BN + pos] = (uint8_t)(p & 0xFFu);
+            vt[(col + i + 1) * SAGE_BN + pos] = (uint8_t)((p >> 8) & 0xFFu);
+        }
+    }
+    __syncthreads();
+    uint8_t* dst = v_fp8 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN);
+    constexpr int OUT_CH = D * SAGE_BN / 16 / kThreads;
+#pragma unroll
+    for (int c = 0; c < OUT_CH; ++c) {
+        const int e = tid + c * kThreads;
+        *reinterpret_cast<uint4*>(dst + e * 16) = *reinterpret_cast<const uint4*>(vt + e * 16);
+    }
+}
+
+// ------------------------------------------------------------ launchers
+template <typename In, int D>
+static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const Shape& s,
+                                const sage_qkv_quant* z, hipStream_t st) {
+    const int nstat = s.B * s.Hkv * s.nchunk;
+    const int nq = s.B * s.Hq * (s.Np / SAGE_BQ);
+    hipLaunchKernelGGL((prep_stats_q<In, D>), dim3(nstat + nq), dim3(kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, z->q_i8,
+                       z->q_scale, z->k_part, z->v_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prep_finalize<D>), dim3(s.B * s.Hkv), dim3(D), 0, st, s, z->k_part,
+                       z->v_part, z->k_mean, z->v_scale, z->v_inv);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int per_head = s.Np / SAGE_BK + s.Np / SAGE_BN;
+    hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
+                       (const uint16_t*)k, (const uint16_t*)v, s, z->k_mean, z->v_inv, z->k_i8,
+                       z->k_scale, z->v_fp8);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, const Shape& s,
+                       const sage_qkv_quant* z, hipStream_t st) {
+    if (dtype == SAGE_F16)
+        return s.d == 64 ? launch_prep_t<_Float16, 64>(q, k, v, s, z, st)
+                         : launch_prep_t<_Float16, 128>(q, k, v, s, z, st);
+    return s.d == 64 ? launch_prep_t<Bf16Tag, 64>(q, k, v, s, z, st)
+                     : launch_prep_t<Bf16Tag, 128>(q, k, v, s, z, st);
+}
+
+}  // namespace sage

@@ -1,0 +1,178 @@
+// Host side of the C ABI declared in include/sage.h: argument validation
+// (before any HIP call), workspace carving and kernel launches.
+#include <math.h>
+#include <string.h>
+
+#include "sage_internal.h"
+
+namespace sage {
+hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, const Shape& s,
+                       const sage_qkv_quant* z, hipStream_t st);
+hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal, float qk,
+                       float l448, hipStream_t st);
+}  // namespace sage
+
+using sage::Shape;
+
+static int check_shape(int B, int Hq, int Hkv, int N, int d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return SAGE_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+    if (Hq % Hkv != 0) return SAGE_ERR_UNSUPPORTED;
+    if (N > SAGE_MAX_N) return SAGE_ERR_UNSUPPORTED;
+    const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
+    // work-group counts must fit a 1-D grid
+    if ((long long)B * Hq * (s.Np / SAGE_BQ) >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
+    if ((long long)B * Hkv * (s.Np / SAGE_BK + s.Np / SAGE_BN) >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
+    return SAGE_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout: each region starts on a 256-byte boundary.
+struct Layout {
+    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale, v_inv, k_part, v_part, total;
+};
+
+static Layout layout(const Shape& s) {
+    Layout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += round256(bytes);
+        return o;
+    };
+    const size_t Bq = (size_t)s.B * s.Hq, Bkv = (size_t)s.B * s.Hkv;
+    L.q_i8 = take((size_t)s.q_elems());
+    L.k_i8 = take((size_t)s.kv_elems());
+    L.v_fp8 = take((size_t)s.kv_elems());
+    L.q_scale = take(Bq * (s.Np / SAGE_BQ) * sizeof(float));
+    L.k_scale = take(Bkv * (s.Np / SAGE_BK) * sizeof(float));
+    L.k_mean = take(Bkv * s.d * sizeof(float));
+    L.v_scale = take(Bkv * s.d * sizeof(float));
+    L.v_inv = take(Bkv * s.d * sizeof(float));
+    L.k_part = take(Bkv * s.nchunk * s.d * sizeof(double));
+    L.v_part = take(Bkv * s.nchunk * s.d * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+static int check_quant(const sage_qkv_quant* z) {
+    if (!z) return SAGE_ERR_INVALID_ARG;
+    if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v_fp8 ||
+        !z->v_scale || !z->v_inv || !z->k_part || !z->v_part)
+        return SAGE_ERR_INVALID_ARG;
+    if (!aligned(z->q_i8, 16) || !aligned(z->k_i8, 16) || !aligned(z->v_fp8, 16) ||
+        !aligned(z->v_scale, 16) || !aligned(z->k_part, 8))
+        return SAGE_ERR_INVALID_ARG;
+    return SAGE_OK;
+}
+
+extern "C" {
+
+size_t sage_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+    if (check_shape(B, Hq, Hkv, N, d) != SAGE_OK) return 0;
+    return layout(sage::make_shape(B, Hq, Hkv, N, d)).total;
+}
+
+int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
+                         sage_qkv_quant* out) {
+    int rc = check_shape(B, Hq, Hkv, N, d);
+    if (rc != SAGE_OK) return rc;
+    if (!out) return SAGE_ERR_INVALID_ARG;
+    if (!ws || !aligned(ws, 256)) return SAGE_ERR_WORKSPACE;
+    const Layout L = layout(sage::make_shape(B, Hq, Hkv, N, d));
+    if (ws_bytes < L.total) return SAGE_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    out->q_i8 = (int8_t*)(base + L.q_i8);
+    out->q_scale = (float*)(base + L.q_scale);
+    out->k_i8 = (int8_t*)(base + L.k_i8);
+    out->k_scale = (float*)(base + L.k_scale);
+    out->k_mean = (float*)(base + L.k_mean);
+    out->v_fp8 = (uint8_t*)(base + L.v_fp8);
+    out->v_scale = (float*)(base + L.v_scale);
+    out->v_inv = (float*)(base + L.v_inv);
+    out->k_part = (double*)(base + L.k_part);
+    out->v_part = (float*)(base + L.v_part);
+    return SAGE_OK;
+}
+
+int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
+                  int N, int d, const sage_qkv_quant* dst, void* stream) {
+    int rc = check_shape(B, Hq, Hkv, N, d);
+    if (rc != SAGE_OK) return rc;
+    if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
+    if (!q || !k || !v || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return SAGE_ERR_INVALID_ARG;
+    rc = check_quant(dst);
+    if (rc != SAGE_OK) return rc;
+    const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
+    hipError_t e = sage::launch_prep(q, k, v, dtype, s, dst, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq, int Hkv, int N,
+                            int d, int causal, float sm_scale, void* stream) {
+    int rc = check_shape(B, Hq, Hkv, N, d);
+    if (rc != SAGE_OK) return rc;
+    if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
+    if (!out || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
+    rc = check_quant(src);
+    if (rc != SAGE_OK) return rc;
+    const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
+    // the exponent factor and log2(448) are rounded once to float32 here, as
+    // the method's spec defines them
+    const float qk = (float)((double)sm_scale * 1.4426950408889634);
+    const float l448 = (float)log2(448.0);
+    hipError_t e = sage::launch_attn(src, out, s, causal, qk, l448, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                  int N, int d, int causal, float sm_scale, int dtype, void* workspace,
+                  size_t ws_bytes, void* stream) {
+    int rc = check_shape(B, Hq, Hkv, N, d);
+    if (rc != SAGE_OK) return rc;
+    if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
+    if (!q || !k || !v || !out || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(out, 16))
+        return SAGE_ERR_INVALID_ARG;
+    sage_qkv_quant z;
+    rc = sage_workspace_carve(workspace, ws_bytes, B, Hq, Hkv, N, d, &z);
+    if (rc != SAGE_OK) return rc;
+    rc = sage_quantize(q, k, v, dtype, B, Hq, Hkv, N, d, &z, stream);
+    if (rc != SAGE_OK) return rc;
+    return sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, causal, sm_scale, stream);
+}
+
+int sage_get_config(sage_config* c) {
+    if (!c) return SAGE_ERR_INVALID_ARG;
+    c->bq = SAGE_BQ;
+    c->bk = SAGE_BK;
+    c->bn = SAGE_BN;
+    c->fp8_max = SAGE_FP8_MAX;
+    c->version = sage::kVersion;
+    return SAGE_OK;
+}
+
+int sage_v_key_position(int j) {
+    if (j < 0 || j >= SAGE_BN) return -1;
+    return sage::v_key_position(j);
+}
+
+const char* sage_status_string(int status) {
+    switch (status) {
+        case SAGE_OK: return "ok";
+        case SAGE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad flag or size)";
+        case SAGE_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128, Hq % Hkv == 0, N <= 2^20)";
+        case SAGE_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+        case SAGE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

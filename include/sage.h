@@ -1,0 +1,158 @@
+/*
+ * sage.h -- C ABI of the MI355X (gfx950) 8-bit quantized attention library.
+ *
+ * The method (SageAttention, with the FP8 P.V of SageAttention2):
+ *   - K is smoothed by subtracting its per-channel mean over all tokens
+ *     (SageAttention article, paragraph on smoothing K: softmax(QK^T) equals
+ *     softmax(Q(K - mean K)^T) because the subtracted term is constant along
+ *     each row);
+ *   - Q and smoothed K are quantized to INT8 per block of rows at the flash
+ *     tile granularity and Q.K^T runs as INT8 x INT8 with INT32 accumulation
+ *     (same article, paragraph on per-block INT8 quantization of Q and K);
+ *   - the softmax is computed online in FP32;
+ *   - P and V are quantized to FP8 E4M3, V per channel and P per block, and
+ *     P.V is accumulated in two levels (SageAttention2 summary on the
+ *     INT4-quantization search page, item (4) on P and V; the Berkeley news
+ *     brief's checklist: outlier smoothing, block-wise scales, two-level
+ *     accumulation, softmax-domain scaling).
+ *
+ * Spec details the pages leave open (the CPU oracle under oracle/ follows the
+ * same ones):
+ *   - INT8: symmetric, +-127, code = rne(x * f32(127/absmax)) in float32; one
+ *     Q scale per SAGE_BQ query rows, one K scale per SAGE_BK keys; an all-zero
+ *     block has scale 0.
+ *   - FP8: OCP E4M3FN (max 448), round to nearest even.  V: one scale per
+ *     channel, code = e4m3(v * f32(448/absmax_c)).
+ *   - P: one block is one query row by SAGE_BN keys; with m the block's largest
+ *     score in log2 units (float32), the block's codes are
+ *     e4m3(2^fmaf(acc, c, f32(log2(448)) - m)) where c = f32(f32(s_q*s_k) *
+ *     f32(sm_scale*log2 e)), so the largest element codes to 448.  Level 1 is
+ *     the block's P8.V8 product (FP32 out of the matrix core); level 2 adds it,
+ *     weighted by 2^(m - running max), into FP32 registers.  The row sum is the
+ *     same weighted sum of the quantized P.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Tensors are contiguous
+ *     [B, H, N, d] with d innermost; Q has Hq heads, K and V have Hkv heads,
+ *     query head h reads kv head h / (Hq/Hkv).
+ *   - Q, K, V and out must be 16-byte aligned; the workspace 256-byte aligned.
+ *   - Supported: d in {64, 128}; N >= 1; B, Hq, Hkv >= 1; Hq % Hkv == 0;
+ *     N <= SAGE_MAX_N.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; device-side faults surface at the
+ *     caller's next synchronisation.
+ *   - Argument errors are detected on the host before any HIP call and return
+ *     a negative sage_status; nothing is enqueued then.  A failed launch
+ *     returns SAGE_ERR_HIP.  No C++ exception crosses this interface.
+ *   - Non-finite inputs give unspecified output.
+ *   - Calls that share a workspace must not overlap (same stream, or ordered).
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_BQ 128       /* query rows per Q scale (one attention work-group tile) */
+#define SAGE_BK 64        /* keys per K scale */
+#define SAGE_BN 128       /* keys per P block (one step of the attention loop) */
+#define SAGE_FP8_MAX 448  /* largest finite E4M3FN value */
+#define SAGE_MAX_N (1 << 20)
+
+typedef enum {
+    SAGE_OK = 0,
+    SAGE_ERR_INVALID_ARG = -1, /* null or misaligned pointer, bad flag, bad size */
+    SAGE_ERR_UNSUPPORTED = -2, /* d not in {64,128}, Hq % Hkv != 0, N too large */
+    SAGE_ERR_WORKSPACE = -3,   /* workspace too small or misaligned */
+    SAGE_ERR_HIP = -4          /* a HIP launch failed */
+} sage_status;
+
+typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1 } sage_dtype;
+
+typedef struct {
+    int bq, bk, bn;  /* SAGE_BQ, SAGE_BK, SAGE_BN */
+    int fp8_max;     /* 448: FP8 is OCP E4M3FN */
+    int version;     /* library version, 100 * major + minor */
+} sage_config;
+
+/*
+ * Device-side views of the quantized operands inside a workspace (filled by
+ * sage_workspace_carve).  N_p = N rounded up to a multiple of SAGE_BN; rows
+ * N..N_p-1 are zero padding.
+ *   q_i8    int8 [B, Hq, N_p, d]            row-major, d innermost
+ *   q_scale f32  [B, Hq, N_p / SAGE_BQ]
+ *   k_i8    int8 [B, Hkv, N_p, d]           codes of K - k_mean
+ *   k_scale f32  [B, Hkv, N_p / SAGE_BK]
+ *   k_mean  f32  [B, Hkv, d]
+ *   v_fp8   E4M3 [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: for each block of SAGE_BN
+ *           keys and each channel, the block's codes in the key order of
+ *           sage_v_key_position()
+ *   v_scale f32  [B, Hkv, d]                absmax / 448 per channel
+ *   v_inv   f32  [B, Hkv, d]                448 / absmax (0 for a zero channel)
+ *   k_part, v_part: per-chunk partial statistics used by sage_quantize.
+ */
+typedef struct {
+    int8_t* q_i8;
+    float* q_scale;
+    int8_t* k_i8;
+    float* k_scale;
+    float* k_mean;
+    uint8_t* v_fp8;
+    float* v_scale;
+    float* v_inv;
+    double* k_part;
+    float* v_part;
+} sage_qkv_quant;
+
+/* Bytes of workspace sage_quantize/sage_attn_fwd need for this shape (0 when
+ * the shape is invalid). */
+size_t sage_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/* Split `workspace` (device memory, 256-byte aligned, ws_bytes long) into the
+ * views above.  Host-only; no HIP call. */
+int sage_workspace_carve(void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
+                         sage_qkv_quant* out);
+
+/*
+ * The prep step (K mean, smoothing, per-block INT8 of Q and K, per-channel
+ * FP8 of V) from fp16/bf16 Q, K, V into the views of `dst`.  Memory-bound; runs
+ * as three kernels on `stream` (statistics + Q, per-head finalisation, K/V
+ * packing).
+ */
+int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
+                  int N, int d, const sage_qkv_quant* dst, void* stream);
+
+/*
+ * Attention on already-quantized operands: out = softmax(Q K^T sm_scale) V as
+ * the method computes it, FP32 output [B, Hq, N, d].  causal = 1 applies the
+ * square, top-left aligned mask j <= i.  sm_scale must be finite and > 0.
+ */
+int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq, int Hkv, int N,
+                            int d, int causal, float sm_scale, void* stream);
+
+/* Both steps: sage_quantize into `workspace`, then sage_attn_fwd_quantized. */
+int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                  int N, int d, int causal, float sm_scale, int dtype, void* workspace,
+                  size_t ws_bytes, void* stream);
+
+/* Block sizes and format constants of this build. */
+int sage_get_config(sage_config* c);
+
+/* Position of key j (0 <= j < SAGE_BN) inside a block's row of v_fp8; -1 if j
+ * is out of range.  Describes the layout only (for callers that read the
+ * quantized V back). */
+int sage_v_key_position(int j);
+
+/* Static, human-readable text for a sage_status value. */
+const char* sage_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H */
