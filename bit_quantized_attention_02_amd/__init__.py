@@ -24,7 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_HIP = 0, -1, -2, -3, -4
 SAGE_F16, SAGE_BF16 = 0, 1
-SAGE_BQ, SAGE_BK, SAGE_BN = 128, 64, 128
+SAGE_BQ, SAGE_BK, SAGE_BN, SAGE_NPAD = 128, 64, 128, 256
 
 
 class sage_config(ctypes.Structure):
@@ -34,7 +34,7 @@ class sage_config(ctypes.Structure):
 
 class sage_qkv_quant(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale", "v_inv",
+                ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_e4m3", "v_scale", "v_inv",
                  "k_part", "v_part")]
 
 
@@ -169,9 +169,10 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
 def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, Hkv: int,
                    N: int, d: int) -> dict:
     """Copy the quantized operands out of `workspace` (carved into `z`) to host
-    tensors in the plain [B,H,N,d] layout, the V block permutation undone.
-    Layout only; `*_pad` hold the padding rows N..N_p-1."""
-    Np = -(-N // SAGE_BN) * SAGE_BN
+    tensors in the plain [B,H,N,d] layout, the V block permutation undone and
+    V given back as E4M3 codes (the workspace holds their binary16 values,
+    which convert back exactly).  Layout only; `*_pad` hold rows N..N_p-1."""
+    Np = -(-N // SAGE_NPAD) * SAGE_NPAD
     base = workspace.data_ptr()
     torch.cuda.synchronize()
 
@@ -185,14 +186,15 @@ def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, 
 
     q_full = host(z.q_i8, (B, Hq, Np, d), torch.int8)
     k_full = host(z.k_i8, (B, Hkv, Np, d), torch.int8)
-    vb = host(z.v_fp8, (B, Hkv, Np // SAGE_BN, d, SAGE_BN), torch.uint8)
+    vb = host(z.v_e4m3, (B, Hkv, Np // SAGE_BN, d, SAGE_BN), torch.float16)
     perm = torch.tensor([sage_v_key_position(j) for j in range(SAGE_BN)], dtype=torch.long)
-    v_full = vb[..., perm].permute(0, 1, 2, 4, 3).reshape(B, Hkv, Np, d)
+    v_half = vb[..., perm].permute(0, 1, 2, 4, 3).reshape(B, Hkv, Np, d)
+    v_full = v_half.to(torch.float8_e4m3fn).view(torch.uint8)
     return dict(
         q_i8=q_full[:, :, :N].contiguous(), k_i8=k_full[:, :, :N].contiguous(),
-        v_fp8=v_full[:, :, :N].contiguous(),
+        v_fp8=v_full[:, :, :N].contiguous(), v_half=v_half[:, :, :N].contiguous(),
         q_pad=q_full[:, :, N:].contiguous(), k_pad=k_full[:, :, N:].contiguous(),
-        v_pad=v_full[:, :, N:].contiguous(),
+        v_pad=v_half[:, :, N:].contiguous(),
         q_scale=host(z.q_scale, (B, Hq, Np // SAGE_BQ), torch.float32),
         k_scale=host(z.k_scale, (B, Hkv, Np // SAGE_BK), torch.float32),
         k_mean=host(z.k_mean, (B, Hkv, d), torch.float32),

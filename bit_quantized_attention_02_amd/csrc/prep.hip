@@ -10,8 +10,9 @@
 //   prep_finalize per kv head: K mean and V scales from the partials, summed
 //                 in a fixed order (deterministic).
 //   prep_pack     per (kv head, 64-row block) K - mean, absmax, scale, codes;
-//                 per (kv head, 128-key block) V codes, transposed to the
-//                 attention kernel's channel-major, permuted-key layout.
+//                 per (kv head, 128-key block) V E4M3 codes, stored as the
+//                 binary16 values they denote and transposed to the attention
+//                 kernel's channel-major, permuted-key layout.
 //                 Heads are visited in the reverse order of prep_stats_q so
 //                 the second read of K and V finds the most recent heads
 //                 still in the last-level cache.
@@ -147,10 +148,10 @@ template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_pack(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s,
     const float* __restrict__ k_mean, const float* __restrict__ v_inv,
-    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint8_t* __restrict__ v_fp8) {
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint16_t* __restrict__ v_e4m3) {
     constexpr int CPR = D / 8;
     __shared__ float red[4];
-    __shared__ __attribute__((aligned(16))) uint8_t vt[D * SAGE_BN];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * SAGE_BN];
     const int tid = threadIdx.x;
     const int nkb = s.Np / SAGE_BK, nvb = s.Np / SAGE_BN;
     const int per_head = nkb + nvb;
@@ -225,18 +226,23 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
             // conversion (which gives NaN above 464) in range regardless.
             const float y0 = fminf(fmaxf(x[i] * inv[col + i], -448.0f), 448.0f);
             const float y1 = fminf(fmaxf(x[i + 1] * inv[col + i + 1], -448.0f), 448.0f);
-            const uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-            vt[(col + i) * SAGE_BN + pos] = (uint8_t)(p & 0xFFu);
-            vt[(col + i + 1) * SAGE_BN + pos] = (uint8_t)((p >> 8) & 0xFFu);
+            const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+            // the binary16 value of each E4M3 code (exact).  The pair is read
+            // as one 32-bit word: this compiler stores element [1] of the
+            // builtin's vector result from the wrong half.
+            const uint32_t h = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false));
+            vt[(col + i) * SAGE_BN + pos] = (uint16_t)(h & 0xFFFFu);
+            vt[(col + i + 1) * SAGE_BN + pos] = (uint16_t)(h >> 16);
         }
     }
     __syncthreads();
-    uint8_t* dst = v_fp8 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN);
-    constexpr int OUT_CH = D * SAGE_BN / 16 / kThreads;
+    uint16_t* dst = v_e4m3 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN);
+    constexpr int OUT_CH = D * SAGE_BN * 2 / 16 / kThreads;
 #pragma unroll
     for (int c = 0; c < OUT_CH; ++c) {
         const int e = tid + c * kThreads;
-        *reinterpret_cast<uint4*>(dst + e * 16) = *reinterpret_cast<const uint4*>(vt + e * 16);
+        *reinterpret_cast<uint4*>(dst + e * 8) = *reinterpret_cast<const uint4*>(vt + e * 8);
     }
 }
 
@@ -258,7 +264,7 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
     const int per_head = s.Np / SAGE_BK + s.Np / SAGE_BN;
     hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
                        (const uint16_t*)k, (const uint16_t*)v, s, z->k_mean, z->v_inv, z->k_i8,
-                       z->k_scale, z->v_fp8);
+                       z->k_scale, z->v_e4m3);
     return hipGetLastError();
 }
 

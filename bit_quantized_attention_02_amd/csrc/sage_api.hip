@@ -32,7 +32,7 @@ static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout: each region starts on a 256-byte boundary.
 struct Layout {
-    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale, v_inv, k_part, v_part, total;
+    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v_e4m3, v_scale, v_inv, k_part, v_part, total;
 };
 
 static Layout layout(const Shape& s) {
@@ -46,7 +46,7 @@ static Layout layout(const Shape& s) {
     const size_t Bq = (size_t)s.B * s.Hq, Bkv = (size_t)s.B * s.Hkv;
     L.q_i8 = take((size_t)s.q_elems());
     L.k_i8 = take((size_t)s.kv_elems());
-    L.v_fp8 = take((size_t)s.kv_elems());
+    L.v_e4m3 = take((size_t)s.kv_elems() * sizeof(uint16_t));
     L.q_scale = take(Bq * (s.Np / SAGE_BQ) * sizeof(float));
     L.k_scale = take(Bkv * (s.Np / SAGE_BK) * sizeof(float));
     L.k_mean = take(Bkv * s.d * sizeof(float));
@@ -60,10 +60,10 @@ static Layout layout(const Shape& s) {
 
 static int check_quant(const sage_qkv_quant* z) {
     if (!z) return SAGE_ERR_INVALID_ARG;
-    if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v_fp8 ||
+    if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v_e4m3 ||
         !z->v_scale || !z->v_inv || !z->k_part || !z->v_part)
         return SAGE_ERR_INVALID_ARG;
-    if (!aligned(z->q_i8, 16) || !aligned(z->k_i8, 16) || !aligned(z->v_fp8, 16) ||
+    if (!aligned(z->q_i8, 16) || !aligned(z->k_i8, 16) || !aligned(z->v_e4m3, 16) ||
         !aligned(z->v_scale, 16) || !aligned(z->k_part, 8))
         return SAGE_ERR_INVALID_ARG;
     return SAGE_OK;
@@ -90,7 +90,7 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->k_i8 = (int8_t*)(base + L.k_i8);
     out->k_scale = (float*)(base + L.k_scale);
     out->k_mean = (float*)(base + L.k_mean);
-    out->v_fp8 = (uint8_t*)(base + L.v_fp8);
+    out->v_e4m3 = (uint16_t*)(base + L.v_e4m3);
     out->v_scale = (float*)(base + L.v_scale);
     out->v_inv = (float*)(base + L.v_inv);
     out->k_part = (double*)(base + L.k_part);

@@ -9,13 +9,13 @@
 
 namespace sage {
 
-constexpr int kThreads = 256;      // every kernel runs 4 waves of 64
+constexpr int kThreads = 256;      // prep kernels run 4 waves of 64
 constexpr int kStatRows = 512;     // rows per partial-statistics chunk
 constexpr int kVersion = 100;
 
 struct Shape {
     int B, Hq, Hkv, N, d;
-    int Np;       // N rounded up to SAGE_BN
+    int Np;       // N rounded up to SAGE_NPAD
     int nchunk;   // statistics chunks per kv head
     long long q_elems() const { return (long long)B * Hq * Np * d; }
     long long kv_elems() const { return (long long)B * Hkv * Np * d; }
@@ -23,15 +23,16 @@ struct Shape {
 
 inline Shape make_shape(int B, int Hq, int Hkv, int N, int d) {
     Shape s{B, Hq, Hkv, N, d, 0, 0};
-    s.Np = (N + SAGE_BN - 1) / SAGE_BN * SAGE_BN;
+    s.Np = (N + SAGE_NPAD - 1) / SAGE_NPAD * SAGE_NPAD;
     s.nchunk = (N + kStatRows - 1) / kStatRows;
     return s;
 }
 
-// Position of key j inside a block's V row.  The attention kernel's P.V
-// operand for lane group g (lanes 16g..16g+15) holds, at byte b, the P value of
-// key 16*(b/4) + 4g + b%4 (that is where the Q.K^T matrix-core output leaves
-// it), so V stores the same key at position 32g + b.
+// Position of key j inside a block's V row.  After the Q.K^T product, lane
+// group g (lanes 16g..16g+15) holds the scores of keys 16*tau + 4g + v
+// (tau = 0..7, v = 0..3); its P.V operand element e = 4*tau + v therefore
+// belongs to key 16*(e/4) + 4g + e%4, and V stores that key at position
+// 32g + e, so each lane reads its V operand contiguously.
 __host__ __device__ inline int v_key_position(int j) {
     int tau = j >> 4, g = (j >> 2) & 3, v = j & 3;
     return 32 * g + 4 * tau + v;

@@ -27,9 +27,9 @@
  *     score in log2 units (float32), the block's codes are
  *     e4m3(2^fmaf(acc, c, f32(log2(448)) - m)) where c = f32(f32(s_q*s_k) *
  *     f32(sm_scale*log2 e)), so the largest element codes to 448.  Level 1 is
- *     the block's P8.V8 product (FP32 out of the matrix core); level 2 adds it,
- *     weighted by 2^(m - running max), into FP32 registers.  The row sum is the
- *     same weighted sum of the quantized P.
+ *     the block's P8.V8 product, exact products summed in FP32 by the matrix
+ *     core; level 2 adds it, weighted by 2^(m - reference max), into FP32
+ *     registers.  The row sum is the same weighted sum of the quantized P.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -58,10 +58,11 @@
 extern "C" {
 #endif
 
-#define SAGE_BQ 128       /* query rows per Q scale (one attention work-group tile) */
+#define SAGE_BQ 128       /* query rows per Q scale */
 #define SAGE_BK 64        /* keys per K scale */
 #define SAGE_BN 128       /* keys per P block (one step of the attention loop) */
 #define SAGE_FP8_MAX 448  /* largest finite E4M3FN value */
+#define SAGE_NPAD 256     /* sequence padding of the quantized operands */
 #define SAGE_MAX_N (1 << 20)
 
 typedef enum {
@@ -82,16 +83,19 @@ typedef struct {
 
 /*
  * Device-side views of the quantized operands inside a workspace (filled by
- * sage_workspace_carve).  N_p = N rounded up to a multiple of SAGE_BN; rows
+ * sage_workspace_carve).  N_p = N rounded up to a multiple of SAGE_NPAD; rows
  * N..N_p-1 are zero padding.
  *   q_i8    int8 [B, Hq, N_p, d]            row-major, d innermost
  *   q_scale f32  [B, Hq, N_p / SAGE_BQ]
  *   k_i8    int8 [B, Hkv, N_p, d]           codes of K - k_mean
  *   k_scale f32  [B, Hkv, N_p / SAGE_BK]
  *   k_mean  f32  [B, Hkv, d]
- *   v_fp8   E4M3 [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: for each block of SAGE_BN
- *           keys and each channel, the block's codes in the key order of
- *           sage_v_key_position()
+ *   v_e4m3  binary16 [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: the E4M3 codes of V,
+ *           each stored as the binary16 number it denotes (exact: every E4M3
+ *           value is a binary16 value), so the P.V product can run on the
+ *           binary16 matrix core with exact products.  For each block of
+ *           SAGE_BN keys and each channel, the block's values in the key order
+ *           of sage_v_key_position()
  *   v_scale f32  [B, Hkv, d]                absmax / 448 per channel
  *   v_inv   f32  [B, Hkv, d]                448 / absmax (0 for a zero channel)
  *   k_part, v_part: per-chunk partial statistics used by sage_quantize.
@@ -102,7 +106,7 @@ typedef struct {
     int8_t* k_i8;
     float* k_scale;
     float* k_mean;
-    uint8_t* v_fp8;
+    uint16_t* v_e4m3;
     float* v_scale;
     float* v_inv;
     double* k_part;
@@ -143,7 +147,7 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
 /* Block sizes and format constants of this build. */
 int sage_get_config(sage_config* c);
 
-/* Position of key j (0 <= j < SAGE_BN) inside a block's row of v_fp8; -1 if j
+/* Position of key j (0 <= j < SAGE_BN) inside a block's row of v_e4m3; -1 if j
  * is out of range.  Describes the layout only (for callers that read the
  * quantized V back). */
 int sage_v_key_position(int j);

@@ -56,6 +56,8 @@ def check_prep(orc, quant, oz):
     np.testing.assert_array_equal(quant["q_scale"].numpy()[..., :nqb], oz["q_scale"])
     np.testing.assert_array_equal(quant["k_scale"].numpy()[..., :nkb], oz["k_scale"])
     assert not quant["q_pad"].any() and not quant["k_pad"].any() and not quant["v_pad"].any()
+    # the binary16 copies denote exactly the E4M3 values of the codes
+    np.testing.assert_array_equal(quant["v_half"].to(torch.float64).numpy(), orc.e4m3_decode(oz["v_fp8"]))
 
 
 def check_attn(orc, out_rows, oz, causal, sm_scale, rows):
