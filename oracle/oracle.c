@@ -26,16 +26,20 @@
  *     saturating at +-448; V codes are e4m3(v * (448/absmax_c)) in float32.
  *   - The P block is one query row by `bn` keys.  Its scale is the block
  *     maximum over 448: with mt the block's largest score (log2 units,
- *     float32), P8 = e4m3(2^x), x = fmaf(acc, c, log2(448) - mt), so the
- *     largest element codes to exactly 448, and the block enters the second
+ *     float32), P8 = e4m3(2^x), x ~ acc*c + log2(448) - mt, so the largest
+ *     element codes to exactly 448, and the block enters the second
  *     accumulation level with weight 2^(mt - M), M the row maximum.  The row
  *     sum l is the same two-level sum over the quantised P, so the quantised
  *     weights are normalised exactly.  See oracle_attn_q.
- *   - The exponent argument x is defined on float32 exactly as above so that
- *     both sides take the P8 decision on the same number; only 2^x itself is
- *     evaluated differently (float64 here).  Codes whose 2^x lies within a
- *     relative `tau` of a rounding midpoint have two correct values; the
- *     oracle returns the interval spanned by both choices.
+ *   - The score enters float32 as F = 1.5*2^23 + acc, which is exact: the
+ *     matrix core's INT32 accumulator is seeded with that constant's bit
+ *     pattern and read as a float32, which saves a conversion per score.  The
+ *     exponent argument x and the block maximum mt are then defined by the
+ *     float32 operations written in oracle_attn_q, so that both sides take the
+ *     P8 decision on the same number; only 2^x itself is evaluated
+ *     differently (float64 here).  Codes whose 2^x lies within a relative
+ *     `tau` of a rounding midpoint have two correct values; the oracle
+ *     returns the interval spanned by both choices.
  */
 #include <math.h>
 #include <stdint.h>
@@ -196,10 +200,11 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  *
  *   acc_j = sum_c q_i8[i,c] * k_i8[j,c]                       (exact integer)
  *   c_j   = f32( f32(sq * sk[j/bk]) * f32(sm_scale*log2 e) )   (float32)
- *   blocks t of bn keys; s_j = f32(acc_j * c_j); m_t = max over the block's
- *   allowed keys; bias_t = f32(f32(log2 448) - m_t)
- *   x_j   = fmaf(acc_j, c_j, bias_t);  y_j = 2^x_j (float64)
- *   P8_j  = e4m3(y_j)                  (the block maximum codes to 448)
+ *   F_j   = 1.5*2^23 + acc_j (exact in float32), u_j = f32(1.5*2^23 * c_j)
+ *   s_j   = fmaf(F_j, c_j, -u_j)       (= acc_j * c_j up to float32 rounding)
+ *   blocks t of bn keys; m_t = max of s_j over the block's allowed keys
+ *   x_j   = fmaf(F_j, c_j, f32(f32(f32(log2 448) - m_t) - u_j))
+ *   y_j   = 2^x_j (float64);  P8_j = e4m3(y_j)   (the block maximum codes to 448)
  *   level 1: A_t[c] = sum_{j in t} P8_j * V8[j,c];  R_t = sum_{j in t} P8_j
  *   level 2: with M = max_t m_t and w_t = 2^(m_t - M) (float64),
  *            O[c] = sum_t w_t A_t[c],  l = sum_t w_t R_t
@@ -222,6 +227,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
     const int nqb = (N + bq - 1) / bq, nkb = (N + bk - 1) / bk;
     const float qk = (float)((double)sm_scale * 1.4426950408889634); /* log2(e) */
     const float l448 = (float)log2(448.0);
+    const float seed = 12582912.0f; /* 1.5 * 2^23 */
     double dec[256];
     for (int i = 0; i < 256; ++i) dec[i] = oracle_e4m3_decode((uint8_t)i);
     if (rows == NULL) nrows = (long)B * Hq * N;
@@ -230,6 +236,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
     {
         int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
         float* cj = (float*)malloc(sizeof(float) * (size_t)N);
+        float* Fj = (float*)malloc(sizeof(float) * (size_t)N);
+        float* uj = (float*)malloc(sizeof(float) * (size_t)N);
         float* mblk = (float*)malloc(sizeof(float) * (size_t)(N / bn + 2));
         double* A = (double*)malloc(sizeof(double) * (size_t)d);
         double* O = (double*)malloc(sizeof(double) * (size_t)d);
@@ -259,6 +267,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 acc[j] = s;
                 float sqk = sq * skh[j / bk];
                 cj[j] = sqk * qk;
+                Fj[j] = (float)(12582912 + s);
+                uj[j] = seed * cj[j];
             }
             /* per-block maximum score: the P scale of the block */
             float M = -INFINITY;
@@ -266,7 +276,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 int j0 = t * bn, j1 = j0 + bn - 1 < jmax ? j0 + bn - 1 : jmax;
                 float mt = -INFINITY;
                 for (int j = j0; j <= j1; ++j) {
-                    float s = (float)acc[j] * cj[j];
+                    float s = fmaf(Fj[j], cj[j], -uj[j]);
                     if (s > mt) mt = s;
                 }
                 mblk[t] = mt;
@@ -283,7 +293,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 double R = 0.0;
                 for (int c = 0; c < d; ++c) A[c] = 0.0;
                 for (int j = j0; j <= j1; ++j) {
-                    float x = fmaf((float)acc[j], cj[j], bias);
+                    float x = fmaf(Fj[j], cj[j], bias - uj[j]);
                     double y = exp2((double)x);
                     uint8_t code = oracle_e4m3_encode(y);
                     double p = dec[code];
@@ -333,6 +343,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
         }
         free(acc);
         free(cj);
+        free(Fj);
+        free(uj);
         free(mblk);
         free(A);
         free(O);

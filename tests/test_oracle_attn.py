@@ -113,7 +113,14 @@ def test_blockwise_constant_keys_give_weighted_block_means(orc, causal):
     qd, kd, vd = _deq_inputs(orc, z)
     ref = orc.attn_f64(qd, kd, vd, causal, 0.125)
     assert fl.sum() == 0
-    np.testing.assert_allclose(out, ref, rtol=0, atol=2e-5 * np.abs(ref).max())
+    # the block weights carry the float32 evaluation of the exponent: its
+    # constant offset u = f32(1.5 2^23 c) is rounded, so each block's log2
+    # weight is off by at most ~3 ulp(u); the weighted mean moves by at most
+    # twice that relative error times max|V|
+    c_max = float(z["q_scale"].max()) * float(z["k_scale"].max()) * 0.125 * math.log2(math.e)
+    ulp_u = 2.0 ** (math.floor(math.log2(12582912 * c_max)) - 23)
+    eps = 3 * ulp_u * math.log(2)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=2 * eps * np.abs(vd).max() + 1e-12)
 
 
 # ----------------------------------------------------------------------------
@@ -162,12 +169,16 @@ def _online_reference(orc, z, causal, sm_scale, bn):
                         c = np.float32(np.float32(s_q * z["k_scale"][b, g, j // z["bk"]]) * qk)
                         accs.append(acc)
                         cs.append(c)
-                    mt = max(np.float32(np.float32(a) * c) for a, c in zip(accs, cs))
-                    bias = np.float32(l448 - mt)
+                    # the score enters float32 as F = 1.5 2^23 + acc (exact),
+                    # with the constant's product u = f32(1.5 2^23 c) taken off
+                    Fs = [np.float32(12582912 + a) for a in accs]
+                    us = [np.float32(np.float32(12582912.0) * c) for c in cs]
+                    mt = max(_fma_f32(F, c, -u) for F, c, u in zip(Fs, cs, us))
                     a_blk = np.zeros(d)
                     r_blk = 0.0
-                    for j, acc, c in zip(blk, accs, cs):
-                        y = 2.0 ** float(_fma_f32(np.float32(acc), c, bias))
+                    for j, F, c, u in zip(blk, Fs, cs, us):
+                        bias = np.float32(np.float32(l448 - mt) - u)
+                        y = 2.0 ** float(_fma_f32(F, c, bias))
                         p = vals[orc.e4m3_encode(np.array([y]))[0]]
                         a_blk += p * vals[z["v_fp8"][b, g, j]]
                         r_blk += p
