@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsage.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_attention_02_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python bit_quantized_attention_02_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

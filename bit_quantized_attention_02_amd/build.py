@@ -1,6 +1,8 @@
 """Build libsage.so (the HIP library behind include/sage.h) for gfx950, in-tree.
 
-    python -m bit_quantized_attention_02_amd.build
+    python bit_quantized_attention_02_amd/build.py
+
+(Run it by path: importing the package loads the library this script builds.)
 
 Each .hip source is compiled to an object with hipcc, then linked into one
 shared library next to this file.  Packed FP32 instructions are disabled

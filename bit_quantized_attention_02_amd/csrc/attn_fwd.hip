@@ -10,9 +10,11 @@
 //   2. S^T = K Q^T on v_mfma_i32_16x16x64_i8 (INT8 x INT8 -> INT32, exact).
 //      With keys on the M side every lane holds 32 scores of ONE query row, so
 //      row maxima are in-lane plus two permlane swaps;
-//   3. online softmax in FP32: block maximum m (on the INT32 scores, scaled per
-//      K-scale half), P8 = e4m3(2^(s*c + log2(448) - m)), so the block's largest
-//      element codes to exactly 448 (the E4M3 P with a per-block scale);
+//   3. online softmax in FP32: the INT32 accumulator is seeded with the bit
+//      pattern of 1.5*2^23, so each score reads as the float32 1.5*2^23 + acc
+//      with no conversion; block maximum m (on the integer patterns, scaled per
+//      K-scale half), P8 = e4m3(2^(acc*c + log2(448) - m)), so the block's
+//      largest element codes to exactly 448 (the E4M3 P with a per-block scale);
 //   4. level 1: the block's P8.V8 product on v_mfma_f32_16x16x32_f16 -- the
 //      E4M3 values are exact in binary16 and that matrix core sums the exact
 //      products in FP32 (gfx950's FP8 matrix core truncates its internal sum to
@@ -34,6 +36,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr float kLazyRescale = 8.0f;
+constexpr float kSeed = 12582912.0f;   // 1.5 * 2^23
+constexpr int kSeedBits = 0x4B400000;  // its float32 bit pattern
 
 struct AttnArgs {
     const int8_t* q_i8;
@@ -54,34 +58,51 @@ __device__ inline int kswz(int row) {
     return D == 64 ? ((row >> 1) & 3) : (row & 7);
 }
 
-// Copy one key block (K: 128 rows x D bytes, V: D rows x 128 binary16) into LDS.
+// Copies key blocks (K: 128 rows x D bytes, V: D rows x 128 binary16) of one
+// kv head into LDS with buffer loads that write LDS directly.  Each lane's
+// byte offsets inside a block are fixed, so a block costs no vector ALU work:
+// the block's base goes in the scalar offset.
 template <int D, int WAVES>
-__device__ inline void load_block(const uint8_t* kg, const uint16_t* vg, uint8_t* lk, uint16_t* lv,
-                                  int wave, int lane) {
-    constexpr int NT = 64 * WAVES;
-    constexpr int KCH = SAGE_BN * D / 16;
-    constexpr int VCH = D * SAGE_BN * 2 / 16;
-    static_assert(KCH % NT == 0 && VCH % NT == 0, "tile must split evenly over the work-group");
+struct TileLoader {
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int KR = SAGE_BN * D / 16 / NT;      // 16-byte chunks per lane, K
+    static constexpr int VR = D * SAGE_BN * 2 / 16 / NT;  // and V
+    static_assert(KR * NT * 16 == SAGE_BN * D && VR * NT * 16 == D * SAGE_BN * 2,
+                  "tile must split evenly over the work-group");
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    uint32_t koff[KR], voff[VR];
+
+    __device__ TileLoader(const uint8_t* kg, const uint16_t* vg, int head_rows, int wave, int lane) {
+        krs = __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_rows * D, 0x00020000);
+        vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_rows * D * 2, 0x00020000);
 #pragma unroll
-    for (int r = 0; r < KCH / NT; ++r) {
-        const int p = r * NT + wave * 64 + lane;
-        const int row = p / (D / 16), qs = p % (D / 16);
-        const int q = qs ^ kswz<D>(row);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(kg + row * D + q * 16),
-            (__attribute__((address_space(3))) void*)(lk + (r * NT + wave * 64) * 16), 16, 0, 0);
-    }
+        for (int r = 0; r < KR; ++r) {
+            // LDS chunk p of the K tile holds chunk p ^ swizzle of its row
+            const int p = r * NT + wave * 64 + lane;
+            const int row = p / (D / 16), qs = p % (D / 16);
+            koff[r] = row * D + ((qs ^ kswz<D>(row)) << 4);
+        }
 #pragma unroll
-    for (int r = 0; r < VCH / NT; ++r) {
-        const int p = r * NT + wave * 64 + lane;
-        const int c = p >> 4, qs = p & 15;
-        const int q = qs ^ (c & 7);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)((const uint8_t*)vg + c * (SAGE_BN * 2) + q * 16),
-            (__attribute__((address_space(3))) void*)((uint8_t*)lv + (r * NT + wave * 64) * 16), 16,
-            0, 0);
+        for (int r = 0; r < VR; ++r) {
+            const int p = r * NT + wave * 64 + lane;
+            const int c = p >> 4, qs = p & 15;
+            voff[r] = c * (SAGE_BN * 2) + ((qs ^ (c & 7)) << 4);
+        }
     }
-}
+
+    __device__ inline void load(int T, uint8_t* lk, uint16_t* lv, int wave) const {
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                krs, (__attribute__((address_space(3))) void*)(lk + (r * NT + wave * 64) * 16), 16,
+                koff[r], T * SAGE_BN * D, 0, 0);
+#pragma unroll
+        for (int r = 0; r < VR; ++r)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vrs, (__attribute__((address_space(3))) void*)((uint8_t*)lv + (r * NT + wave * 64) * 16),
+                16, voff[r], T * SAGE_BN * D * 2, 0, 0);
+    }
+};
 
 __device__ inline int max_across_row(int x) {
     // the 4 lanes that hold one query row are l, l^16, l^32, l^48
@@ -101,6 +122,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            float (&mref)[2], float (&lsum)[2],
                                            v4f (&O)[2][D / 16]) {
     constexpr int KK = D / 64, CT = D / 16;
+    const float u0 = kSeed * c0, u1 = kSeed * c1;
 
     // ---- S^T = K Q^T (INT32)
     v4i S[2][8];
@@ -113,7 +135,9 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
             kf[kk] = *reinterpret_cast<const v4i*>(lk + row * D + (((4 * kk + g16) ^ kswz<D>(row)) << 4));
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
-            v4i acc = {0, 0, 0, 0};
+            // seeded with the bit pattern of 1.5*2^23: the INT32 result, read
+            // as a float32, is exactly 1.5*2^23 + acc (|acc| < 2^22)
+            v4i acc = {kSeedBits, kSeedBits, kSeedBits, kSeedBits};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[kk], qf[qg][kk], acc, 0, 0, 0);
@@ -147,7 +171,8 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
             }
         M0 = max_across_row(M0);
         M1 = max_across_row(M1);
-        float m0 = (float)M0 * c0, m1 = (float)M1 * c1;
+        float m0 = __builtin_fmaf(__builtin_bit_cast(float, M0), c0, -u0);
+        float m1 = __builtin_fmaf(__builtin_bit_cast(float, M1), c1, -u1);
         if (MASKED) {
             if (M0 == INT32_MIN) m0 = -INFINITY;
             if (M1 == INT32_MIN) m1 = -INFINITY;
@@ -174,38 +199,43 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
         w[qg] = mt[qg] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mt[qg] - nr);
     }
 
-    // ---- P: E4M3 codes, as binary16 operands (pairs of binary16 per int)
-    int pd[2][8][2];
-#pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        const float bias = l448 - mt[qg];
-#pragma unroll
-        for (int tau = 0; tau < 8; ++tau) {
-            const float c = tau < 4 ? c0 : c1;
-            float y[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                y[v] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[qg][tau][v], c, bias));
-                if (MASKED && S[qg][tau][v] == INT32_MIN) y[v] = 0.0f;
-            }
-            // the first conversion writes the low half; the high half of its
-            // destination is then written by the second, so the register's old
-            // contents never matter (the builtin would zero it first)
-            int code;
-            asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(code) : "v"(y[0]), "v"(y[1]));
-            code = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], code, true);
-            pd[qg][tau][0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false));
-            pd[qg][tau][1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
-        }
-    }
+    // ---- P: E4M3 codes, as binary16 operands.  Piece p of a row group is
+    // the 8 values of tiles 2p and 2p+1, in the order of v_key_position.
     v8h P[2][4];
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg)
+    for (int qg = 0; qg < 2; ++qg) {
+        const float e = l448 - mt[qg];
+        const float bias0 = e - u0, bias1 = e - u1;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const v4i d4 = {pd[qg][2 * p][0], pd[qg][2 * p][1], pd[qg][2 * p + 1][0], pd[qg][2 * p + 1][1]};
-            P[qg][p] = __builtin_bit_cast(v8h, d4);
+            v4i quad;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int tau = 2 * p + half;
+                const float c = tau < 4 ? c0 : c1;
+                const float bias = tau < 4 ? bias0 : bias1;
+                float y[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    // (bit_cast of the whole vector: this compiler mis-reads a
+                    // bit_cast of a single vector element as element 0)
+                    const float F = __builtin_bit_cast(v4f, S[qg][tau])[v];
+                    y[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(F, c, bias));
+                    if (MASKED && S[qg][tau][v] == INT32_MIN) y[v] = 0.0f;
+                }
+                // the first conversion writes the low half; the high half of
+                // its destination is then written by the second, so the
+                // register's old contents never matter (the builtin would zero
+                // it first)
+                int code;
+                asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(code) : "v"(y[0]), "v"(y[1]));
+                code = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], code, true);
+                quad[2 * half] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false));
+                quad[2 * half + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
+            }
+            P[qg][p] = __builtin_bit_cast(v8h, quad);
         }
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- level 1 on the matrix core, level 2 in FP32 registers
@@ -301,25 +331,34 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_fwd(AttnArgs a) {
         for (int ct = 0; ct < CT; ++ct) O[qg][ct] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    load_block<D, WAVES>(kbase, vbase, lk0, lv0, wave, lane);
+    const TileLoader<D, WAVES> tiles(kbase, vbase, a.Np, wave, lane);
+    tiles.load(0, lk0, lv0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int T = 0; T < nblk; ++T) {
+    // Blocks [0, nA) need no mask for any wave of the work-group: a loop of
+    // its own keeps that body free of per-wave branches.
+    const int nA = CAUSAL ? min(q0 / SAGE_BN, a.N / SAGE_BN) : a.N / SAGE_BN;
+    int T = 0;
+    for (; T < nA; ++T) {
         const bool odd = T & 1;
-        if (T + 1 < nblk)
-            load_block<D, WAVES>(kbase + (long long)(T + 1) * SAGE_BN * D,
-                                 vbase + (long long)(T + 1) * SAGE_BN * D, odd ? lk0 : lk1,
-                                 odd ? lv0 : lv1, wave, lane);
-        const uint8_t* lk = odd ? lk1 : lk0;
-        const uint16_t* lv = odd ? lv1 : lv0;
+        if (T + 1 < nblk) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
+        const float c0 = (sq * ksc[2 * T]) * a.qk, c1 = (sq * ksc[2 * T + 1]) * a.qk;
+        attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, rbase + r16, a.N, c0,
+                                     c1, a.l448, g16, r16, mref, lsum, O);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    for (; T < nblk; ++T) {
+        const bool odd = T & 1;
+        if (T + 1 < nblk) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
         const float c0 = (sq * ksc[2 * T]) * a.qk, c1 = (sq * ksc[2 * T + 1]) * a.qk;
         if (T < n_full)
-            attn_block<D, CAUSAL, false>(lk, lv, qf, T, rbase + r16, a.N, c0, c1, a.l448, g16, r16,
-                                         mref, lsum, O);
+            attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, rbase + r16, a.N,
+                                         c0, c1, a.l448, g16, r16, mref, lsum, O);
         else if (T <= wave_last)
-            attn_block<D, CAUSAL, true>(lk, lv, qf, T, rbase + r16, a.N, c0, c1, a.l448, g16, r16,
-                                        mref, lsum, O);
+            attn_block<D, CAUSAL, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, rbase + r16, a.N,
+                                        c0, c1, a.l448, g16, r16, mref, lsum, O);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
@@ -346,13 +385,29 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_fwd(AttnArgs a) {
     }
 }
 
-#ifndef SAGE_ATTN_WAVES
-#define SAGE_ATTN_WAVES 8
+// d = 64: 4-wave work-groups, two per CU (48 KB of LDS each), whose waves
+// interleave on each SIMD.  d = 128: the 96 KB of LDS allow one work-group
+// per CU, so it runs 8 waves (2 per SIMD).
+template <int D>
+constexpr int attn_waves() {
+#ifdef SAGE_ATTN_WAVES
+    return SAGE_ATTN_WAVES;
+#else
+    return D == 64 ? 4 : 8;
 #endif
+}
+
+// Explicit instantiations: with the packed-FP32 feature switched off on the
+// command line, this compiler otherwise leaves the host stubs of some of these
+// kernels undefined.
+template __global__ void attn_fwd<64, false, attn_waves<64>()>(AttnArgs);
+template __global__ void attn_fwd<64, true, attn_waves<64>()>(AttnArgs);
+template __global__ void attn_fwd<128, false, attn_waves<128>()>(AttnArgs);
+template __global__ void attn_fwd<128, true, attn_waves<128>()>(AttnArgs);
 
 template <int D, bool CAUSAL>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
-    constexpr int WAVES = SAGE_ATTN_WAVES;
+    constexpr int WAVES = attn_waves<D>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
     if (lds > 65536) {
