@@ -38,7 +38,25 @@ def parse():
                    help="1..5; 3 is the non-causal N=17550 video-diffusion shape")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="instead of the benchmark, run a plain device-to-device copy of BYTES "
+                        "bytes 5 times: a known-size reference for hardware byte counters")
     return p.parse_args()
+
+
+def measured_traffic(kernel_source):
+    """HBM bytes per attention launch from the committed byte-counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    import glob
+    import hashlib
+    src = open(kernel_source, "rb").read()
+    digest = hashlib.sha256(src).hexdigest()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "attn_fwd_*_counters.json")):
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("kernel_source_sha256") == digest:
+            return d.get("workload"), d.get("traffic_bytes_per_launch")
+    return None, None
 
 
 def timed(fn, iters, torch):
@@ -98,6 +116,15 @@ def main():
     import bit_quantized_attention_02_amd as sage
     import workloads
 
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 5}), flush=True)
+        return
+
     w = workloads.WORKLOADS[args.workload]
     q, k, v = workloads.generate(w)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
@@ -119,6 +146,10 @@ def main():
     ms_prep = timed(lambda: sage.sage_quantize(qd, kd, vd, z), args.steps, torch)
     ms_attn = timed(lambda: sage.sage_attn_fwd_quantized(z, out, w.B, w.Hq, w.Hkv, w.N, w.d,
                                                          w.causal, w.sm_scale), args.steps, torch)
+    traffic_wl, traffic = measured_traffic(
+        os.path.join(ROOT, "bit_quantized_attention_02_amd", "csrc", "attn_fwd.hip"))
+    if traffic_wl != w.name:
+        traffic = None
     tops = w.ops / (ms_step * 1e-3) / 1e12
     attn_tops = w.ops / (ms_attn * 1e-3) / 1e12
     elems = (w.B * w.Hq + 2 * w.B * w.Hkv) * w.N * w.d
@@ -128,12 +159,12 @@ def main():
         "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8xi8->i32 + e4m3xe4m3->f32", "data": "synthetic",
+        "dtype": "i8 (QK^T, i32 acc) + e4m3 values (P.V, f32 acc)", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "input_dtype": w.dtype, "sm_scale": w.sm_scale,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd", "ms_per_launch": round(ms_attn, 4)},
         "prep": {"ms_per_launch": round(ms_prep, 4), "alg_GBps": round(prep_gbs, 1),
                  "frac_hbm": round(prep_gbs / HBM_PEAK_GBS, 4)},

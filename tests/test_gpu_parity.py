@@ -131,3 +131,38 @@ def test_sage_attn_fwd_matches_two_step_path(sage):
     two, _ = run_gpu(sage, q.cpu(), k.cpu(), v.cpu(), True, w.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(one, two)
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_parity_full_size_workloads(sage, orc, index):
+    """Each workload at its full size, through sage_attn_fwd as the benchmark
+    times it: the prep outputs are compared in full (bit-exact), the attention
+    output on sampled rows the oracle computes one by one (first and last row
+    of the first and last head, 256 seeded rows, and for the peaked-row recipe
+    some of the x20 rows)."""
+    w = workloads.WORKLOADS[index]
+    _say(f"case full-size workload {index} {w.name}")
+    q, k, v = workloads.generate(w)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    ws = sage.workspace_for(qd, kd)
+    sage.sage_attn_fwd(qd, kd, vd, out, w.causal, w.sm_scale, ws)
+    torch.cuda.synchronize()
+    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d)
+    quant = sage.read_quantized(z, ws, w.B, w.Hq, w.Hkv, w.N, w.d)
+    del qd, kd, vd
+    oz = orc.quantize(q, k, v)
+    check_prep(orc, quant, oz)
+    rows = workloads.sample_rows(w, 256, seed=11)
+    if w.recipe == 4:
+        # rows scaled x20 in the first head: the largest |Q| rows
+        qn = q[0, 0].float().abs().amax(dim=-1)
+        hot = torch.nonzero(qn > 4 * qn.median()).flatten()[:32].numpy().astype(np.int64)
+        rows = np.unique(np.concatenate([rows, hot]))
+    got = out.reshape(-1, w.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    nom = check_attn(orc, got, oz, w.causal, w.sm_scale, rows)
+    # the method's accuracy against full precision (reported, not a parity bar)
+    ref = orc.attn_f64(q, k, v, w.causal, w.sm_scale, rows=rows)
+    a_gpu, a_orc = orc.accuracy(got, ref), orc.accuracy(nom, ref)
+    _say(f"   vs float64: gpu cos={a_gpu['cos']:.6f} relL1={a_gpu['rel_l1']:.4f}; "
+         f"oracle cos={a_orc['cos']:.6f} relL1={a_orc['rel_l1']:.4f}")
