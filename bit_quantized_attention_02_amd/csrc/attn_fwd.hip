@@ -1,38 +1,42 @@
 // Fused 8-bit attention forward for CDNA4 (gfx950).
 //
 // One work-group = WAVES waves = 32*WAVES query rows of one (batch, q head);
-// each wave owns 32 rows as two 16-row groups.  The loop runs over blocks of
-// SAGE_BN (128) keys:
+// each wave owns 32 rows, one 32-wide matrix-core tile.  The loop runs over
+// blocks of SAGE_BN (128) keys:
 //   1. the next block's INT8 K tile [128 x d] and V tile [d x 128] (binary16
-//      copies of the E4M3 codes) are copied global -> LDS with global_load_lds,
-//      double-buffered, with 16-byte chunks XOR-swizzled so the fragment reads
-//      are free of bank conflicts;
-//   2. S^T = K Q^T on v_mfma_i32_16x16x64_i8 (INT8 x INT8 -> INT32, exact).
-//      With keys on the M side every lane holds 32 scores of ONE query row, so
-//      row maxima are in-lane plus two permlane swaps;
+//      copies of the E4M3 codes) are copied global -> LDS by buffer loads that
+//      write LDS directly, double-buffered, with 16-byte chunks XOR-swizzled
+//      so the fragment reads are free of bank conflicts;
+//   2. S^T = K Q^T on v_mfma_i32_32x32x32_i8 (INT8 x INT8 -> INT32, exact).
+//      With keys on the M side every lane holds 64 scores of ONE query row,
+//      and the other 64 sit in the lane 32 apart: a row maximum is in-lane
+//      work plus one permlane32 swap;
 //   3. online softmax in FP32: the INT32 accumulator is seeded with the bit
 //      pattern of 1.5*2^23, so each score reads as the float32 1.5*2^23 + acc
 //      with no conversion; block maximum m (on the integer patterns, scaled per
 //      K-scale half), P8 = e4m3(2^(acc*c + log2(448) - m)), so the block's
 //      largest element codes to exactly 448 (the E4M3 P with a per-block scale);
-//   4. level 1: the block's P8.V8 product on v_mfma_f32_16x16x32_f16 -- the
+//   4. level 1: the block's P8.V8 product on v_mfma_f32_32x32x16_f16 -- the
 //      E4M3 values are exact in binary16 and that matrix core sums the exact
 //      products in FP32 (gfx950's FP8 matrix core truncates its internal sum to
 //      about 2^-11 of the largest product, too coarse for rows dominated by a
 //      single key); level 2: the FP32 register update O += w * acc with
 //      w = 2^(m - reference max).  The row sum of P comes out of the same
 //      matrix core (an all-ones operand), so the quantized weights are
-//      normalised exactly.
+//      normalised exactly.  P is converted 16 keys at a time and each piece
+//      goes to the matrix core at once, so the conversions of one piece run
+//      while the products of the previous one are in flight.
 // The reference max is raised lazily, only when a block's maximum exceeds it
 // by more than 8 (log2 units), so O is rescaled rarely.
-// The P operand a lane feeds to P.V is exactly the 32 scores it computed, so
+// The P operand a lane feeds to P.V is exactly the scores it computed, so
 // nothing moves between lanes; V is stored by the prep kernel in that order.
 #include "sage_internal.h"
 
 namespace sage {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr float kLazyRescale = 8.0f;
@@ -52,11 +56,15 @@ struct AttnArgs {
     float l448;  // f32(log2 448)
 };
 
-// XOR swizzle of the 16-byte chunks of one K-tile row (d bytes long).
+// XOR swizzle of the 16-byte chunks of one K-tile row (d bytes long): the 16
+// lanes of one LDS read phase (16 consecutive rows, same chunk) land on 16
+// different 16-byte bank groups.
 template <int D>
 __device__ inline int kswz(int row) {
-    return D == 64 ? ((row >> 1) & 3) : (row & 7);
+    return D == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
 }
+// and of one V-tile row (a channel, 128 binary16 = 16 chunks)
+__device__ inline int vswz(int ch) { return ch & 15; }
 
 // Copies key blocks (K: 128 rows x D bytes, V: D rows x 128 binary16) of one
 // kv head into LDS with buffer loads that write LDS directly.  Each lane's
@@ -86,7 +94,7 @@ struct TileLoader {
         for (int r = 0; r < VR; ++r) {
             const int p = r * NT + wave * 64 + lane;
             const int c = p >> 4, qs = p & 15;
-            voff[r] = c * (SAGE_BN * 2) + ((qs ^ (c & 7)) << 4);
+            voff[r] = c * (SAGE_BN * 2) + ((qs ^ vswz(c)) << 4);
         }
     }
 
@@ -104,173 +112,164 @@ struct TileLoader {
     }
 };
 
-__device__ inline int max_across_row(int x) {
-    // the 4 lanes that hold one query row are l, l^16, l^32, l^48
+// Maximum over the two lanes (l, l^32) that hold one query row.
+__device__ inline int max_across_halves(int x) {
     auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    x = max((int)a[0], (int)a[1]);
-    auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return max((int)b[0], (int)b[1]);
+    return max((int)a[0], (int)a[1]);
 }
 
-// One key block for one wave (two 16-row groups).  MASKED: some keys of the
+// One key block for one wave (32 query rows).  MASKED: some keys of the
 // block are excluded (causal diagonal, or keys >= N).
 template <int D, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const uint16_t* __restrict__ lv,
-                                           const v4i (&qf)[2][D / 64], int T, int row0, int N,
-                                           float c0, float c1, float l448, int g16, int r16,
-                                           float (&mref)[2], float (&lsum)[2],
-                                           v4f (&O)[2][D / 16]) {
-    constexpr int KK = D / 64, CT = D / 16;
+                                           const v4i (&qf)[D / 32], int T, int row, int N,
+                                           float c0, float c1, float l448, int h, int r32,
+                                           float& mref, float& lsum, v16f (&O)[D / 32]) {
+    constexpr int KS = D / 32, CT = D / 32;
     const float u0 = kSeed * c0, u1 = kSeed * c1;
 
-    // ---- S^T = K Q^T (INT32)
-    v4i S[2][8];
+    // ---- S^T = K Q^T (INT32).  Tile t, element v: key 32t + 8(v/4) + 4h + v%4.
+    v16i S[4];
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) {
-        const int row = 16 * tau + r16;
-        v4i kf[KK];
+    for (int t = 0; t < 4; ++t) {
+        const int kr = 32 * t + r32;
+        // seeded with the bit pattern of 1.5*2^23: the INT32 result, read as a
+        // float32, is exactly 1.5*2^23 + acc (|acc| < 2^22)
+        v16i acc;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            kf[kk] = *reinterpret_cast<const v4i*>(lk + row * D + (((4 * kk + g16) ^ kswz<D>(row)) << 4));
+        for (int v = 0; v < 16; ++v) acc[v] = kSeedBits;
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
-            // seeded with the bit pattern of 1.5*2^23: the INT32 result, read
-            // as a float32, is exactly 1.5*2^23 + acc (|acc| < 2^22)
-            v4i acc = {kSeedBits, kSeedBits, kSeedBits, kSeedBits};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[kk], qf[qg][kk], acc, 0, 0, 0);
-            S[qg][tau] = acc;
+        for (int ks = 0; ks < KS; ++ks) {
+            const v4i kf = *reinterpret_cast<const v4i*>(lk + kr * D + (((2 * ks + h) ^ kswz<D>(kr)) << 4));
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ks], acc, 0, 0, 0);
         }
+        S[t] = acc;
     }
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- block maxima
-    float mt[2];
+    // ---- block maxima, one per K-scale half (tiles 0-1 and 2-3)
+    if (MASKED) {
+        const int rel = row - T * SAGE_BN;  // this lane's row, relative to the block
+        const int lim = N - T * SAGE_BN;    // keys at or past this are padding
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        if (MASKED) {
-            const int rel = row0 + 16 * qg - T * SAGE_BN;  // this lane's row, relative to the block
-            const int lim = N - T * SAGE_BN;                // keys at or past this are padding
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int tau = 0; tau < 8; ++tau)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int kr = 16 * tau + 4 * g16 + v;
-                    if ((CAUSAL && kr > rel) || kr >= lim) S[qg][tau][v] = INT32_MIN;
-                }
-        }
-        int M0 = S[qg][0][0], M1 = S[qg][4][0];
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                M0 = max(M0, S[qg][tau][v]);
-                M1 = max(M1, S[qg][tau + 4][v]);
+            for (int v = 0; v < 16; ++v) {
+                const int kr = 32 * t + 8 * (v >> 2) + 4 * h + (v & 3);
+                if ((CAUSAL && kr > rel) || kr >= lim) S[t][v] = INT32_MIN;
             }
-        M0 = max_across_row(M0);
-        M1 = max_across_row(M1);
-        float m0 = __builtin_fmaf(__builtin_bit_cast(float, M0), c0, -u0);
-        float m1 = __builtin_fmaf(__builtin_bit_cast(float, M1), c1, -u1);
-        if (MASKED) {
-            if (M0 == INT32_MIN) m0 = -INFINITY;
-            if (M1 == INT32_MIN) m1 = -INFINITY;
-        }
-        mt[qg] = fmaxf(m0, m1);
     }
+    int M0 = S[0][0], M1 = S[2][0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) {
+        M0 = max(M0, S[0][v]);
+        M1 = max(M1, S[2][v]);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        M0 = max(M0, S[1][v]);
+        M1 = max(M1, S[3][v]);
+    }
+    M0 = max_across_halves(M0);
+    M1 = max_across_halves(M1);
+    float m0 = __builtin_fmaf(__builtin_bit_cast(float, M0), c0, -u0);
+    float m1 = __builtin_fmaf(__builtin_bit_cast(float, M1), c1, -u1);
+    if (MASKED) {
+        if (M0 == INT32_MIN) m0 = -INFINITY;
+        if (M1 == INT32_MIN) m1 = -INFINITY;
+    }
+    const float mt = fmaxf(m0, m1);
 
     // ---- lazy update of the reference maximum
-    float w[2];
-#pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        const float mr = mref[qg];
-        const float nr = mt[qg] > mr + kLazyRescale ? mt[qg] : mr;
-        const bool up = nr > mr;
+    {
+        const float nr = mt > mref + kLazyRescale ? mt : mref;
+        const bool up = nr > mref;
         if (__any(up)) {
-            const float alpha = up ? __builtin_amdgcn_exp2f(mr - nr) : 1.0f;
-            lsum[qg] *= alpha;
+            const float alpha = up ? __builtin_amdgcn_exp2f(mref - nr) : 1.0f;
+            lsum *= alpha;
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) O[qg][ct][v] *= alpha;
+                for (int v = 0; v < 16; ++v) O[ct][v] *= alpha;
         }
-        mref[qg] = nr;
-        w[qg] = mt[qg] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mt[qg] - nr);
+        mref = nr;
     }
+    const float w = mt == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mt - mref);
 
-    // ---- P: E4M3 codes, as binary16 operands.  Piece p of a row group is
-    // the 8 values of tiles 2p and 2p+1, in the order of v_key_position.
-    v8h P[2][4];
-#pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        const float e = l448 - mt[qg];
-        const float bias0 = e - u0, bias1 = e - u1;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            v4i quad;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int tau = 2 * p + half;
-                const float c = tau < 4 ? c0 : c1;
-                const float bias = tau < 4 ? bias0 : bias1;
-                float y[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    // (bit_cast of the whole vector: this compiler mis-reads a
-                    // bit_cast of a single vector element as element 0)
-                    const float F = __builtin_bit_cast(v4f, S[qg][tau])[v];
-                    y[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(F, c, bias));
-                    if (MASKED && S[qg][tau][v] == INT32_MIN) y[v] = 0.0f;
-                }
-                // the first conversion writes the low half; the high half of
-                // its destination is then written by the second, so the
-                // register's old contents never matter (the builtin would zero
-                // it first)
-                int code;
-                asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(code) : "v"(y[0]), "v"(y[1]));
-                code = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], code, true);
-                quad[2 * half] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false));
-                quad[2 * half + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
-            }
-            P[qg][p] = __builtin_bit_cast(v8h, quad);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- level 1 on the matrix core, level 2 in FP32 registers
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        const int c = 16 * ct + r16;
-        const uint16_t* vr = lv + c * SAGE_BN;
-        v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const v8h vf = *reinterpret_cast<const v8h*>(vr + (((4 * g16 + p) ^ (c & 7)) << 3));
-#pragma unroll
-            for (int qg = 0; qg < 2; ++qg)
-                acc[qg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, P[qg][p], acc[qg], 0, 0, 0);
-        }
-#pragma unroll
-        for (int qg = 0; qg < 2; ++qg)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) O[qg][ct][v] = __builtin_fmaf(acc[qg][v], w[qg], O[qg][ct][v]);
-    }
+    // ---- P in pieces of 16 keys (8 per lane), each straight into level 1.
+    // At d = 128 the channel tiles go in two passes of two, so that one pass's
+    // accumulators, the P pieces and O fit in the architectural registers.
+    constexpr int CG = CT < 2 ? CT : 2;
+    const float e = l448 - mt;
+    const float bias0 = e - u0, bias1 = e - u1;
     const _Float16 one = (_Float16)1.0f;
     const v8h ones = {one, one, one, one, one, one, one, one};
+    v8h P[8];
+    v16f rs;
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        v4f rs = {0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < 16; ++v) rs[v] = 0.0f;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) rs = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[qg][p], rs, 0, 0, 0);
-        lsum[qg] = __builtin_fmaf(rs[0], w[qg], lsum[qg]);
+    for (int pass = 0; pass < CT / CG; ++pass) {
+        v16f acc[CG];
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (pass == 0) {
+                const int t = s >> 1, base = 8 * (s & 1);
+                const float c = t < 2 ? c0 : c1;
+                const float bias = t < 2 ? bias0 : bias1;
+                // (bit_cast of the whole vector: this compiler mis-reads a
+                // bit_cast of a single vector element as element 0)
+                const v16f F = __builtin_bit_cast(v16f, S[t]);
+                v4i quad;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    float y[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int v = base + 4 * g + i;
+                        y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[v], c, bias));
+                        if (MASKED && S[t][v] == INT32_MIN) y[i] = 0.0f;
+                    }
+                    // the first conversion writes the low half; the high half
+                    // of its destination is then written by the second, so the
+                    // register's old contents never matter (the builtin would
+                    // zero it first)
+                    int code;
+                    asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(code) : "v"(y[0]), "v"(y[1]));
+                    code = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], code, true);
+                    quad[2 * g] =
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false));
+                    quad[2 * g + 1] =
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
+                }
+                P[s] = __builtin_bit_cast(v8h, quad);
+                rs = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, P[s], rs, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < CG; ++j) {
+                const int ch = 32 * (pass * CG + j) + r32;
+                const v8h vf = *reinterpret_cast<const v8h*>(lv + ch * SAGE_BN + (((2 * s + h) ^ vswz(ch)) << 3));
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[s], acc[j], 0, 0, 0);
+            }
+        }
+        // ---- level 2 in FP32 registers
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                O[pass * CG + j][v] = __builtin_fmaf(acc[j][v], w, O[pass * CG + j][v]);
     }
+    lsum = __builtin_fmaf(rs[0], w, lsum);
 }
 
-template <int D, bool CAUSAL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void attn_fwd(AttnArgs a) {
-    constexpr int KK = D / 64;
-    constexpr int CT = D / 16;
+template <int D, bool CAUSAL, int WAVES, int WAVES_PER_SIMD>
+__global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs a) {
+    constexpr int KS = D / 32;
+    constexpr int CT = D / 32;
     constexpr int ROWS = 32 * WAVES;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* const lk0 = smem;
@@ -279,7 +278,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_fwd(AttnArgs a) {
     uint16_t* const lv1 = lv0 + D * SAGE_BN;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g16 = lane >> 4, r16 = lane & 15;
+    const int h = lane >> 5, r32 = lane & 31;
 
     // Work-group -> tile.  Work-groups are dispatched round-robin over the 8
     // XCDs; give each XCD a contiguous range of tiles (same heads, so K and V
@@ -297,6 +296,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_fwd(AttnArgs a) {
     const int bg = b * a.Hkv + hq / a.G;
     const int q0 = qt * ROWS;
     const int rbase = q0 + 32 * wave;  // this wave's first row
+    const int row = rbase + r32;       // this lane's row
 
     const int nkb = (a.N + SAGE_BN - 1) / SAGE_BN;  // key blocks holding real keys
     const int nblk = CAUSAL ? min(nkb, (q0 + ROWS - 1) / SAGE_BN + 1) : nkb;
@@ -309,28 +309,26 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_fwd(AttnArgs a) {
     const uint16_t* vbase = a.v_e4m3 + (long long)bg * a.Np * D;
     const float* ksc = a.k_scale + (long long)bg * (a.Np / SAGE_BK);
 
-    // Q fragments (B operand of Q.K^T): query row r16 of group qg, bytes
-    // [64*kk + 16*g16, +16).
-    v4i qf[2][KK];
+    // Q fragments (B operand of Q.K^T): query row r32, bytes [32*ks + 16*h, +16).
+    v4i qf[KS];
+    {
+        const int8_t* qp = a.q_i8 + ((long long)bh * a.Np + row) * D + 16 * h;
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        const int row = rbase + 16 * qg + r16;
-        const int8_t* qp = a.q_i8 + ((long long)bh * a.Np + row) * D + 16 * g16;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[qg][kk] = *reinterpret_cast<const v4i*>(qp + 64 * kk);
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const v4i*>(qp + 32 * ks);
     }
     const float sq = a.q_scale[(long long)bh * (a.Np / SAGE_BQ) + rbase / SAGE_BQ];
 
-    v4f O[2][CT];
-    float mref[2], lsum[2];
+    v16f O[CT];
+    float mref = -INFINITY, lsum = 0.0f;
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        mref[qg] = -INFINITY;
-        lsum[qg] = 0.0f;
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) O[qg][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
+        for (int v = 0; v < 16; ++v) O[ct][v] = 0.0f;
 
+    // The K scales of a block are loaded one block ahead, before that block's
+    // tile copy is issued: vector-memory waits count in issue order, so a
+    // scale load issued after the copy would make its wait cover the copy too.
+    float2 kscale = *reinterpret_cast<const float2*>(ksc);
     const TileLoader<D, WAVES> tiles(kbase, vbase, a.Np, wave, lane);
     tiles.load(0, lk0, lv0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -342,52 +340,57 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_fwd(AttnArgs a) {
     int T = 0;
     for (; T < nA; ++T) {
         const bool odd = T & 1;
-        if (T + 1 < nblk) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
-        const float c0 = (sq * ksc[2 * T]) * a.qk, c1 = (sq * ksc[2 * T + 1]) * a.qk;
-        attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, rbase + r16, a.N, c0,
-                                     c1, a.l448, g16, r16, mref, lsum, O);
+        const bool more = T + 1 < nblk;
+        const float2 knext = *reinterpret_cast<const float2*>(ksc + 2 * (more ? T + 1 : T));
+        if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
+        const float c0 = (sq * kscale.x) * a.qk, c1 = (sq * kscale.y) * a.qk;
+        attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
+                                     a.l448, h, r32, mref, lsum, O);
+        kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
     for (; T < nblk; ++T) {
         const bool odd = T & 1;
-        if (T + 1 < nblk) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
-        const float c0 = (sq * ksc[2 * T]) * a.qk, c1 = (sq * ksc[2 * T + 1]) * a.qk;
+        const bool more = T + 1 < nblk;
+        const float2 knext = *reinterpret_cast<const float2*>(ksc + 2 * (more ? T + 1 : T));
+        if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
+        const float c0 = (sq * kscale.x) * a.qk, c1 = (sq * kscale.y) * a.qk;
         if (T < n_full)
-            attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, rbase + r16, a.N,
-                                         c0, c1, a.l448, g16, r16, mref, lsum, O);
+            attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
+                                         a.l448, h, r32, mref, lsum, O);
         else if (T <= wave_last)
-            attn_block<D, CAUSAL, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, rbase + r16, a.N,
-                                        c0, c1, a.l448, g16, r16, mref, lsum, O);
+            attn_block<D, CAUSAL, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
+                                        a.l448, h, r32, mref, lsum, O);
+        kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
-    // ---- epilogue: out = O * s_V / l
+    // ---- epilogue: out = O * s_V / l.  O[ct][v] is channel 32ct + 8(v/4) + 4h + v%4.
+    if (row >= a.N) return;
     const float* sv = a.v_scale + (long long)bg * D;
+    const float inv_l = 1.0f / lsum;
+    float* op = a.out + ((long long)bh * a.N + row) * D;
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        const int row = rbase + 16 * qg + r16;
-        if (row >= a.N) continue;
-        const float inv_l = 1.0f / lsum[qg];
-        float* op = a.out + ((long long)bh * a.N + row) * D;
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const int ch = 16 * ct + 4 * g16;
+        for (int i = 0; i < 4; ++i) {
+            const int ch = 32 * ct + 8 * i + 4 * h;
             const float4 s4 = *reinterpret_cast<const float4*>(sv + ch);
             float4 o;
-            o.x = O[qg][ct][0] * s4.x * inv_l;
-            o.y = O[qg][ct][1] * s4.y * inv_l;
-            o.z = O[qg][ct][2] * s4.z * inv_l;
-            o.w = O[qg][ct][3] * s4.w * inv_l;
+            o.x = O[ct][4 * i + 0] * s4.x * inv_l;
+            o.y = O[ct][4 * i + 1] * s4.y * inv_l;
+            o.z = O[ct][4 * i + 2] * s4.z * inv_l;
+            o.w = O[ct][4 * i + 3] * s4.w * inv_l;
             *reinterpret_cast<float4*>(op + ch) = o;
         }
-    }
 }
 
 // d = 64: 4-wave work-groups, two per CU (48 KB of LDS each), whose waves
-// interleave on each SIMD.  d = 128: the 96 KB of LDS allow one work-group
-// per CU, so it runs 8 waves (2 per SIMD).
+// interleave on each SIMD.  d = 128: one 8-wave work-group per CU (96 KB of
+// LDS), two waves per SIMD.  Either way a wave has half the register file,
+// all of it architectural registers.
 template <int D>
 constexpr int attn_waves() {
 #ifdef SAGE_ATTN_WAVES
@@ -396,27 +399,36 @@ constexpr int attn_waves() {
     return D == 64 ? 4 : 8;
 #endif
 }
+template <int D>
+constexpr int attn_waves_per_simd() {
+#ifdef SAGE_ATTN_WPS
+    return SAGE_ATTN_WPS;
+#else
+    return 2;
+#endif
+}
 
 // Explicit instantiations: with the packed-FP32 feature switched off on the
 // command line, this compiler otherwise leaves the host stubs of some of these
 // kernels undefined.
-template __global__ void attn_fwd<64, false, attn_waves<64>()>(AttnArgs);
-template __global__ void attn_fwd<64, true, attn_waves<64>()>(AttnArgs);
-template __global__ void attn_fwd<128, false, attn_waves<128>()>(AttnArgs);
-template __global__ void attn_fwd<128, true, attn_waves<128>()>(AttnArgs);
+template __global__ void attn_fwd<64, false, attn_waves<64>(), attn_waves_per_simd<64>()>(AttnArgs);
+template __global__ void attn_fwd<64, true, attn_waves<64>(), attn_waves_per_simd<64>()>(AttnArgs);
+template __global__ void attn_fwd<128, false, attn_waves<128>(), attn_waves_per_simd<128>()>(AttnArgs);
+template __global__ void attn_fwd<128, true, attn_waves<128>(), attn_waves_per_simd<128>()>(AttnArgs);
 
 template <int D, bool CAUSAL>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WAVES = attn_waves<D>();
+    constexpr int WPS = attn_waves_per_simd<D>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, CAUSAL, WAVES>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, CAUSAL, WAVES, WPS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int total = a.B * a.Hq * a.nqt;
-    hipLaunchKernelGGL((attn_fwd<D, CAUSAL, WAVES>), dim3(total), dim3(64 * WAVES), lds, st, a);
+    hipLaunchKernelGGL((attn_fwd<D, CAUSAL, WAVES, WPS>), dim3(total), dim3(64 * WAVES), lds, st, a);
     return hipGetLastError();
 }
 

@@ -28,14 +28,17 @@ inline Shape make_shape(int B, int Hq, int Hkv, int N, int d) {
     return s;
 }
 
-// Position of key j inside a block's V row.  After the Q.K^T product, lane
-// group g (lanes 16g..16g+15) holds the scores of keys 16*tau + 4g + v
-// (tau = 0..7, v = 0..3); its P.V operand element e = 4*tau + v therefore
-// belongs to key 16*(e/4) + 4g + e%4, and V stores that key at position
-// 32g + e, so each lane reads its V operand contiguously.
+// Position of key j inside a block's V row.  The attention kernel's 32x32
+// Q.K^T tiles leave, in lane half h (lanes 32h..32h+31), the scores of keys
+// 8i + 4h + j (i, j = 0..3) of each 32-key tile.  Each 16-key step of P.V
+// takes 8 of them per lane as its operand elements e = 0..7, which the matrix
+// core reads as reduction index 8h + e; that index belongs to key
+// 8*(e/4) + 4h + e%4 of the step.  V stores each step's 16 keys in reduction
+// order, so a lane reads its V operand contiguously: within every group of 16
+// keys, keys 4..7 and 8..11 trade places (the map is its own inverse).
 __host__ __device__ inline int v_key_position(int j) {
-    int tau = j >> 4, g = (j >> 2) & 3, v = j & 3;
-    return 32 * g + 4 * tau + v;
+    const int a = (j >> 2) & 3;
+    return (j & ~15) | ((((a & 1) << 1) | (a >> 1)) << 2) | (j & 3);
 }
 
 // ---------------------------------------------------------------- device
