@@ -21,11 +21,12 @@
 //      products in FP32 (gfx950's FP8 matrix core truncates its internal sum to
 //      about 2^-11 of the largest product, too coarse for rows dominated by a
 //      single key); level 2: the FP32 register update O += w * acc with
-//      w = 2^(m - reference max).  The row sum of P comes out of the same
-//      matrix core (an all-ones operand), so the quantized weights are
-//      normalised exactly.  P is converted 16 keys at a time and each piece
-//      goes to the matrix core at once, so the conversions of one piece run
-//      while the products of the previous one are in flight.
+//      w = 2^(m - reference max).  The row sum of P comes out of the 16x16
+//      binary16 matrix core (a 0/1 operand, see row_sum_selector), so the
+//      quantized weights are normalised exactly.  P is converted 16 keys at a
+//      time and each piece goes to the matrix core at once, so the
+//      conversions of one piece run while the products of the previous one
+//      are in flight.
 // The reference max is raised lazily, only when a block's maximum exceeds it
 // by more than 8 (log2 units), so O is rescaled rarely.
 // The P operand a lane feeds to P.V is exactly the scores it computed, so
@@ -36,6 +37,7 @@ namespace sage {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
@@ -112,6 +114,21 @@ struct TileLoader {
     }
 };
 
+// A operand of v_mfma_f32_16x16x32_f16 that turns a P piece into row sums.
+// Read as that shape's B operand, a P piece puts lane l's 8 values in column
+// l%16, reduction rows 8(l/16)..8(l/16)+7.  Lane l holds keys of query l%32,
+// so column n mixes query n (lane quarters 0 and 2) with query n+16 (quarters
+// 1 and 3).  Output rows 4G..4G+3 land in lane quarter G, whose own query is
+// n + 16(G%2); A[m][k] = 1 exactly when (k/8)%2 == (m/4)%2 sums the two
+// quarters of that query, so each lane receives its own row's sum over the
+// piece's 16 keys (in all four output registers).  Lane l supplies
+// A[l%16][8(l/16)..+8]: ones when (l/16)%2 == (l%16/4)%2, else zeros.
+__device__ inline v8h row_sum_selector(int lane) {
+    const _Float16 x = (((lane >> 4) ^ (lane >> 2)) & 1) ? (_Float16)0.0f : (_Float16)1.0f;
+    const v8h r = {x, x, x, x, x, x, x, x};
+    return r;
+}
+
 // Maximum over the two lanes (l, l^32) that hold one query row.
 __device__ inline int max_across_halves(int x) {
     auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
@@ -125,7 +142,8 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const uint16_t* __restrict__ lv,
                                            const v4i (&qf)[D / 32], int T, int row, int N,
                                            float c0, float c1, float l448, int h, int r32,
-                                           float& mref, float& lsum, v16f (&O)[D / 32]) {
+                                           const v8h& rsel, float& mref, float& lsum,
+                                           v16f (&O)[D / 32]) {
     constexpr int KS = D / 32, CT = D / 32;
     const float u0 = kSeed * c0, u1 = kSeed * c1;
 
@@ -202,12 +220,8 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
     constexpr int CG = CT < 2 ? CT : 2;
     const float e = l448 - mt;
     const float bias0 = e - u0, bias1 = e - u1;
-    const _Float16 one = (_Float16)1.0f;
-    const v8h ones = {one, one, one, one, one, one, one, one};
     v8h P[8];
-    v16f rs;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) rs[v] = 0.0f;
+    v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int pass = 0; pass < CT / CG; ++pass) {
         v16f acc[CG];
@@ -247,7 +261,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                         __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
                 }
                 P[s] = __builtin_bit_cast(v8h, quad);
-                rs = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, P[s], rs, 0, 0, 0);
+                rs = __builtin_amdgcn_mfma_f32_16x16x32_f16(rsel, P[s], rs, 0, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < CG; ++j) {
@@ -279,6 +293,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = lane >> 5, r32 = lane & 31;
+    const v8h rsel = row_sum_selector(lane);
 
     // Work-group -> tile.  Work-groups are dispatched round-robin over the 8
     // XCDs; give each XCD a contiguous range of tiles (same heads, so K and V
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
         const float c0 = (sq * kscale.x) * a.qk, c1 = (sq * kscale.y) * a.qk;
         attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
-                                     a.l448, h, r32, mref, lsum, O);
+                                     a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -358,10 +373,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         const float c0 = (sq * kscale.x) * a.qk, c1 = (sq * kscale.y) * a.qk;
         if (T < n_full)
             attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
-                                         a.l448, h, r32, mref, lsum, O);
+                                         a.l448, h, r32, rsel, mref, lsum, O);
         else if (T <= wave_last)
             attn_block<D, CAUSAL, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
-                                        a.l448, h, r32, mref, lsum, O);
+                                        a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
