@@ -35,7 +35,7 @@ class sage_config(ctypes.Structure):
 class sage_qkv_quant(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_e4m3", "v_scale", "v_inv",
-                 "k_part", "v_part")]
+                 "k_part", "v_part", "sync")]
 
 
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t

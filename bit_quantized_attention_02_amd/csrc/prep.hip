@@ -4,86 +4,94 @@
 // for V).  Memory-bound: every kernel streams 16-byte loads and does its
 // reductions in registers, wavefront shuffles and LDS.
 //
-//   prep_stats_q  per (kv head, 512-row chunk): partial K channel sums
-//                 (float64) and V channel absmax; per (q head, 128-row block):
-//                 Q absmax, scale and INT8 codes.
-//   prep_finalize per kv head: K mean and V scales from the partials, summed
-//                 in a fixed order (deterministic).
-//   prep_pack     per (kv head, 64-row block) K - mean, absmax, scale, codes;
-//                 per (kv head, 128-key block) V E4M3 codes, stored as the
-//                 binary16 values they denote and transposed to the attention
-//                 kernel's channel-major, permuted-key layout.
-//                 Heads are visited in the reverse order of prep_stats_q so
-//                 the second read of K and V finds the most recent heads
-//                 still in the last-level cache.
+//   prep_q      per (q head, 128-row block): Q absmax, scale and INT8 codes;
+//               one extra work-group clears the per-head arrival counters.
+//   prep_stats  per (kv head, 512-row chunk): partial statistics (float64 K
+//               channel sums, V channel absmax).  The head's last work-group
+//               to arrive (an atomic counter; nobody waits) reduces the
+//               partials in a fixed chunk order (deterministic) into the K
+//               mean and the V scales.
+//   prep_pack   per (kv head, 64-row block) K - mean, absmax, scale, codes;
+//               per (kv head, 128-key block) V E4M3 codes, stored as the
+//               binary16 values they denote and transposed to the attention
+//               kernel's channel-major, permuted-key layout.  Heads are
+//               visited in the reverse order of prep_stats so the second read
+//               of K and V finds the most recent heads still in the
+//               last-level cache.
 #include "sage_internal.h"
 
 namespace sage {
 
-// ------------------------------------------------------------ statistics + Q
+// The arrival counters of prep_stats, one per kv head.
+__host__ __device__ inline int sync_words(const Shape& s) { return s.B * s.Hkv; }
+
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ shared pieces
+// INT8 codes of 8 values with multiplier inv (RNE, clamped to +-127).
+__device__ inline uint2 int8_codes(const float (&x)[8], float inv) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float r = __builtin_rintf(x[i] * inv);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (i & 3));
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+// The binary16 values of the E4M3 codes of x[i] * inv[i], i = 0..7, into the
+// transposed V tile vt[D][SAGE_BN] at key position pos.
+template <int D>
+__device__ inline void v_codes_to_tile(const float (&x)[8], const float* inv, int col, int pos,
+                                       uint16_t* vt) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        // |v * inv| <= 448 (1 + 2^-23); the clamp keeps the hardware
+        // conversion (which gives NaN above 464) in range regardless.
+        const float y0 = fminf(fmaxf(x[i] * inv[i], -448.0f), 448.0f);
+        const float y1 = fminf(fmaxf(x[i + 1] * inv[i + 1], -448.0f), 448.0f);
+        const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        // the binary16 value of each E4M3 code (exact).  The pair is read as
+        // one 32-bit word: this compiler stores element [1] of the builtin's
+        // vector result from the wrong half.
+        const uint32_t h =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false));
+        vt[(col + i) * SAGE_BN + pos] = (uint16_t)(h & 0xFFFFu);
+        vt[(col + i + 1) * SAGE_BN + pos] = (uint16_t)(h >> 16);
+    }
+}
+
+// Copies a transposed V tile from LDS to its place in v_e4m3 (streaming
+// stores: the tile is not read again by this step).
+template <int D>
+__device__ inline void store_v_tile(const uint16_t* vt, uint16_t* dst, int tid) {
+    constexpr int OUT_CH = D * SAGE_BN * 2 / 16 / kThreads;
+#pragma unroll
+    for (int c = 0; c < OUT_CH; ++c) {
+        const int e = tid + c * kThreads;
+        __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(vt + e * 8),
+                                    reinterpret_cast<v4u*>(dst + e * 8));
+    }
+}
+
+// ------------------------------------------------------------ Q
 template <typename In, int D>
-__global__ __launch_bounds__(kThreads) void prep_stats_q(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, Shape s, int8_t* __restrict__ q_i8,
-    float* __restrict__ q_scale, double* __restrict__ k_part, float* __restrict__ v_part) {
-    constexpr int CPR = D / 8;            // 16-byte chunks per row
-    constexpr int RPI = kThreads / CPR;   // rows per iteration
-    __shared__ double ssum[RPI][D];
-    __shared__ float smax[RPI][D];
+__global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ q, Shape s,
+                                                   int8_t* __restrict__ q_i8,
+                                                   float* __restrict__ q_scale,
+                                                   int* __restrict__ sync) {
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
     __shared__ float red[4];
     const int tid = threadIdx.x;
-    const int nstat = s.B * s.Hkv * s.nchunk;
-    const int bid = blockIdx.x;
-
-    if (bid < nstat) {
-        const int bg = bid / s.nchunk, chunk = bid % s.nchunk;
-        const int cg = tid % CPR, rr = tid / CPR;
-        const long long head = (long long)bg * s.N * D;
-        const int r0 = chunk * kStatRows;
-        const int r1 = min(s.N, r0 + kStatRows);
-        double sum[8];
-        float mx[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            sum[i] = 0.0;
-            mx[i] = 0.0f;
-        }
-        for (int r = r0 + rr; r < r1; r += RPI) {
-            const long long off = head + (long long)r * D + cg * 8;
-            const uint4 uk = *reinterpret_cast<const uint4*>(k + off);
-            const uint4 uv = *reinterpret_cast<const uint4*>(v + off);
-            float fk[8], fv[8];
-            unpack8<In>(uk, fk);
-            unpack8<In>(uv, fv);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sum[i] += (double)fk[i];
-                mx[i] = fmaxf(mx[i], fabsf(fv[i]));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            ssum[rr][cg * 8 + i] = sum[i];
-            smax[rr][cg * 8 + i] = mx[i];
-        }
-        __syncthreads();
-        if (tid < D) {
-            double t = 0.0;
-            float m = 0.0f;
-            for (int r = 0; r < RPI; ++r) {
-                t += ssum[r][tid];
-                m = fmaxf(m, smax[r][tid]);
-            }
-            const long long o = ((long long)bg * s.nchunk + chunk) * D + tid;
-            k_part[o] = t;
-            v_part[o] = m;
-        }
+    const int nqt = s.Np / SAGE_BQ;
+    const int qb = blockIdx.x;
+    if (qb == s.B * s.Hq * nqt) {
+        for (int i = tid; i < sync_words(s); i += kThreads) sync[i] = 0;
         return;
     }
-
-    // Q block: rows [t*BQ, t*BQ+BQ) of head bh; rows >= N are zero padding.
-    const int qb = bid - nstat;
-    const int nqt = s.Np / SAGE_BQ;
+    // rows [t*BQ, t*BQ+BQ) of head bh; rows >= N are zero padding
     const int bh = qb / nqt, t = qb % nqt;
     constexpr int NCH = SAGE_BQ * CPR / kThreads;  // chunks per thread
     const long long src_head = (long long)bh * s.N * D;
@@ -111,39 +119,88 @@ __global__ __launch_bounds__(kThreads) void prep_stats_q(
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
         const int row = t * SAGE_BQ + e / CPR, col = (e % CPR) * 8;
-        uint32_t w[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float r = __builtin_rintf(x[c][i] * inv);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (i & 3));
-        }
-        *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = make_uint2(w[0], w[1]);
+        *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv);
     }
 }
 
-// ------------------------------------------------------------ finalisation
-template <int D>
-__global__ __launch_bounds__(D) void prep_finalize(Shape s, const double* __restrict__ k_part,
-                                                   const float* __restrict__ v_part,
-                                                   float* __restrict__ k_mean,
-                                                   float* __restrict__ v_scale,
-                                                   float* __restrict__ v_inv) {
-    const int bg = blockIdx.x, c = threadIdx.x;
-    double sum = 0.0;
-    float m = 0.0f;
-    for (int ch = 0; ch < s.nchunk; ++ch) {
-        const long long o = ((long long)bg * s.nchunk + ch) * D + c;
-        sum += k_part[o];
-        m = fmaxf(m, v_part[o]);
+// ------------------------------------------------------------ K and V
+template <typename In, int D>
+__global__ __launch_bounds__(kThreads) void prep_stats(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s,
+    double* __restrict__ k_part, float* __restrict__ v_part, int* __restrict__ cnt,
+    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = kThreads / CPR;
+    __shared__ double ssum[RPI][D];
+    __shared__ float smax[RPI][D];
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    const int nchunk = s.part_chunks();
+    const int bg = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    const int cg = tid % CPR, rr = tid / CPR;
+    const long long head = (long long)bg * s.N * D;
+    const int r0 = chunk * kStatRows;
+    const int r1 = min(s.N, r0 + kStatRows);
+    double sum[8];
+    float mx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        sum[i] = 0.0;
+        mx[i] = 0.0f;
     }
-    const long long o = (long long)bg * D + c;
-    k_mean[o] = (float)(sum / (double)s.N);
+    for (int r = r0 + rr; r < r1; r += RPI) {
+        const long long off = head + (long long)r * D + cg * 8;
+        float fk[8], fv[8];
+        unpack8<In>(*reinterpret_cast<const uint4*>(k + off), fk);
+        unpack8<In>(*reinterpret_cast<const uint4*>(v + off), fv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sum[i] += (double)fk[i];
+            mx[i] = fmaxf(mx[i], fabsf(fv[i]));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ssum[rr][cg * 8 + i] = sum[i];
+        smax[rr][cg * 8 + i] = mx[i];
+    }
+    __syncthreads();
+    if (tid < D) {
+        double t = 0.0;
+        float m = 0.0f;
+        for (int r = 0; r < RPI; ++r) {
+            t += ssum[r][tid];
+            m = fmaxf(m, smax[r][tid]);
+        }
+        const long long o = ((long long)bg * nchunk + chunk) * D + tid;
+        __hip_atomic_store(k_part + o, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(v_part + o, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Arrival.  The partials are written and read by device-scope atomic
+    // accesses (coherent across the chip's L2 caches); waiting for the stores
+    // to complete before the barrier and the arrival orders them, with no
+    // cache writeback or invalidation.  Only the last work-group of the head
+    // goes on; nobody waits.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(cnt + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 nchunk - 1;
+    __syncthreads();
+    if (!s_last || tid >= D) return;
+    double t = 0.0;
+    float m = 0.0f;
+    for (int c = 0; c < nchunk; ++c) {
+        const long long o = ((long long)bg * nchunk + c) * D + tid;
+        t += __hip_atomic_load(k_part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        m = fmaxf(m, __hip_atomic_load(v_part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+    const long long o = (long long)bg * D + tid;
+    k_mean[o] = (float)(t / (double)s.N);
     v_scale[o] = m / 448.0f;
     v_inv[o] = m > 0.0f ? 448.0f / m : 0.0f;
 }
 
-// ------------------------------------------------------------ K and V packing
 template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_pack(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s,
@@ -155,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     const int tid = threadIdx.x;
     const int nkb = s.Np / SAGE_BK, nvb = s.Np / SAGE_BN;
     const int per_head = nkb + nvb;
-    // reverse head order relative to prep_stats_q
+    // reverse head order relative to prep_stats
     const int bg = s.B * s.Hkv - 1 - (int)(blockIdx.x / per_head);
     const int j = blockIdx.x % per_head;
     const long long src_head = (long long)bg * s.N * D;
@@ -190,14 +247,7 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
         for (int c = 0; c < NCH; ++c) {
             const int e = tid + c * kThreads;
             const int row = t * SAGE_BK + e / CPR, col = (e % CPR) * 8;
-            uint32_t w[2] = {0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float r = __builtin_rintf(x[c][i] * inv);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (i & 3));
-            }
-            *reinterpret_cast<uint2*>(k_i8 + dst_head + (long long)row * D + col) = make_uint2(w[0], w[1]);
+            *reinterpret_cast<uint2*>(k_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv);
         }
         return;
     }
@@ -205,7 +255,6 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     // V block T: codes of 128 keys x D channels, transposed through LDS.
     const int T = j - nkb;
     constexpr int NCH = SAGE_BN * CPR / kThreads;
-    const float* inv = v_inv + (long long)bg * D;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
@@ -219,46 +268,25 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = 0.0f;
         }
-        const int pos = v_key_position(key);
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            // |v * inv| <= 448 (1 + 2^-23); the clamp keeps the hardware
-            // conversion (which gives NaN above 464) in range regardless.
-            const float y0 = fminf(fmaxf(x[i] * inv[col + i], -448.0f), 448.0f);
-            const float y1 = fminf(fmaxf(x[i + 1] * inv[col + i + 1], -448.0f), 448.0f);
-            const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-            // the binary16 value of each E4M3 code (exact).  The pair is read
-            // as one 32-bit word: this compiler stores element [1] of the
-            // builtin's vector result from the wrong half.
-            const uint32_t h = __builtin_bit_cast(
-                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false));
-            vt[(col + i) * SAGE_BN + pos] = (uint16_t)(h & 0xFFFFu);
-            vt[(col + i + 1) * SAGE_BN + pos] = (uint16_t)(h >> 16);
-        }
+        v_codes_to_tile<D>(x, v_inv + (long long)bg * D + col, col, v_key_position(key), vt);
     }
     __syncthreads();
-    uint16_t* dst = v_e4m3 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN);
-    constexpr int OUT_CH = D * SAGE_BN * 2 / 16 / kThreads;
-#pragma unroll
-    for (int c = 0; c < OUT_CH; ++c) {
-        const int e = tid + c * kThreads;
-        *reinterpret_cast<uint4*>(dst + e * 8) = *reinterpret_cast<const uint4*>(vt + e * 8);
-    }
+    store_v_tile<D>(vt, v_e4m3 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN), tid);
 }
 
 // ------------------------------------------------------------ launchers
 template <typename In, int D>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const Shape& s,
                                 const sage_qkv_quant* z, hipStream_t st) {
-    const int nstat = s.B * s.Hkv * s.nchunk;
     const int nq = s.B * s.Hq * (s.Np / SAGE_BQ);
-    hipLaunchKernelGGL((prep_stats_q<In, D>), dim3(nstat + nq), dim3(kThreads), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, z->q_i8,
-                       z->q_scale, z->k_part, z->v_part);
+    hipLaunchKernelGGL((prep_q<In, D>), dim3(nq + 1), dim3(kThreads), 0, st, (const uint16_t*)q, s,
+                       z->q_i8, z->q_scale, z->sync);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_finalize<D>), dim3(s.B * s.Hkv), dim3(D), 0, st, s, z->k_part,
-                       z->v_part, z->k_mean, z->v_scale, z->v_inv);
+    const int nchunk = s.part_chunks();
+    hipLaunchKernelGGL((prep_stats<In, D>), dim3(s.B * s.Hkv * nchunk), dim3(kThreads), 0, st,
+                       (const uint16_t*)k, (const uint16_t*)v, s, z->k_part, z->v_part, z->sync,
+                       z->k_mean, z->v_scale, z->v_inv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int per_head = s.Np / SAGE_BK + s.Np / SAGE_BN;
@@ -276,5 +304,7 @@ hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, c
     return s.d == 64 ? launch_prep_t<Bf16Tag, 64>(q, k, v, s, z, st)
                      : launch_prep_t<Bf16Tag, 128>(q, k, v, s, z, st);
 }
+
+int prep_sync_words(const Shape& s) { return sync_words(s); }
 
 }  // namespace sage

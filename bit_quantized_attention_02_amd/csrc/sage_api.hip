@@ -10,6 +10,7 @@ hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, c
                        const sage_qkv_quant* z, hipStream_t st);
 hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal, float qk,
                        float l448, hipStream_t st);
+int prep_sync_words(const Shape& s);
 }  // namespace sage
 
 using sage::Shape;
@@ -32,7 +33,7 @@ static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout: each region starts on a 256-byte boundary.
 struct Layout {
-    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v_e4m3, v_scale, v_inv, k_part, v_part, total;
+    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v_e4m3, v_scale, v_inv, k_part, v_part, sync, total;
 };
 
 static Layout layout(const Shape& s) {
@@ -52,8 +53,9 @@ static Layout layout(const Shape& s) {
     L.k_mean = take(Bkv * s.d * sizeof(float));
     L.v_scale = take(Bkv * s.d * sizeof(float));
     L.v_inv = take(Bkv * s.d * sizeof(float));
-    L.k_part = take(Bkv * s.nchunk * s.d * sizeof(double));
-    L.v_part = take(Bkv * s.nchunk * s.d * sizeof(float));
+    L.k_part = take(Bkv * s.part_chunks() * s.d * sizeof(double));
+    L.v_part = take(Bkv * s.part_chunks() * s.d * sizeof(float));
+    L.sync = take((size_t)sage::prep_sync_words(s) * sizeof(int32_t));
     L.total = off;
     return L;
 }
@@ -61,7 +63,7 @@ static Layout layout(const Shape& s) {
 static int check_quant(const sage_qkv_quant* z) {
     if (!z) return SAGE_ERR_INVALID_ARG;
     if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v_e4m3 ||
-        !z->v_scale || !z->v_inv || !z->k_part || !z->v_part)
+        !z->v_scale || !z->v_inv || !z->k_part || !z->v_part || !z->sync)
         return SAGE_ERR_INVALID_ARG;
     if (!aligned(z->q_i8, 16) || !aligned(z->k_i8, 16) || !aligned(z->v_e4m3, 16) ||
         !aligned(z->v_scale, 16) || !aligned(z->k_part, 8))
@@ -95,6 +97,7 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->v_inv = (float*)(base + L.v_inv);
     out->k_part = (double*)(base + L.k_part);
     out->v_part = (float*)(base + L.v_part);
+    out->sync = (int32_t*)(base + L.sync);
     return SAGE_OK;
 }
 

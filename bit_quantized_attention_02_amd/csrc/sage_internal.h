@@ -10,21 +10,20 @@
 namespace sage {
 
 constexpr int kThreads = 256;      // prep kernels run 4 waves of 64
-constexpr int kStatRows = 512;     // rows per partial-statistics chunk
-constexpr int kVersion = 100;
+constexpr int kStatRows = 512;     // rows per partial-statistics chunk of the prep step
+constexpr int kVersion = 101;
 
 struct Shape {
     int B, Hq, Hkv, N, d;
     int Np;       // N rounded up to SAGE_NPAD
-    int nchunk;   // statistics chunks per kv head
     long long q_elems() const { return (long long)B * Hq * Np * d; }
     long long kv_elems() const { return (long long)B * Hkv * Np * d; }
+    __host__ __device__ int part_chunks() const { return (N + kStatRows - 1) / kStatRows; }
 };
 
 inline Shape make_shape(int B, int Hq, int Hkv, int N, int d) {
-    Shape s{B, Hq, Hkv, N, d, 0, 0};
+    Shape s{B, Hq, Hkv, N, d, 0};
     s.Np = (N + SAGE_NPAD - 1) / SAGE_NPAD * SAGE_NPAD;
-    s.nchunk = (N + kStatRows - 1) / kStatRows;
     return s;
 }
 

@@ -99,6 +99,8 @@ typedef struct {
  *   v_scale f32  [B, Hkv, d]                absmax / 448 per channel
  *   v_inv   f32  [B, Hkv, d]                448 / absmax (0 for a zero channel)
  *   k_part, v_part: per-chunk partial statistics used by sage_quantize.
+ *   sync    int32 [B * Hkv]: per-kv-head arrival counters of the statistics
+ *           kernel of sage_quantize, which clears them itself on every call.
  */
 typedef struct {
     int8_t* q_i8;
@@ -111,6 +113,7 @@ typedef struct {
     float* v_inv;
     double* k_part;
     float* v_part;
+    int32_t* sync;
 } sage_qkv_quant;
 
 /* Bytes of workspace sage_quantize/sage_attn_fwd need for this shape (0 when
@@ -125,8 +128,8 @@ int sage_workspace_carve(void* workspace, size_t ws_bytes, int B, int Hq, int Hk
 /*
  * The prep step (K mean, smoothing, per-block INT8 of Q and K, per-channel
  * FP8 of V) from fp16/bf16 Q, K, V into the views of `dst`.  Memory-bound; runs
- * as three kernels on `stream` (statistics + Q, per-head finalisation, K/V
- * packing).
+ * as three kernels on `stream`: Q codes; K/V statistics, whose last
+ * work-group per kv head forms the K mean and V scales; K/V codes.
  */
 int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
                   int N, int d, const sage_qkv_quant* dst, void* stream);

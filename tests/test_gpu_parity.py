@@ -124,6 +124,35 @@ def test_degenerate_inputs(sage, orc):
         check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 0.125, None)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prep_on_a_used_workspace(sage, orc, d):
+    """The prep step clears its own arrival counters: a workspace filled with
+    0xFF bytes, and one already used by a call on other inputs, give the same
+    bytes as a fresh one."""
+    N = 1100
+    B, Hq, Hkv = 2, 4, 2
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, "bf16" if d == 64 else "f16",
+                                      seed=77 + d, scale=2.0)
+    q2, k2, v2 = workloads.random_inputs(B, Hq, Hkv, N, d, "bf16" if d == 64 else "f16",
+                                         seed=78 + d, scale=3.0)
+    _say(f"case prep on a used workspace d={d} N={N}")
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    ws = sage.workspace_for(qd, kd)
+    z = sage.sage_workspace_carve(ws, ws.numel(), B, Hq, Hkv, N, d)
+    results = []
+    for fill in ("ones", "used"):
+        if fill == "ones":
+            ws.fill_(0xFF)
+        else:
+            sage.sage_quantize(q2.cuda(), k2.cuda(), v2.cuda(), z)
+        sage.sage_quantize(qd, kd, vd, z)
+        torch.cuda.synchronize()
+        results.append(sage.read_quantized(z, ws, B, Hq, Hkv, N, d))
+    for key in ("q_i8", "k_i8", "v_half", "k_mean", "v_scale", "q_scale", "k_scale"):
+        assert torch.equal(results[0][key], results[1][key]), key
+    check_prep(orc, results[1], orc.quantize(q, k, v))
+
+
 def test_sage_attn_fwd_matches_two_step_path(sage):
     w = workloads.WORKLOADS[2].resized(B=1, Hq=4, Hkv=4, N=515)
     q, k, v = (t.cuda() for t in workloads.generate(w, seed=3))
