@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=3,
                    help="1..5; 3 is the non-causal N=17550 video-diffusion shape")
+    p.add_argument("--granularity", choices=("block", "thread"), default="block",
+                   help="Q/K scale granularity: block (128 rows / 64 keys) or thread (per row / 32 keys)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -72,7 +74,7 @@ def timed(fn, iters, torch):
     return start.elapsed_time(end) / iters
 
 
-def cpu_baseline(w, q, k, v, rows_wanted):
+def cpu_baseline(w, q, k, v, rows_wanted, bq, bk):
     """The oracle as it stands: its prep over the whole input, pro-rated to the
     sampled rows, plus its attention over the sampled rows."""
     import numpy as np
@@ -82,7 +84,7 @@ def cpu_baseline(w, q, k, v, rows_wanted):
 
     oracle.build()
     t0 = time.perf_counter()
-    oz = oracle.quantize(q, k, v)
+    oz = oracle.quantize(q, k, v, bq=bq, bk=bk)
     t_prep = time.perf_counter() - t0
     total_rows = w.B * w.Hq * w.N
     if rows_wanted <= 0:
@@ -130,10 +132,12 @@ def main():
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
     ws = sage.workspace_for(qd, kd)
-    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d)
+    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d,
+                                  granularity=args.granularity)
+    qb, kb = sage.GRANULARITY[args.granularity]
 
     def step():
-        sage.sage_attn_fwd(qd, kd, vd, out, w.causal, w.sm_scale, ws)
+        sage.sage_attn_fwd_granular(qd, kd, vd, out, w.causal, w.sm_scale, qb, kb, ws)
 
     for _ in range(args.warmup):
         step()
@@ -162,7 +166,7 @@ def main():
         "dtype": "i8 (QK^T, i32 acc) + e4m3 values (P.V, f32 acc)", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "input_dtype": w.dtype, "sm_scale": w.sm_scale,
-                   "parallelism": "single GPU"},
+                   "q_block": qb, "k_block": kb, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd", "ms_per_launch": round(ms_attn, 4)},
@@ -171,7 +175,7 @@ def main():
         "timed_wall_s": round(wall, 3),
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, qb, kb)
     print(json.dumps(line), flush=True)
 
 

@@ -25,6 +25,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_HIP = 0, -1, -2, -3, -4
 SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_BQ, SAGE_BK, SAGE_BN, SAGE_NPAD = 128, 64, 128, 256
+SAGE_BQ_THREAD, SAGE_BK_THREAD = 1, 32
+# (q_block, k_block) of the two quantization granularities
+GRANULARITY = {"block": (SAGE_BQ, SAGE_BK), "thread": (SAGE_BQ_THREAD, SAGE_BK_THREAD)}
 
 
 class sage_config(ctypes.Structure):
@@ -35,7 +38,7 @@ class sage_config(ctypes.Structure):
 class sage_qkv_quant(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_e4m3", "v_scale", "v_inv",
-                 "k_part", "v_part", "sync")]
+                 "k_part", "v_part", "sync")] + [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32)]
 
 
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -46,13 +49,15 @@ _lib.sage_quantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTE
 _lib.sage_attn_fwd_quantized.argtypes = [ctypes.POINTER(sage_qkv_quant), _P, _I, _I, _I, _I, _I, _I,
                                          _F, _P]
 _lib.sage_attn_fwd.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]
+_lib.sage_attn_fwd_granular.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P,
+                                        _S, _P]
 _lib.sage_get_config.argtypes = [ctypes.POINTER(sage_config)]
 _lib.sage_v_key_position.argtypes = [_I]
 _lib.sage_status_string.restype = ctypes.c_char_p
 _lib.sage_status_string.argtypes = [_I]
 
 EXPORTED = ["sage_workspace_bytes", "sage_workspace_carve", "sage_quantize",
-            "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_get_config",
+            "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_attn_fwd_granular", "sage_get_config",
             "sage_v_key_position", "sage_status_string"]
 
 
@@ -111,10 +116,12 @@ def sage_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
 
 
 def sage_workspace_carve(workspace: torch.Tensor | int | None, ws_bytes: int, B: int, Hq: int,
-                         Hkv: int, N: int, d: int) -> sage_qkv_quant:
+                         Hkv: int, N: int, d: int, granularity: str = "block") -> sage_qkv_quant:
+    """The C call, then (q_block, k_block) set to the chosen granularity."""
     z = sage_qkv_quant()
     ptr = workspace.data_ptr() if isinstance(workspace, torch.Tensor) else workspace
     _check(_lib.sage_workspace_carve(ptr, ws_bytes, B, Hq, Hkv, N, d, ctypes.byref(z)))
+    z.q_block, z.k_block = GRANULARITY[granularity]
     return z
 
 
@@ -139,6 +146,16 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def sage_attn_fwd_granular(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                           causal: bool, sm_scale: float, q_block: int, k_block: int,
+                           workspace: torch.Tensor, stream=None) -> None:
+    B, Hq, Hkv, N, d = _shape(q, k)
+    _check(_lib.sage_attn_fwd_granular(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d,
+                                       int(causal), float(sm_scale), _dtype_code(q), int(q_block),
+                                       int(k_block), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 # ------------------------------------------------------------------ helpers
 
 def workspace_for(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
@@ -151,9 +168,12 @@ def workspace_for(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
 
 
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-         sm_scale: float | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+         sm_scale: float | None = None, workspace: torch.Tensor | None = None,
+         granularity: str = "block") -> torch.Tensor:
     """Drop-in attention: [B,Hq,N,d] fp16/bf16 Q and [B,Hkv,N,d] K,V on the GPU
-    -> FP32 [B,Hq,N,d], on the current stream."""
+    -> FP32 [B,Hq,N,d], on the current stream.  granularity: "block" (one Q
+    scale per 128 rows, one K scale per 64 keys) or "thread" (per row, per 32
+    keys)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     for t in (q, k, v):
@@ -162,7 +182,8 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = workspace_for(q, k)
-    sage_attn_fwd(q, k, v, out, causal, sm_scale, workspace)
+    qb, kb = GRANULARITY[granularity]
+    sage_attn_fwd_granular(q, k, v, out, causal, sm_scale, qb, kb, workspace)
     return out
 
 
@@ -195,7 +216,7 @@ def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, 
         v_fp8=v_full[:, :, :N].contiguous(), v_half=v_half[:, :, :N].contiguous(),
         q_pad=q_full[:, :, N:].contiguous(), k_pad=k_full[:, :, N:].contiguous(),
         v_pad=v_half[:, :, N:].contiguous(),
-        q_scale=host(z.q_scale, (B, Hq, Np // SAGE_BQ), torch.float32),
-        k_scale=host(z.k_scale, (B, Hkv, Np // SAGE_BK), torch.float32),
+        q_scale=host(z.q_scale, (B, Hq, Np // z.q_block), torch.float32),
+        k_scale=host(z.k_scale, (B, Hkv, Np // z.k_block), torch.float32),
         k_mean=host(z.k_mean, (B, Hkv, d), torch.float32),
         v_scale=host(z.v_scale, (B, Hkv, d), torch.float32))

@@ -41,6 +41,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
+static_assert(SAGE_BQ == 128 && SAGE_BQ_THREAD == 1 && SAGE_BK == 64 && SAGE_BK_THREAD == 32,
+              "the launch maps the two granularities to q_shift 7/0 and 2/4 K scales per block");
+
 constexpr float kLazyRescale = 8.0f;
 constexpr float kSeed = 12582912.0f;   // 1.5 * 2^23
 constexpr int kSeedBits = 0x4B400000;  // its float32 bit pattern
@@ -54,6 +57,7 @@ struct AttnArgs {
     const float* v_scale;
     float* out;
     int B, Hq, Hkv, N, Np, G, nqt;
+    int q_shift;  // log2 of the query rows per Q scale (7 or 0)
     float qk;    // f32(sm_scale * log2 e)
     float l448;  // f32(log2 448)
 };
@@ -137,15 +141,21 @@ __device__ inline int max_across_halves(int x) {
 
 // One key block for one wave (32 query rows).  MASKED: some keys of the
 // block are excluded (causal diagonal, or keys >= N).
-template <int D, bool CAUSAL, bool MASKED>
+// KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
+// 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
+// log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
+template <int D, int KSPLIT, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const uint16_t* __restrict__ lv,
                                            const v4i (&qf)[D / 32], int T, int row, int N,
-                                           float c0, float c1, float l448, int h, int r32,
+                                           const float (&c)[KSPLIT], float l448, int h, int r32,
                                            const v8h& rsel, float& mref, float& lsum,
                                            v16f (&O)[D / 32]) {
     constexpr int KS = D / 32, CT = D / 32;
-    const float u0 = kSeed * c0, u1 = kSeed * c1;
+    constexpr int TPG = 4 / KSPLIT;  // tiles per scale group
+    float u[KSPLIT];
+#pragma unroll
+    for (int g = 0; g < KSPLIT; ++g) u[g] = kSeed * c[g];
 
     // ---- S^T = K Q^T (INT32).  Tile t, element v: key 32t + 8(v/4) + 4h + v%4.
     v16i S[4];
@@ -165,7 +175,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
         S[t] = acc;
     }
 
-    // ---- block maxima, one per K-scale half (tiles 0-1 and 2-3)
+    // ---- block maxima, one per K-scale group
     if (MASKED) {
         const int rel = row - T * SAGE_BN;  // this lane's row, relative to the block
         const int lim = N - T * SAGE_BN;    // keys at or past this are padding
@@ -177,26 +187,19 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                 if ((CAUSAL && kr > rel) || kr >= lim) S[t][v] = INT32_MIN;
             }
     }
-    int M0 = S[0][0], M1 = S[2][0];
+    float mt = -INFINITY;
 #pragma unroll
-    for (int v = 1; v < 16; ++v) {
-        M0 = max(M0, S[0][v]);
-        M1 = max(M1, S[2][v]);
-    }
+    for (int g = 0; g < KSPLIT; ++g) {
+        int M = S[g * TPG][0];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        M0 = max(M0, S[1][v]);
-        M1 = max(M1, S[3][v]);
+        for (int tt = 0; tt < TPG; ++tt)
+#pragma unroll
+            for (int v = (tt == 0 ? 1 : 0); v < 16; ++v) M = max(M, S[g * TPG + tt][v]);
+        M = max_across_halves(M);
+        float m = __builtin_fmaf(__builtin_bit_cast(float, M), c[g], -u[g]);
+        if (MASKED && M == INT32_MIN) m = -INFINITY;
+        mt = fmaxf(mt, m);
     }
-    M0 = max_across_halves(M0);
-    M1 = max_across_halves(M1);
-    float m0 = __builtin_fmaf(__builtin_bit_cast(float, M0), c0, -u0);
-    float m1 = __builtin_fmaf(__builtin_bit_cast(float, M1), c1, -u1);
-    if (MASKED) {
-        if (M0 == INT32_MIN) m0 = -INFINITY;
-        if (M1 == INT32_MIN) m1 = -INFINITY;
-    }
-    const float mt = fmaxf(m0, m1);
 
     // ---- lazy update of the reference maximum
     {
@@ -219,7 +222,9 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
     // accumulators, the P pieces and O fit in the architectural registers.
     constexpr int CG = CT < 2 ? CT : 2;
     const float e = l448 - mt;
-    const float bias0 = e - u0, bias1 = e - u1;
+    float bias[KSPLIT];
+#pragma unroll
+    for (int g = 0; g < KSPLIT; ++g) bias[g] = e - u[g];
     v8h P[8];
     v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -233,8 +238,8 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
         for (int s = 0; s < 8; ++s) {
             if (pass == 0) {
                 const int t = s >> 1, base = 8 * (s & 1);
-                const float c = t < 2 ? c0 : c1;
-                const float bias = t < 2 ? bias0 : bias1;
+                const float ct = c[t / TPG];
+                const float bt = bias[t / TPG];
                 // (bit_cast of the whole vector: this compiler mis-reads a
                 // bit_cast of a single vector element as element 0)
                 const v16f F = __builtin_bit_cast(v16f, S[t]);
@@ -245,7 +250,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int v = base + 4 * g + i;
-                        y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[v], c, bias));
+                        y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[v], ct, bt));
                         if (MASKED && S[t][v] == INT32_MIN) y[i] = 0.0f;
                     }
                     // the first conversion writes the low half; the high half
@@ -280,7 +285,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
     lsum = __builtin_fmaf(rs[0], w, lsum);
 }
 
-template <int D, bool CAUSAL, int WAVES, int WAVES_PER_SIMD>
+template <int D, int KSPLIT, bool CAUSAL, int WAVES, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs a) {
     constexpr int KS = D / 32;
     constexpr int CT = D / 32;
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 
     const uint8_t* kbase = (const uint8_t*)a.k_i8 + (long long)bg * a.Np * D;
     const uint16_t* vbase = a.v_e4m3 + (long long)bg * a.Np * D;
-    const float* ksc = a.k_scale + (long long)bg * (a.Np / SAGE_BK);
+    const float* ksc = a.k_scale + (long long)bg * (a.Np / (SAGE_BN / KSPLIT));
 
     // Q fragments (B operand of Q.K^T): query row r32, bytes [32*ks + 16*h, +16).
     v4i qf[KS];
@@ -331,7 +336,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const v4i*>(qp + 32 * ks);
     }
-    const float sq = a.q_scale[(long long)bh * (a.Np / SAGE_BQ) + rbase / SAGE_BQ];
+    // this lane's Q scale (its row's block, or its own row)
+    const float sq = a.q_scale[(long long)bh * (a.Np >> a.q_shift) + (row >> a.q_shift)];
 
     v16f O[CT];
     float mref = -INFINITY, lsum = 0.0f;
@@ -343,7 +349,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     // The K scales of a block are loaded one block ahead, before that block's
     // tile copy is issued: vector-memory waits count in issue order, so a
     // scale load issued after the copy would make its wait cover the copy too.
-    float2 kscale = *reinterpret_cast<const float2*>(ksc);
+    typedef float kvec __attribute__((ext_vector_type(KSPLIT)));
+    kvec kscale = *reinterpret_cast<const kvec*>(ksc);
     const TileLoader<D, WAVES> tiles(kbase, vbase, a.Np, wave, lane);
     tiles.load(0, lk0, lv0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -356,11 +363,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     for (; T < nA; ++T) {
         const bool odd = T & 1;
         const bool more = T + 1 < nblk;
-        const float2 knext = *reinterpret_cast<const float2*>(ksc + 2 * (more ? T + 1 : T));
+        const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
         if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
-        const float c0 = (sq * kscale.x) * a.qk, c1 = (sq * kscale.y) * a.qk;
-        attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
-                                     a.l448, h, r32, rsel, mref, lsum, O);
+        float c[KSPLIT];
+#pragma unroll
+        for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
+        attn_block<D, KSPLIT, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
+                                             a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -368,15 +377,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     for (; T < nblk; ++T) {
         const bool odd = T & 1;
         const bool more = T + 1 < nblk;
-        const float2 knext = *reinterpret_cast<const float2*>(ksc + 2 * (more ? T + 1 : T));
+        const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
         if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
-        const float c0 = (sq * kscale.x) * a.qk, c1 = (sq * kscale.y) * a.qk;
+        float c[KSPLIT];
+#pragma unroll
+        for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
         if (T < n_full)
-            attn_block<D, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
-                                         a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
+                                                 a.l448, h, r32, rsel, mref, lsum, O);
         else if (T <= wave_last)
-            attn_block<D, CAUSAL, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c0, c1,
-                                        a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
+                                                a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -426,25 +437,38 @@ constexpr int attn_waves_per_simd() {
 // Explicit instantiations: with the packed-FP32 feature switched off on the
 // command line, this compiler otherwise leaves the host stubs of some of these
 // kernels undefined.
-template __global__ void attn_fwd<64, false, attn_waves<64>(), attn_waves_per_simd<64>()>(AttnArgs);
-template __global__ void attn_fwd<64, true, attn_waves<64>(), attn_waves_per_simd<64>()>(AttnArgs);
-template __global__ void attn_fwd<128, false, attn_waves<128>(), attn_waves_per_simd<128>()>(AttnArgs);
-template __global__ void attn_fwd<128, true, attn_waves<128>(), attn_waves_per_simd<128>()>(AttnArgs);
+#define SAGE_ATTN_INST(D, KSPLIT, CAUSAL) \
+    template __global__ void attn_fwd<D, KSPLIT, CAUSAL, attn_waves<D>(), attn_waves_per_simd<D>()>(AttnArgs);
+SAGE_ATTN_INST(64, 2, false)
+SAGE_ATTN_INST(64, 2, true)
+SAGE_ATTN_INST(64, 4, false)
+SAGE_ATTN_INST(64, 4, true)
+SAGE_ATTN_INST(128, 2, false)
+SAGE_ATTN_INST(128, 2, true)
+SAGE_ATTN_INST(128, 4, false)
+SAGE_ATTN_INST(128, 4, true)
+#undef SAGE_ATTN_INST
 
-template <int D, bool CAUSAL>
+template <int D, int KSPLIT, bool CAUSAL>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WAVES = attn_waves<D>();
     constexpr int WPS = attn_waves_per_simd<D>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, CAUSAL, WAVES, WPS>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, WAVES, WPS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int total = a.B * a.Hq * a.nqt;
-    hipLaunchKernelGGL((attn_fwd<D, CAUSAL, WAVES, WPS>), dim3(total), dim3(64 * WAVES), lds, st, a);
+    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, WAVES, WPS>), dim3(total), dim3(64 * WAVES), lds,
+                       st, a);
     return hipGetLastError();
+}
+
+template <int D, int KSPLIT>
+static hipError_t launch_attn_d(AttnArgs a, int causal, hipStream_t st) {
+    return causal ? launch_attn_t<D, KSPLIT, true>(a, st) : launch_attn_t<D, KSPLIT, false>(a, st);
 }
 
 hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal,
@@ -464,10 +488,12 @@ hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int 
     a.Np = s.Np;
     a.G = s.Hq / s.Hkv;
     a.nqt = 0;
+    a.q_shift = z->q_block == SAGE_BQ ? 7 : 0;  // SAGE_BQ = 128, SAGE_BQ_THREAD = 1
     a.qk = qk;
     a.l448 = l448;
-    if (s.d == 64) return causal ? launch_attn_t<64, true>(a, st) : launch_attn_t<64, false>(a, st);
-    return causal ? launch_attn_t<128, true>(a, st) : launch_attn_t<128, false>(a, st);
+    const bool fine_k = z->k_block == SAGE_BK_THREAD;  // 4 K scales per block, else 2
+    if (s.d == 64) return fine_k ? launch_attn_d<64, 4>(a, causal, st) : launch_attn_d<64, 2>(a, causal, st);
+    return fine_k ? launch_attn_d<128, 4>(a, causal, st) : launch_attn_d<128, 2>(a, causal, st);
 }
 
 }  // namespace sage

@@ -4,14 +4,18 @@
 // for V).  Memory-bound: every kernel streams 16-byte loads and does its
 // reductions in registers, wavefront shuffles and LDS.
 //
-//   prep_q      per (q head, 128-row block): Q absmax, scale and INT8 codes;
+//   prep_q      per (q head, 128-row block): Q absmax per scale group (the
+//               block, or each row at the thread-level granularity), scales
+//               and INT8 codes;
 //               one extra work-group clears the per-head arrival counters.
 //   prep_stats  per (kv head, 512-row chunk): partial statistics (float64 K
 //               channel sums, V channel absmax).  The head's last work-group
 //               to arrive (an atomic counter; nobody waits) reduces the
 //               partials in a fixed chunk order (deterministic) into the K
 //               mean and the V scales.
-//   prep_pack   per (kv head, 64-row block) K - mean, absmax, scale, codes;
+//   prep_pack   per (kv head, 64-row block) K - mean, absmax per scale group
+//               (the block, or each 32-row half at the thread-level
+//               granularity), scales, codes;
 //               per (kv head, 128-key block) V E4M3 codes, stored as the
 //               binary16 values they denote and transposed to the attention
 //               kernel's channel-major, permuted-key layout.  Heads are
@@ -39,6 +43,40 @@ __device__ inline uint2 int8_codes(const float (&x)[8], float inv) {
         w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (i & 3));
     }
     return make_uint2(w[0], w[1]);
+}
+
+// Absolute maxima over groups of G rows (G a power of two dividing R, the
+// work-group's rows).  On entry am[c] is this thread's absmax over the 8
+// values of its chunk c, which lies in row (tid + c * kThreads) / CPR; on
+// return it is the absmax over that row's group.  rmax and gmax are R floats
+// of LDS each.
+template <int CPR, int R, int NCH>
+__device__ inline void group_absmax(float (&am)[NCH], int G, float* rmax, float* gmax) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int o = CPR / 2; o > 0; o >>= 1) am[c] = fmaxf(am[c], __shfl_xor(am[c], o));
+    if (G == 1) return;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (tid % CPR == 0) rmax[(tid + c * kThreads) / CPR] = am[c];
+    __syncthreads();
+    const int span = G < 64 ? G : 64;  // rows reduced within one wavefront
+    if (tid < R) {
+        float m = rmax[tid];
+        for (int o = 1; o < span; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if ((tid & (span - 1)) == 0) gmax[tid / span] = m;
+    }
+    __syncthreads();
+    const int per = G / span;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int g = (tid + c * kThreads) / CPR / G;
+        float m = gmax[g * per];
+        for (int j = 1; j < per; ++j) m = fmaxf(m, gmax[g * per + j]);
+        am[c] = m;
+    }
 }
 
 // The binary16 values of the E4M3 codes of x[i] * inv[i], i = 0..7, into the
@@ -77,31 +115,32 @@ __device__ inline void store_v_tile(const uint16_t* vt, uint16_t* dst, int tid) 
 }
 
 // ------------------------------------------------------------ Q
+// One work-group per 128 rows of a q head; one scale per bq rows (128 or 1).
 template <typename In, int D>
-__global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ q, Shape s,
+__global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ q, Shape s, int bq,
                                                    int8_t* __restrict__ q_i8,
                                                    float* __restrict__ q_scale,
                                                    int* __restrict__ sync) {
     constexpr int CPR = D / 8;  // 16-byte chunks per row
-    __shared__ float red[4];
+    constexpr int R = 128;      // rows per work-group
+    constexpr int NCH = R * CPR / kThreads;  // chunks per thread
+    __shared__ float rmax[R], gmax[R];
     const int tid = threadIdx.x;
-    const int nqt = s.Np / SAGE_BQ;
+    const int nwg = s.Np / R;
     const int qb = blockIdx.x;
-    if (qb == s.B * s.Hq * nqt) {
+    if (qb == s.B * s.Hq * nwg) {
         for (int i = tid; i < sync_words(s); i += kThreads) sync[i] = 0;
         return;
     }
-    // rows [t*BQ, t*BQ+BQ) of head bh; rows >= N are zero padding
-    const int bh = qb / nqt, t = qb % nqt;
-    constexpr int NCH = SAGE_BQ * CPR / kThreads;  // chunks per thread
+    // rows [t*R, t*R+R) of head bh; rows >= N are zero padding
+    const int bh = qb / nwg, t = qb % nwg;
     const long long src_head = (long long)bh * s.N * D;
     const long long dst_head = (long long)bh * s.Np * D;
-    float x[NCH][8];
-    float a = 0.0f;
+    float x[NCH][8], am[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
-        const int row = t * SAGE_BQ + e / CPR, col = (e % CPR) * 8;
+        const int row = t * R + e / CPR, col = (e % CPR) * 8;
         if (row < s.N) {
             const uint4 u = *reinterpret_cast<const uint4*>(q + src_head + (long long)row * D + col);
             unpack8<In>(u, x[c]);
@@ -109,16 +148,19 @@ __global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ 
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[c][i] = 0.0f;
         }
+        am[c] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[c][i]));
+        for (int i = 0; i < 8; ++i) am[c] = fmaxf(am[c], fabsf(x[c][i]));
     }
-    a = block_max(a, red);
-    const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-    if (tid == 0) q_scale[(long long)bh * nqt + t] = a / 127.0f;
+    group_absmax<CPR, R, NCH>(am, bq, rmax, gmax);
+    const long long sbase = (long long)bh * (s.Np / bq);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
-        const int row = t * SAGE_BQ + e / CPR, col = (e % CPR) * 8;
+        const int row = t * R + e / CPR, col = (e % CPR) * 8;
+        const float a = am[c];
+        if (e % CPR == 0 && row % bq == 0) q_scale[sbase + row / bq] = a / 127.0f;
+        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
         *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv);
     }
 }
@@ -203,14 +245,14 @@ __global__ __launch_bounds__(kThreads) void prep_stats(
 
 template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_pack(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s, int bk,
     const float* __restrict__ k_mean, const float* __restrict__ v_inv,
     int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint16_t* __restrict__ v_e4m3) {
     constexpr int CPR = D / 8;
-    __shared__ float red[4];
+    __shared__ float rmax[64], gmax[64];
     __shared__ __attribute__((aligned(16))) uint16_t vt[D * SAGE_BN];
     const int tid = threadIdx.x;
-    const int nkb = s.Np / SAGE_BK, nvb = s.Np / SAGE_BN;
+    const int nkb = s.Np / 64, nvb = s.Np / SAGE_BN;
     const int per_head = nkb + nvb;
     // reverse head order relative to prep_stats
     const int bg = s.B * s.Hkv - 1 - (int)(blockIdx.x / per_head);
@@ -218,15 +260,16 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     const long long src_head = (long long)bg * s.N * D;
 
     if (j < nkb) {
+        // K rows [t*64, t*64+64): smoothed, one scale per bk rows (64 or 32)
         const int t = j;
-        constexpr int NCH = SAGE_BK * CPR / kThreads;
+        constexpr int R = 64;
+        constexpr int NCH = R * CPR / kThreads;
         const long long dst_head = (long long)bg * s.Np * D;
-        float x[NCH][8];
-        float a = 0.0f;
+        float x[NCH][8], am[NCH];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int e = tid + c * kThreads;
-            const int row = t * SAGE_BK + e / CPR, col = (e % CPR) * 8;
+            const int row = t * R + e / CPR, col = (e % CPR) * 8;
             if (row < s.N) {
                 const uint4 u = *reinterpret_cast<const uint4*>(k + src_head + (long long)row * D + col);
                 unpack8<In>(u, x[c]);
@@ -237,16 +280,19 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) x[c][i] = 0.0f;
             }
+            am[c] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[c][i]));
+            for (int i = 0; i < 8; ++i) am[c] = fmaxf(am[c], fabsf(x[c][i]));
         }
-        a = block_max(a, red);
-        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-        if (tid == 0) k_scale[(long long)bg * nkb + t] = a / 127.0f;
+        group_absmax<CPR, R, NCH>(am, bk, rmax, gmax);
+        const long long sbase = (long long)bg * (s.Np / bk);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int e = tid + c * kThreads;
-            const int row = t * SAGE_BK + e / CPR, col = (e % CPR) * 8;
+            const int row = t * R + e / CPR, col = (e % CPR) * 8;
+            const float a = am[c];
+            if (e % CPR == 0 && row % bk == 0) k_scale[sbase + row / bk] = a / 127.0f;
+            const float inv = a > 0.0f ? 127.0f / a : 0.0f;
             *reinterpret_cast<uint2*>(k_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv);
         }
         return;
@@ -278,9 +324,9 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
 template <typename In, int D>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const Shape& s,
                                 const sage_qkv_quant* z, hipStream_t st) {
-    const int nq = s.B * s.Hq * (s.Np / SAGE_BQ);
+    const int nq = s.B * s.Hq * (s.Np / 128);
     hipLaunchKernelGGL((prep_q<In, D>), dim3(nq + 1), dim3(kThreads), 0, st, (const uint16_t*)q, s,
-                       z->q_i8, z->q_scale, z->sync);
+                       (int)z->q_block, z->q_i8, z->q_scale, z->sync);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nchunk = s.part_chunks();
@@ -289,10 +335,10 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
                        z->k_mean, z->v_scale, z->v_inv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int per_head = s.Np / SAGE_BK + s.Np / SAGE_BN;
+    const int per_head = s.Np / 64 + s.Np / SAGE_BN;
     hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, s, z->k_mean, z->v_inv, z->k_i8,
-                       z->k_scale, z->v_e4m3);
+                       (const uint16_t*)k, (const uint16_t*)v, s, (int)z->k_block, z->k_mean,
+                       z->v_inv, z->k_i8, z->k_scale, z->v_e4m3);
     return hipGetLastError();
 }
 

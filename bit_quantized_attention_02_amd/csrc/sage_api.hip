@@ -48,8 +48,9 @@ static Layout layout(const Shape& s) {
     L.q_i8 = take((size_t)s.q_elems());
     L.k_i8 = take((size_t)s.kv_elems());
     L.v_e4m3 = take((size_t)s.kv_elems() * sizeof(uint16_t));
-    L.q_scale = take(Bq * (s.Np / SAGE_BQ) * sizeof(float));
-    L.k_scale = take(Bkv * (s.Np / SAGE_BK) * sizeof(float));
+    // scales sized for the finer of the two granularities
+    L.q_scale = take(Bq * (s.Np / SAGE_BQ_THREAD) * sizeof(float));
+    L.k_scale = take(Bkv * (s.Np / SAGE_BK_THREAD) * sizeof(float));
     L.k_mean = take(Bkv * s.d * sizeof(float));
     L.v_scale = take(Bkv * s.d * sizeof(float));
     L.v_inv = take(Bkv * s.d * sizeof(float));
@@ -60,8 +61,14 @@ static Layout layout(const Shape& s) {
     return L;
 }
 
+static bool granularity_ok(int q_block, int k_block) {
+    return (q_block == SAGE_BQ && k_block == SAGE_BK) ||
+           (q_block == SAGE_BQ_THREAD && k_block == SAGE_BK_THREAD);
+}
+
 static int check_quant(const sage_qkv_quant* z) {
     if (!z) return SAGE_ERR_INVALID_ARG;
+    if (!granularity_ok(z->q_block, z->k_block)) return SAGE_ERR_UNSUPPORTED;
     if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v_e4m3 ||
         !z->v_scale || !z->v_inv || !z->k_part || !z->v_part || !z->sync)
         return SAGE_ERR_INVALID_ARG;
@@ -98,6 +105,8 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->k_part = (double*)(base + L.k_part);
     out->v_part = (float*)(base + L.v_part);
     out->sync = (int32_t*)(base + L.sync);
+    out->q_block = SAGE_BQ;
+    out->k_block = SAGE_BK;
     return SAGE_OK;
 }
 
@@ -133,11 +142,13 @@ int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
-int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
-                  int N, int d, int causal, float sm_scale, int dtype, void* workspace,
-                  size_t ws_bytes, void* stream) {
+int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                           int Hkv, int N, int d, int causal, float sm_scale, int dtype,
+                           int q_block, int k_block, void* workspace, size_t ws_bytes,
+                           void* stream) {
     int rc = check_shape(B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
+    if (!granularity_ok(q_block, k_block)) return SAGE_ERR_UNSUPPORTED;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
     if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
@@ -147,9 +158,18 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
     sage_qkv_quant z;
     rc = sage_workspace_carve(workspace, ws_bytes, B, Hq, Hkv, N, d, &z);
     if (rc != SAGE_OK) return rc;
+    z.q_block = q_block;
+    z.k_block = k_block;
     rc = sage_quantize(q, k, v, dtype, B, Hq, Hkv, N, d, &z, stream);
     if (rc != SAGE_OK) return rc;
     return sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, causal, sm_scale, stream);
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                  int N, int d, int causal, float sm_scale, int dtype, void* workspace,
+                  size_t ws_bytes, void* stream) {
+    return sage_attn_fwd_granular(q, k, v, out, B, Hq, Hkv, N, d, causal, sm_scale, dtype, SAGE_BQ,
+                                  SAGE_BK, workspace, ws_bytes, stream);
 }
 
 int sage_get_config(sage_config* c) {
@@ -171,7 +191,9 @@ const char* sage_status_string(int status) {
     switch (status) {
         case SAGE_OK: return "ok";
         case SAGE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad flag or size)";
-        case SAGE_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128, Hq % Hkv == 0, N <= 2^20)";
+        case SAGE_ERR_UNSUPPORTED:
+            return "unsupported shape or granularity (d must be 64 or 128, Hq % Hkv == 0, N <= 2^20; "
+                   "(q_block, k_block) = (128, 64) or (1, 32))";
         case SAGE_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
         case SAGE_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";

@@ -18,9 +18,14 @@
  *
  * Spec details the pages leave open (the CPU oracle under oracle/ follows the
  * same ones):
- *   - INT8: symmetric, +-127, code = rne(x * f32(127/absmax)) in float32; one
- *     Q scale per SAGE_BQ query rows, one K scale per SAGE_BK keys; an all-zero
- *     block has scale 0.
+ *   - INT8: symmetric, +-127, code = rne(x * f32(127/absmax)) in float32; an
+ *     all-zero block has scale 0.  Two granularities: per block (the default:
+ *     one Q scale per SAGE_BQ query rows, one K scale per SAGE_BK keys, the
+ *     flash tile of the SageAttention article) and thread-level (one Q scale
+ *     per query row -- each lane of the attention kernel owns one row -- and
+ *     one K scale per 32-key matrix-core tile; the Berkeley brief's checklist
+ *     item on thread-level block quantization).  sage_qkv_quant.q_block and
+ *     .k_block select it.
  *   - FP8: OCP E4M3FN (max 448), round to nearest even.  V: one scale per
  *     channel, code = e4m3(v * f32(448/absmax_c)).
  *   - P: one block is one query row by SAGE_BN keys; with m the block's largest
@@ -64,6 +69,8 @@ extern "C" {
 #define SAGE_FP8_MAX 448  /* largest finite E4M3FN value */
 #define SAGE_NPAD 256     /* sequence padding of the quantized operands */
 #define SAGE_MAX_N (1 << 20)
+#define SAGE_BQ_THREAD 1  /* query rows per Q scale, thread-level granularity */
+#define SAGE_BK_THREAD 32 /* keys per K scale, thread-level granularity */
 
 typedef enum {
     SAGE_OK = 0,
@@ -84,11 +91,11 @@ typedef struct {
 /*
  * Device-side views of the quantized operands inside a workspace (filled by
  * sage_workspace_carve).  N_p = N rounded up to a multiple of SAGE_NPAD; rows
- * N..N_p-1 are zero padding.
+ * N..N_p-1 are zero padding.  bq = q_block, bk = k_block below.
  *   q_i8    int8 [B, Hq, N_p, d]            row-major, d innermost
- *   q_scale f32  [B, Hq, N_p / SAGE_BQ]
+ *   q_scale f32  [B, Hq, N_p / bq]
  *   k_i8    int8 [B, Hkv, N_p, d]           codes of K - k_mean
- *   k_scale f32  [B, Hkv, N_p / SAGE_BK]
+ *   k_scale f32  [B, Hkv, N_p / bk]
  *   k_mean  f32  [B, Hkv, d]
  *   v_e4m3  binary16 [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: the E4M3 codes of V,
  *           each stored as the binary16 number it denotes (exact: every E4M3
@@ -114,6 +121,8 @@ typedef struct {
     double* k_part;
     float* v_part;
     int32_t* sync;
+    int32_t q_block; /* query rows per Q scale: SAGE_BQ (set by sage_workspace_carve) or SAGE_BQ_THREAD */
+    int32_t k_block; /* keys per K scale: SAGE_BK (set by sage_workspace_carve) or SAGE_BK_THREAD */
 } sage_qkv_quant;
 
 /* Bytes of workspace sage_quantize/sage_attn_fwd need for this shape (0 when
@@ -121,7 +130,12 @@ typedef struct {
 size_t sage_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /* Split `workspace` (device memory, 256-byte aligned, ws_bytes long) into the
- * views above.  Host-only; no HIP call. */
+ * views above, with the per-block granularity (q_block = SAGE_BQ, k_block =
+ * SAGE_BK); the caller may then switch both to SAGE_BQ_THREAD and
+ * SAGE_BK_THREAD (the workspace holds the scales of either).  The quantize and
+ * attention calls given the struct read the granularity from it; any other
+ * pair of values makes them return SAGE_ERR_UNSUPPORTED.  Host-only; no HIP
+ * call. */
 int sage_workspace_carve(void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
                          sage_qkv_quant* out);
 
@@ -146,6 +160,15 @@ int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq
 int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                   int N, int d, int causal, float sm_scale, int dtype, void* workspace,
                   size_t ws_bytes, void* stream);
+
+/* sage_attn_fwd with the quantization granularity chosen by the caller:
+ * (q_block, k_block) = (SAGE_BQ, SAGE_BK) is sage_attn_fwd itself,
+ * (SAGE_BQ_THREAD, SAGE_BK_THREAD) the thread-level granularity; any other
+ * pair returns SAGE_ERR_UNSUPPORTED. */
+int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                           int Hkv, int N, int d, int causal, float sm_scale, int dtype,
+                           int q_block, int k_block, void* workspace, size_t ws_bytes,
+                           void* stream);
 
 /* Block sizes and format constants of this build. */
 int sage_get_config(sage_config* c);

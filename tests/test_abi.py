@@ -69,8 +69,10 @@ def test_carve_checks_alignment_and_size(sage):
     fake = 1 << 40  # never dereferenced: carving is host arithmetic only
     rc, z = _carve(sage, fake, need, shape)
     assert rc == 0
-    ptrs = [getattr(z, f) for f, _ in sage.sage_qkv_quant._fields_]
+    ptrs = [getattr(z, f) for f, t in sage.sage_qkv_quant._fields_ if t is ctypes.c_void_p]
+    assert len(ptrs) == 11
     assert all(p % 256 == 0 for p in ptrs) and len(set(ptrs)) == len(ptrs)
+    assert (z.q_block, z.k_block) == (128, 64)
     assert max(ptrs) < fake + need
     assert _carve(sage, fake, need - 1, shape)[0] == sage.SAGE_ERR_WORKSPACE
     assert _carve(sage, fake + 16, need, shape)[0] == sage.SAGE_ERR_WORKSPACE
@@ -127,15 +129,27 @@ def test_entry_points_reject_bad_arguments_before_any_hip_call(sage):
     assert L.sage_get_config(None) == sage.SAGE_ERR_INVALID_ARG
 
 
-def test_binding_fails_loudly_without_library(tmp_path):
-    """Importing the binding from a copy without libsage.so must raise, never
-    fall back to another implementation."""
-    import shutil
-    import subprocess
-    import sys
-    pkg = tmp_path / "bit_quantized_attention_02_amd"
-    pkg.mkdir()
-    shutil.copy(os.path.join(ROOT, "bit_quantized_attention_02_amd", "__init__.py"), pkg)
-    r = subprocess.run([sys.executable, "-c", "import bit_quantized_attention_02_amd"],
-                       cwd=tmp_path, capture_output=True, text=True)
-    assert r.returncode != 0 and "not built" in r.stderr
+def test_granularity_is_validated(sage):
+    """Only (128, 64) and (1, 32) are accepted, by the struct-taking calls and
+    by sage_attn_fwd_granular; both fit the same workspace."""
+    L = sage._lib
+    fake = 1 << 40
+    shape = (1, 4, 2, 300, 64)
+    need = sage.sage_workspace_bytes(*shape)
+    f = ctypes.c_float
+    bad = sage.SAGE_ERR_UNSUPPORTED
+    for qb, kb, ok in ((128, 64, True), (1, 32, True), (1, 64, False), (128, 32, False),
+                       (32, 32, False), (0, 0, False)):
+        rc = L.sage_attn_fwd_granular(fake, fake, fake, None, *shape, 0, f(0.125), 0, qb, kb, fake,
+                                      need, None)
+        # the granularity is checked before the pointers: a valid pair gets as
+        # far as the null `out`
+        assert rc == (sage.SAGE_ERR_INVALID_ARG if ok else bad)
+        if not ok:
+            rc, z = _carve(sage, fake, need, shape)
+            z.q_block, z.k_block = qb, kb
+            zp = ctypes.byref(z)
+            assert L.sage_quantize(fake, fake, fake, 0, *shape, zp, None) == bad
+            assert L.sage_attn_fwd_quantized(zp, fake, *shape, 0, f(0.125), None) == bad
+    z = sage.sage_workspace_carve(fake, need, *shape, granularity="thread")
+    assert (z.q_block, z.k_block) == (sage.SAGE_BQ_THREAD, sage.SAGE_BK_THREAD)

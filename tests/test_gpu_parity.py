@@ -32,12 +32,12 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(sage, q, k, v, causal, sm_scale):
+def run_gpu(sage, q, k, v, causal, sm_scale, granularity="block"):
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     ws = sage.workspace_for(qd, kd)
-    z = sage.sage_workspace_carve(ws, ws.numel(), B, Hq, Hkv, N, d)
+    z = sage.sage_workspace_carve(ws, ws.numel(), B, Hq, Hkv, N, d, granularity=granularity)
     sage.sage_quantize(qd, kd, vd, z)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     sage.sage_attn_fwd_quantized(z, out, B, Hq, Hkv, N, d, causal, sm_scale)
@@ -78,16 +78,23 @@ def _rows_of(out, rows, d):
     return out.reshape(-1, d).cpu().numpy()[rows]
 
 
+def quantize_as(orc, q, k, v, granularity):
+    bq, bk = {"block": (128, 64), "thread": (1, 32)}[granularity]
+    return orc.quantize(q, k, v, bq=bq, bk=bk)
+
+
+@pytest.mark.parametrize("granularity", ["block", "thread"])
 @pytest.mark.parametrize("recipe", [1, 2, 3, 4, 5])
-def test_parity_reduced_workloads(sage, orc, recipe):
+def test_parity_reduced_workloads(sage, orc, recipe, granularity):
     """Each workload's recipe at a size the oracle covers in full: several
     128-row tiles and a ragged tail (N = 700)."""
     w0 = workloads.WORKLOADS[recipe]
     w = w0.resized(B=2, Hq=2 * (w0.Hq // w0.Hkv), Hkv=2, N=700)
-    _say(f"case recipe={recipe} shape={(w.B, w.Hq, w.Hkv, w.N, w.d)} causal={w.causal}")
+    _say(f"case recipe={recipe} shape={(w.B, w.Hq, w.Hkv, w.N, w.d)} causal={w.causal} "
+         f"granularity={granularity}")
     q, k, v = workloads.generate(w, seed=1000 + recipe)
-    out, quant = run_gpu(sage, q, k, v, w.causal, w.sm_scale)
-    oz = orc.quantize(q, k, v)
+    out, quant = run_gpu(sage, q, k, v, w.causal, w.sm_scale, granularity)
+    oz = quantize_as(orc, q, k, v, granularity)
     check_prep(orc, quant, oz)
     rows = np.arange(w.B * w.Hq * w.N)
     check_attn(orc, out.reshape(-1, w.d).cpu().numpy(), oz, w.causal, w.sm_scale, rows)
@@ -97,11 +104,12 @@ def test_parity_reduced_workloads(sage, orc, recipe):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_parity_edge_lengths(sage, orc, N, d, causal):
-    _say(f"case N={N} d={d} causal={causal}")
+    granularity = "thread" if N in (17, 129, 300) else "block"
+    _say(f"case N={N} d={d} causal={causal} granularity={granularity}")
     q, k, v = workloads.random_inputs(1, 4, 2, N, d, "f16" if d == 64 else "bf16",
                                       seed=N * 7 + d + causal, scale=1.5)
-    out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d))
-    oz = orc.quantize(q, k, v)
+    out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d), granularity)
+    oz = quantize_as(orc, q, k, v, granularity)
     check_prep(orc, quant, oz)
     check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 1 / math.sqrt(d), None)
 
@@ -116,10 +124,10 @@ def test_degenerate_inputs(sage, orc):
     v[0, 0, :, 3] = 0.0
     k[0, 0, 100] = 12.0
     q[0, 1, :, :] = q[0, 1, :, :].abs()
-    for causal in (False, True):
-        _say(f"case degenerate causal={causal}")
-        out, quant = run_gpu(sage, q, k, v, causal, 0.125)
-        oz = orc.quantize(q, k, v)
+    for causal, granularity in ((False, "block"), (True, "block"), (True, "thread")):
+        _say(f"case degenerate causal={causal} granularity={granularity}")
+        out, quant = run_gpu(sage, q, k, v, causal, 0.125, granularity)
+        oz = quantize_as(orc, q, k, v, granularity)
         check_prep(orc, quant, oz)
         check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 0.125, None)
 
@@ -162,25 +170,28 @@ def test_sage_attn_fwd_matches_two_step_path(sage):
     assert torch.equal(one, two)
 
 
-@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
-def test_parity_full_size_workloads(sage, orc, index):
+@pytest.mark.parametrize("index,granularity", [(1, "block"), (2, "block"), (3, "block"), (4, "block"),
+                                               (5, "block"), (3, "thread"), (4, "thread"),
+                                               (5, "thread")])
+def test_parity_full_size_workloads(sage, orc, index, granularity):
     """Each workload at its full size, through sage_attn_fwd as the benchmark
     times it: the prep outputs are compared in full (bit-exact), the attention
     output on sampled rows the oracle computes one by one (first and last row
     of the first and last head, 256 seeded rows, and for the peaked-row recipe
     some of the x20 rows)."""
     w = workloads.WORKLOADS[index]
-    _say(f"case full-size workload {index} {w.name}")
+    _say(f"case full-size workload {index} {w.name} granularity={granularity}")
     q, k, v = workloads.generate(w)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
     ws = sage.workspace_for(qd, kd)
-    sage.sage_attn_fwd(qd, kd, vd, out, w.causal, w.sm_scale, ws)
+    qb, kb = sage.GRANULARITY[granularity]
+    sage.sage_attn_fwd_granular(qd, kd, vd, out, w.causal, w.sm_scale, qb, kb, ws)
     torch.cuda.synchronize()
-    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d)
+    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d, granularity=granularity)
     quant = sage.read_quantized(z, ws, w.B, w.Hq, w.Hkv, w.N, w.d)
     del qd, kd, vd
-    oz = orc.quantize(q, k, v)
+    oz = quantize_as(orc, q, k, v, granularity)
     check_prep(orc, quant, oz)
     rows = workloads.sample_rows(w, 256, seed=11)
     if w.recipe == 4:
