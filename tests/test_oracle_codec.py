@@ -85,6 +85,27 @@ def test_int8_blocks_round_half_even_within_half_step(orc, N, d):
                 assert np.all(err <= (0.5 + 1e-4) * s)
 
 
+@pytest.mark.parametrize("bq,bk", [(1, 32), (128, 64)])
+def test_scale_groups_of_both_granularities(orc, bq, bk):
+    """Q scales per bq rows and K scales per bk keys, each the group's absmax /
+    127 with numpy's rint on the float32 product, for the per-block and the
+    thread-level (per-row Q, 32-key K) granularities; ragged last groups."""
+    N, d = 70, 64
+    q, k, v = workloads.random_inputs(1, 2, 2, N, d, "bf16", seed=bq + bk, scale=2.0)
+    z = orc.quantize(q, k, v, bq=bq, bk=bk)
+    assert z["q_scale"].shape[-1] == -(-N // bq) and z["k_scale"].shape[-1] == -(-N // bk)
+    q32 = orc.to_f32(q)
+    ks = orc.to_f32(k) - z["k_mean"][:, :, None, :]
+    for x, codes, scales, g in ((q32, z["q_i8"], z["q_scale"], bq), (ks, z["k_i8"], z["k_scale"], bk)):
+        for h in range(2):
+            for t in range(-(-N // g)):
+                blk = x[0, h, t * g:(t + 1) * g]
+                a = np.abs(blk).max()
+                assert scales[0, h, t] == np.float32(a) / np.float32(127.0)
+                ref = np.clip(np.rint(blk * (np.float32(127.0) / np.float32(a))), -127, 127)
+                np.testing.assert_array_equal(codes[0, h, t * g:(t + 1) * g], ref.astype(np.int8))
+
+
 def test_k_mean_is_the_token_mean_and_smoothed_codes_bound_k_minus_mean(orc):
     w = workloads.WORKLOADS[1].resized(N=333)
     q, k, v = workloads.generate(w, seed=11)
