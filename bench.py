@@ -40,6 +40,12 @@ def parse():
                    help="Q/K scale granularity: block (128 rows / 64 keys) or thread (per row / 32 keys)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
+    p.add_argument("--contrast", action="store_true",
+                   help="also time torch's scaled_dot_product_attention (flash backend only) in the "
+                        "input dtype on the same inputs: the native attention this path replaces")
+    p.add_argument("--prep-flush", action="store_true",
+                   help="also time the prep step alone with a 512 MB write between launches, so the "
+                        "last-level cache holds none of its inputs")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="instead of the benchmark, run a plain device-to-device copy of BYTES "
                         "bytes 5 times: a known-size reference for hardware byte counters")
@@ -72,6 +78,43 @@ def timed(fn, iters, torch):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / iters
+
+
+def contrast_sdpa(w, qd, kd, vd, steps, torch):
+    """Native attention on the same inputs: torch SDPA restricted to its flash
+    backend (it raises rather than falling back to the unfused math path)."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    kw = {"enable_gqa": True} if w.Hq != w.Hkv else {}
+
+    def run():
+        return torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, is_causal=w.causal,
+                                                                scale=w.sm_scale, **kw)
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            run()
+            torch.cuda.synchronize()
+            ms = timed(run, steps, torch)
+    except RuntimeError as e:
+        return {"kind": "torch sdpa flash", "error": str(e).splitlines()[0][:200]}
+    return {"kind": f"torch {torch.__version__} scaled_dot_product_attention, flash backend, "
+                    f"{w.dtype} in and out", "ms_per_call": round(ms, 4),
+            "TOPS": round(w.ops / (ms * 1e-3) / 1e12, 2)}
+
+
+def prep_flushed(sage, qd, kd, vd, z, steps, torch):
+    """sage_quantize alone, each launch timed on its own after a 512 MB write."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=qd.device)
+    times = []
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        sage.sage_quantize(qd, kd, vd, z)
+        s1.record()
+        torch.cuda.synchronize()
+        times.append(s0.elapsed_time(s1))
+    times.sort()
+    return times[len(times) // 2]
 
 
 def cpu_baseline(w, q, k, v, rows_wanted, bq, bk):
@@ -174,6 +217,12 @@ def main():
                  "frac_hbm": round(prep_gbs / HBM_PEAK_GBS, 4)},
         "timed_wall_s": round(wall, 3),
     }
+    if args.prep_flush:
+        ms_pf = prep_flushed(sage, qd, kd, vd, z, max(args.steps, 20), torch)
+        line["prep"]["flushed_median_ms"] = round(ms_pf, 4)
+        line["prep"]["flushed_alg_GBps"] = round(3.0 * elems / (ms_pf * 1e-3) / 1e9, 1)
+    if args.contrast:
+        line["contrast"] = contrast_sdpa(w, qd, kd, vd, args.steps, torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, qb, kb)
     print(json.dumps(line), flush=True)
