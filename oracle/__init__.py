@@ -61,9 +61,15 @@ def _load():
         lib.oracle_e4m3_encode.argtypes = [dd]
         lib.oracle_e4m3_encode_array.argtypes = [P, l, P]
         lib.oracle_e4m3_decode_array.argtypes = [P, l, P]
+        lib.oracle_f16_decode.restype = dd
+        lib.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_encode.restype = ctypes.c_uint16
+        lib.oracle_f16_encode.argtypes = [dd]
+        lib.oracle_f16_encode_array.argtypes = [P, l, P]
+        lib.oracle_f16_decode_array.argtypes = [P, l, P]
         lib.oracle_quantize.argtypes = [P, P, P, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
-        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, f, dd, P, l,
-                                      P, P, P, P]
+        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, f, dd, P,
+                                      l, P, P, P, P]
         lib.oracle_attn_f64.argtypes = [P, P, P, i, i, i, i, i, i, dd, P, l, P]
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -99,9 +105,33 @@ def e4m3_decode(c) -> np.ndarray:
     return out
 
 
-def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True) -> dict:
+def f16_encode(x) -> np.ndarray:
+    """binary16 codes (uint16), round to nearest even, saturating at +-65504."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_f16_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def f16_decode(c) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(c, dtype=np.uint16))
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_f16_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+# P.V formats: P and V as E4M3 (per-block P scale, per-channel V scale), or as
+# binary16 (SageAttention's own P.V, accumulated in FP32 here)
+PV_FORMATS = ("e4m3", "f16")
+
+
+def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True, pv: str = "e4m3") -> dict:
     """The prep step on [B,H,N,d] inputs.  Returns codes in the plain logical
-    layout [B,H,N,d] and the scales (see oracle_quantize in oracle.c)."""
+    layout [B,H,N,d] and the scales (see oracle_quantize in oracle.c).  With
+    pv="f16" it also returns v_f16, the binary16 codes of V, which attn_q then
+    uses (no V scale)."""
+    if pv not in PV_FORMATS:
+        raise ValueError(f"pv must be one of {PV_FORMATS}")
     q, k, v = to_f32(q), to_f32(k), to_f32(v)
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -115,14 +145,20 @@ def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True) -> dict:
                             _ptr(r["q_i8"]), _ptr(r["q_scale"]), _ptr(r["k_i8"]),
                             _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(r["v_fp8"]),
                             _ptr(r["v_scale"]))
-    r.update(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, bq=bq, bk=bk)
+    if pv == "f16":
+        r["v_f16"] = f16_encode(v)
+    r.update(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, bq=bq, bk=bk, pv=pv)
     return r
 
 
 def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
            tau: float = TAU, interval: bool = True):
     """Quantized attention from the prep outputs `qz` for the given flattened
-    rows (None = all).  Returns (out, lo, hi, flagged), float64 [nrows, d]."""
+    rows (None = all), in the P.V format qz["pv"] was made for.  Returns
+    (out, lo, hi, flagged), float64 [nrows, d]."""
+    f16 = qz.get("pv", "e4m3") == "f16"
+    v_codes = qz["v_f16"] if f16 else qz["v_fp8"]
+    v_scale = None if f16 else qz["v_scale"]
     B, Hq, Hkv, N, d = qz["B"], qz["Hq"], qz["Hkv"], qz["N"], qz["d"]
     if rows is not None:
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
@@ -134,7 +170,7 @@ def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
     hi = np.empty((nrows, d), np.float64) if interval else None
     flagged = np.empty(nrows, np.int64) if interval else None
     _load().oracle_attn_q(_ptr(qz["q_i8"]), _ptr(qz["q_scale"]), _ptr(qz["k_i8"]),
-                          _ptr(qz["k_scale"]), _ptr(qz["v_fp8"]), _ptr(qz["v_scale"]),
+                          _ptr(qz["k_scale"]), _ptr(v_codes), _ptr(v_scale), int(f16),
                           B, Hq, Hkv, N, d, qz["bq"], qz["bk"], bn, int(causal),
                           float(sm_scale), float(tau), _ptr(rows), nrows,
                           _ptr(out), _ptr(lo), _ptr(hi), _ptr(flagged))

@@ -40,6 +40,14 @@
  *     differently (float64 here).  Codes whose 2^x lies within a relative
  *     `tau` of a rounding midpoint have two correct values; the oracle
  *     returns the interval spanned by both choices.
+ *
+ * The binary16 P.V mode (SageAttention article, paragraph on the P, V product:
+ * P and V stay FP16 there, with an FP16 accumulator).  The matrix cores this
+ * library targets accumulate binary16 products in FP32 only, so the mode keeps
+ * P and V in IEEE binary16 and the two accumulation levels in FP32/float64:
+ *   - V16 = f16(v), round to nearest even, saturating at +-65504; no V scale.
+ *   - P16 = f16(2^x) with x as above but log2(448) replaced by 0, so the
+ *     block's largest element is exactly 1 (P stays in (0, 1]).
  */
 #include <math.h>
 #include <stdint.h>
@@ -94,6 +102,50 @@ void oracle_e4m3_encode_array(const double* x, long n, uint8_t* out) {
 
 void oracle_e4m3_decode_array(const uint8_t* c, long n, double* out) {
     for (long i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+
+/* ------------------------------------------------------------ binary16 codec */
+
+/* IEEE 754 binary16: sign, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent 0 is subnormal (m * 2^-24); exponent 31 is infinity (m = 0) or NaN. */
+double oracle_f16_decode(uint16_t code) {
+    int s = code >> 15, e = (code >> 10) & 31, m = code & 1023;
+    double v;
+    if (e == 31) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -24);
+    else v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even to binary16, saturating at +-65504 (no infinities
+ * from finite inputs). */
+uint16_t oracle_f16_encode(double x) {
+    uint16_t s = signbit(x) ? 0x8000 : 0x0000;
+    double a = fabs(x);
+    if (isnan(x)) return (uint16_t)(s | 0x7E00);
+    if (a >= 65504.0) return (uint16_t)(s | 0x7BFF);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: multiples of 2^-24; a result of 1024 is the
+         * smallest normal, whose code is also 1024 */
+        return (uint16_t)(s | (uint16_t)rint(ldexp(a, 24)));
+    }
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;                        /* a in [2^e, 2^(e+1)) */
+    double r = rint(ldexp(a, 10 - e));     /* 10 fraction bits: r in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        e += 1;
+    }
+    return (uint16_t)(s | (uint16_t)(((e + 15) << 10) | ((int)r - 1024)));
+}
+
+void oracle_f16_encode_array(const double* x, long n, uint16_t* out) {
+    for (long i = 0; i < n; ++i) out[i] = oracle_f16_encode(x[i]);
+}
+
+void oracle_f16_decode_array(const uint16_t* c, long n, double* out) {
+    for (long i = 0; i < n; ++i) out[i] = oracle_f16_decode(c[i]);
 }
 
 /* ------------------------------------------------------------ quantisation */
@@ -210,6 +262,10 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  *            O[c] = sum_t w_t A_t[c],  l = sum_t w_t R_t
  *   out[c] = O[c] * sv[c] / l
  *
+ * pv_f16 = 1 selects the binary16 P.V mode: v_codes holds binary16 codes of V
+ * (uint16), v_scale may be NULL (sv = 1), f32(log2 448) above is replaced by 0
+ * and P16_j = f16(y_j) replaces P8_j; the rest is unchanged.
+ *
  * out_lo/out_hi (optional) bound the output over every choice of the P8 codes
  * whose y lies within relative distance tau of a rounding midpoint: changing
  * code j by delta moves out[c] by w delta (V8[j,c] sv[c] - out[c]) / (l + w
@@ -218,7 +274,7 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  * receives the number of such codes per row.
  */
 void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                   const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                   const float* k_scale, const void* v_codes, const float* v_scale, int pv_f16,
                    int B, int Hq, int Hkv, int N, int d, int bq, int bk, int bn, int causal,
                    float sm_scale, double tau, const int64_t* rows, long nrows,
                    double* out, double* out_lo, double* out_hi, int64_t* flagged) {
@@ -226,10 +282,18 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
     const int G = Hq / Hkv;
     const int nqb = (N + bq - 1) / bq, nkb = (N + bk - 1) / bk;
     const float qk = (float)((double)sm_scale * 1.4426950408889634); /* log2(e) */
-    const float l448 = (float)log2(448.0);
+    /* the P block scale: the block maximum maps to 448 (E4M3) or to 1 (binary16) */
+    const float l448 = pv_f16 ? 0.0f : (float)log2(448.0);
     const float seed = 12582912.0f; /* 1.5 * 2^23 */
-    double dec[256];
-    for (int i = 0; i < 256; ++i) dec[i] = oracle_e4m3_decode((uint8_t)i);
+    /* decoded value of every code of the P.V format, and its largest finite
+     * positive code */
+    const int ncode = pv_f16 ? 65536 : 256;
+    const int top = pv_f16 ? 0x7BFF : 0x7E;
+    double* dec = (double*)malloc(sizeof(double) * (size_t)ncode);
+    for (int i = 0; i < ncode; ++i)
+        dec[i] = pv_f16 ? oracle_f16_decode((uint16_t)i) : oracle_e4m3_decode((uint8_t)i);
+    const uint8_t* v8 = (const uint8_t*)v_codes;
+    const uint16_t* v16 = (const uint16_t*)v_codes;
     if (rows == NULL) nrows = (long)B * Hq * N;
 
 #pragma omp parallel
@@ -252,8 +316,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
             int g = h / G;
             const int8_t* qrow = q_i8 + bh * nd + (long)i * d;
             const int8_t* kh = k_i8 + ((long)b * Hkv + g) * nd;
-            const uint8_t* vh = v_fp8 + ((long)b * Hkv + g) * nd;
-            const float* svh = v_scale + ((long)b * Hkv + g) * d;
+            const long vhead = ((long)b * Hkv + g) * nd;
+            const float* svh = v_scale ? v_scale + ((long)b * Hkv + g) * d : NULL;
             const float sq = q_scale[bh * nqb + i / bq];
             const float* skh = k_scale + ((long)b * Hkv + g) * nkb;
             int jmax = causal ? i : N - 1;
@@ -295,16 +359,19 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 for (int j = j0; j <= j1; ++j) {
                     float x = fmaf(Fj[j], cj[j], bias - uj[j]);
                     double y = exp2((double)x);
-                    uint8_t code = oracle_e4m3_encode(y);
+                    int code = pv_f16 ? (int)oracle_f16_encode(y) : (int)oracle_e4m3_encode(y);
                     double p = dec[code];
                     R += p;
-                    const uint8_t* vr = vh + (long)j * d;
-                    for (int c = 0; c < d; ++c) A[c] += p * dec[vr[c]];
+                    const long vr = vhead + (long)j * d;
+                    if (pv_f16)
+                        for (int c = 0; c < d; ++c) A[c] += p * dec[v16[vr + c]];
+                    else
+                        for (int c = 0; c < d; ++c) A[c] += p * dec[v8[vr + c]];
                     if (out_lo || flagged) {
                         /* the other code is also correct when y sits within
                          * tau of the midpoint to a neighbouring code */
                         double alt = p;
-                        if (code < 0x7E) {
+                        if (code < top) {
                             double up = dec[code + 1], mid = 0.5 * (p + up);
                             if (fabs(y - mid) <= tau * mid) alt = up;
                         }
@@ -322,14 +389,15 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 for (int c = 0; c < d; ++c) O[c] += w * A[c];
                 l += w * R;
             }
-            for (int c = 0; c < d; ++c) out[ri * d + c] = O[c] * (double)svh[c] / l;
+            for (int c = 0; c < d; ++c) out[ri * d + c] = O[c] * (svh ? (double)svh[c] : 1.0) / l;
             if (out_lo) {
                 double inter = 0.0;
                 for (int64_t e = 0; e < nflag; ++e) inter += fabs(fwd[e]) / l;
                 for (int c = 0; c < d; ++c) {
                     double o = out[ri * d + c], neg = 0.0, pos = 0.0;
                     for (int64_t e = 0; e < nflag; ++e) {
-                        double vjc = dec[vh[(long)fj[e] * d + c]] * (double)svh[c];
+                        const long vi = vhead + (long)fj[e] * d + c;
+                        double vjc = (pv_f16 ? dec[v16[vi]] : dec[v8[vi]]) * (svh ? (double)svh[c] : 1.0);
                         double mv = fwd[e] * (vjc - o) / (l + fwd[e]);
                         if (mv < 0) neg += mv;
                         else pos += mv;
@@ -351,6 +419,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
         free(fj);
         free(fwd);
     }
+    free(dec);
 }
 
 /* ------------------------------------------- full-precision attention */

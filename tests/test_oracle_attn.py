@@ -55,19 +55,23 @@ def _deq_inputs(orc, z):
     sk = np.repeat(z["k_scale"].astype(np.float64), z["bk"], axis=-1)[..., :N, None]
     qd = z["q_i8"].astype(np.float64) * sq
     kd = z["k_i8"].astype(np.float64) * sk
-    vd = orc.e4m3_decode(z["v_fp8"]) * z["v_scale"].astype(np.float64)[:, :, None, :]
+    if z["pv"] == "f16":
+        vd = z["v_f16"].view(np.float16).astype(np.float64)
+    else:
+        vd = orc.e4m3_decode(z["v_fp8"]) * z["v_scale"].astype(np.float64)[:, :, None, :]
     return qd, kd, vd
 
 
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_zero_q_gives_mean_of_dequantized_v(orc, causal):
-    """Q = 0: every score is 0, every P code is 448 and the output is the
-    (prefix) mean of the dequantized V rows, exactly (the quantized weights
-    are normalised by their own sum)."""
+def test_zero_q_gives_mean_of_dequantized_v(orc, causal, pv):
+    """Q = 0: every score is 0, every P code is the block maximum's (448, or 1
+    in binary16) and the output is the (prefix) mean of the dequantized V
+    rows, exactly (the quantized weights are normalised by their own sum)."""
     N, d = 300, 64
     _, k, v = workloads.random_inputs(1, 2, 2, N, d, "f16", seed=5)
     q = torch.zeros(1, 2, N, d, dtype=torch.float16)
-    z = orc.quantize(q, k, v)
+    z = orc.quantize(q, k, v, pv=pv)
     out, lo, hi, fl = orc.attn_q(z, causal, 0.125)
     _, _, vd = _deq_inputs(orc, z)
     vd = vd.reshape(2, N, d)
@@ -79,9 +83,11 @@ def test_zero_q_gives_mean_of_dequantized_v(orc, causal):
     assert fl.sum() == 0
 
 
-def test_one_dominant_key_gives_its_value(orc):
-    """A key whose score exceeds every other by > 30 nats: every other P code
-    is 0, so the output is exactly its dequantized V row."""
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
+def test_one_dominant_key_gives_its_value(orc, pv):
+    """A key whose score exceeds every other by > 30 nats (> 43 in log2, past
+    binary16's smallest subnormal 2^-24): every other P code is 0, so the
+    output is exactly its dequantized V row."""
     N, d = 256, 64
     rng = np.random.Generator(np.random.PCG64(9))
     q = torch.ones(1, 1, N, d, dtype=torch.float16)
@@ -89,15 +95,17 @@ def test_one_dominant_key_gives_its_value(orc):
     jstar = 77
     k[0, 0, jstar] = 10.0
     v = torch.from_numpy(rng.normal(0, 1, (1, 1, N, d)).astype(np.float32)).half()
-    z = orc.quantize(q, k, v)
+    z = orc.quantize(q, k, v, pv=pv)
     out, _, _, _ = orc.attn_q(z, False, 0.125)
     _, _, vd = _deq_inputs(orc, z)
     np.testing.assert_allclose(out, np.broadcast_to(vd[0, 0, jstar], out.shape), rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_blockwise_constant_keys_give_weighted_block_means(orc, causal):
-    """Keys equal within every 128-key P block: every P code of a block is 448,
+def test_blockwise_constant_keys_give_weighted_block_means(orc, causal, pv):
+    """Keys equal within every 128-key P block: every P code of a block is the
+    block maximum's (448, or 1 in binary16),
     so the output is the softmax over blocks (weights n_t * e^{S_t}) of the
     per-block V means -- checks the second accumulation level and the row
     normalisation against the dequantized scores in float64."""
@@ -108,7 +116,7 @@ def test_blockwise_constant_keys_give_weighted_block_means(orc, causal):
     k = torch.from_numpy(np.repeat(kblk, bn, axis=0)[:N][None, None]).half()
     q = torch.from_numpy(rng.normal(0, 1, (1, 1, N, d)).astype(np.float32)).half()
     v = torch.from_numpy(rng.normal(0, 1, (1, 1, N, d)).astype(np.float32)).half()
-    z = orc.quantize(q, k, v, bk=128)
+    z = orc.quantize(q, k, v, bk=128, pv=pv)
     out, _, _, fl = orc.attn_q(z, causal, 0.125, bn=bn)
     qd, kd, vd = _deq_inputs(orc, z)
     ref = orc.attn_f64(qd, kd, vd, causal, 0.125)
@@ -146,11 +154,26 @@ def _fma_f32(a, b, c) -> np.float32:
 
 
 def _online_reference(orc, z, causal, sm_scale, bn):
+    """P.V in E4M3 (codes through torch's float8_e4m3fn) or in binary16 (codes
+    through numpy's float16), never through the oracle's own encoders."""
     B, Hq, Hkv, N, d = z["B"], z["Hq"], z["Hkv"], z["N"], z["d"]
     G = Hq // Hkv
+    f16 = z["pv"] == "f16"
     qk = np.float32(sm_scale * math.log2(math.e))
-    l448 = np.float32(math.log2(448.0))
-    vals = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    l448 = np.float32(0.0) if f16 else np.float32(math.log2(448.0))
+    if f16:
+        vrow = z["v_f16"].view(np.float16).astype(np.float64)
+        vscale = np.ones((B, Hkv, d))
+
+        def p_code(y):
+            return float(np.float16(y))
+    else:
+        vrow = torch.from_numpy(z["v_fp8"]).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        vscale = z["v_scale"].astype(np.float64)
+
+        def p_code(y):
+            return torch.tensor([y], dtype=torch.float64).to(torch.float8_e4m3fn).to(
+                torch.float64).item()
     out = np.zeros((B * Hq * N, d))
     for b in range(B):
         for h in range(Hq):
@@ -179,8 +202,8 @@ def _online_reference(orc, z, causal, sm_scale, bn):
                     for j, F, c, u in zip(blk, Fs, cs, us):
                         bias = np.float32(np.float32(l448 - mt) - u)
                         y = 2.0 ** float(_fma_f32(F, c, bias))
-                        p = vals[orc.e4m3_encode(np.array([y]))[0]]
-                        a_blk += p * vals[z["v_fp8"][b, g, j]]
+                        p = p_code(y)
+                        a_blk += p * vrow[b, g, j]
                         r_blk += p
                     m_new = max(m_run, float(mt))
                     alpha = 2.0 ** (m_run - m_new) if m_run > -math.inf else 0.0
@@ -188,19 +211,20 @@ def _online_reference(orc, z, causal, sm_scale, bn):
                     o_run = alpha * o_run + wgt * a_blk
                     l_run = alpha * l_run + wgt * r_blk
                     m_run = m_new
-                out[(b * Hq + h) * N + i] = o_run * z["v_scale"][b, g].astype(np.float64) / l_run
+                out[(b * Hq + h) * N + i] = o_run * vscale[b, g] / l_run
     return out
 
 
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
 @pytest.mark.parametrize("N", [1, 2, 3, 5, 16])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d,G", [(64, 1), (128, 4)])
-def test_closed_form_equals_online_recurrence_tiny(orc, N, causal, d, G):
+def test_closed_form_equals_online_recurrence_tiny(orc, N, causal, d, G, pv):
     """The oracle's closed form over P blocks equals the online recurrence
     (running max, rescaled accumulator) with small blocks so several blocks and
     ragged tails occur (bq=4, bk=2, bn=4)."""
     q, k, v = workloads.random_inputs(1, G, 1, N, d, "bf16", seed=100 + N + d, scale=1.5)
-    z = orc.quantize(q, k, v, bq=4, bk=2)
+    z = orc.quantize(q, k, v, bq=4, bk=2, pv=pv)
     out, lo, hi, fl = orc.attn_q(z, causal, 1 / math.sqrt(d), bn=4)
     ref = _online_reference(orc, z, causal, 1 / math.sqrt(d), bn=4)
     ok = fl == 0
@@ -231,6 +255,50 @@ def test_quantized_attention_within_p_rounding_of_dequantized_reference(orc, rec
     acc = orc.accuracy(out, ref)
     assert acc["rel_l1"] < 0.04 and acc["cos"] > 0.999
     assert np.all(lo <= out) and np.all(out <= hi)
+
+
+@pytest.mark.parametrize("recipe", [1, 2, 3, 4, 5])
+def test_f16_pv_within_p_rounding_of_dequantized_reference(orc, recipe):
+    """The binary16 P.V mode against float64 attention on the dequantized Q,
+    K-smoothed and binary16 V.  Two errors remain: P16_j = y_j (1 + e_j) with
+    |e_j| <= 2^-11 for y_j >= 2^-14 and |P16_j - y_j| <= 2^-25 below; and the
+    float32 evaluation of the exponent, whose constant offset u = f32(1.5 2^23
+    c) and bias are rounded, which moves each log2 weight by at most ~3
+    ulp(u).  Each weight is thus off by a factor within 1 +- r,
+    r = (1 + 2^-11) 2^(3 ulp(u)) - 1, and (the row sum being at least 1, the
+    code of the row maximum) the output is within
+    2 max|V| (r / (1 - r) + n 2^-25) of the exact weighted mean."""
+    w0 = workloads.WORKLOADS[recipe]
+    w = w0.resized(B=1, Hq=w0.Hq // w0.Hkv * 2, Hkv=2, N=700)
+    q, k, v = workloads.generate(w, seed=recipe)
+    z = orc.quantize(q, k, v, pv="f16")
+    rows = workloads.sample_rows(w, 200)
+    out, lo, hi, _ = orc.attn_q(z, w.causal, w.sm_scale, rows=rows)
+    qd, kd, vd = _deq_inputs(orc, z)
+    ref = orc.attn_f64(qd, kd, vd, w.causal, w.sm_scale, rows=rows)
+    vmax = np.abs(vd).max()
+    c_max = float(z["q_scale"].max()) * float(z["k_scale"].max()) * w.sm_scale * math.log2(math.e)
+    ulp_u = 2.0 ** (math.floor(math.log2(12582912 * c_max)) - 23)
+    r = (1 + 2.0 ** -11) * 2.0 ** (3 * ulp_u) - 1
+    bound = 2 * vmax * (r / (1 - r) + w.N * 2.0 ** -25)
+    assert np.abs(out - ref).max() <= bound
+    assert np.all(lo <= out) and np.all(out <= hi)
+
+
+@pytest.mark.parametrize("recipe", [3, 5])
+def test_f16_pv_is_closer_to_full_precision_than_e4m3(orc, recipe):
+    """The SageAttention2 summary ranks E4M3 as nearly as accurate as FP16
+    for P and V: the binary16 mode's error against float64 attention on the
+    original inputs is the smaller one, and what remains is the INT8 Q.K^T."""
+    w0 = workloads.WORKLOADS[recipe]
+    w = w0.resized(B=1, Hq=w0.Hq // w0.Hkv * 2, Hkv=2, N=700)
+    q, k, v = workloads.generate(w, seed=recipe)
+    rows = workloads.sample_rows(w, 200)
+    ref = orc.attn_f64(q, k, v, w.causal, w.sm_scale, rows=rows)
+    e8 = orc.accuracy(orc.attn_q(orc.quantize(q, k, v), w.causal, w.sm_scale, rows=rows)[0], ref)
+    e16 = orc.accuracy(orc.attn_q(orc.quantize(q, k, v, pv="f16"), w.causal, w.sm_scale,
+                                  rows=rows)[0], ref)
+    assert e16["rel_l1"] < e8["rel_l1"] and e16["cos"] > e8["cos"]
 
 
 def test_smoothing_helps_when_k_has_channel_outliers(orc):

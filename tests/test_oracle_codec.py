@@ -1,7 +1,8 @@
 """Pins of the oracle's prep step (K smoothing, per-block INT8, per-channel
-E4M3) against facts that do not come from the oracle itself: an independent
-FP8 implementation (torch.float8_e4m3fn), numpy's rounding and mean, and the
-defining error bounds of round-to-nearest quantisation."""
+E4M3, binary16 V) against facts that do not come from the oracle itself:
+independent FP8 and binary16 implementations (torch.float8_e4m3fn, numpy's
+float16), numpy's rounding and mean, and the defining error bounds of
+round-to-nearest quantisation."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +54,65 @@ def test_e4m3_encode_hand_values(orc, x, code):
     """Round-half-even ties, saturation at 448 and signed zero, worked by hand
     from the E4M3FN definition (bias 7, three mantissa bits)."""
     assert int(orc.e4m3_encode(np.array([x]))[0]) == code
+
+
+# ---------------------------------------------------------------- binary16
+
+def test_f16_decode_every_code_matches_numpy(orc):
+    codes = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    mine = orc.f16_decode(codes)
+    ref = codes.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.isnan(mine[nan]).all()
+    np.testing.assert_array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7BFF] == 65504.0 and mine[0x0001] == 2.0 ** -24 and mine[0x0400] == 2.0 ** -14
+
+
+def test_f16_encode_matches_numpy_on_every_midpoint(orc):
+    """Every finite binary16 value, every midpoint between neighbours and the
+    next float64 either side of it, both signs: numpy's float64 -> float16
+    conversion rounds to nearest even in one step."""
+    vals = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = 0.5 * (vals[1:] + vals[:-1])
+    pts = np.concatenate([vals, mids, np.nextafter(mids, np.inf), np.nextafter(mids, 0.0)])
+    pts = np.concatenate([pts, -pts])
+    pts = pts[np.abs(pts) < 65504.0]  # numpy overflows to inf at the 65504/65536 tie
+    np.testing.assert_array_equal(orc.f16_encode(pts), pts.astype(np.float16).view(np.uint16))
+
+
+def test_f16_encode_matches_numpy_on_random_doubles(orc):
+    rng = np.random.Generator(np.random.PCG64(3))
+    x = np.ldexp(rng.uniform(1.0, 2.0, 200000), rng.integers(-30, 16, 200000))
+    x *= rng.choice([-1.0, 1.0], x.size)
+    x = x[np.abs(x) < 65504.0]
+    np.testing.assert_array_equal(orc.f16_encode(x), x.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("x,code", [
+    (65504.0, 0x7BFF), (65519.0, 0x7BFF), (65520.0, 0x7BFF), (1e30, 0x7BFF), (-1e30, 0xFBFF),
+    (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000), (1.5 * 2.0 ** -25, 0x0001), (3 * 2.0 ** -25, 0x0002),
+    (1.0 + 2.0 ** -11, 0x3C00), (1.0 + 3 * 2.0 ** -11, 0x3C02), (0.0, 0x0000), (-0.0, 0x8000),
+    (1.0, 0x3C00), (0.5, 0x3800)])
+def test_f16_encode_hand_values(orc, x, code):
+    """Ties to even, signed zero, the subnormal step 2^-24 and saturation at
+    65504 (where IEEE rounding would give infinity from 65520 up), worked by
+    hand from the binary16 definition (bias 15, ten fraction bits)."""
+    assert int(orc.f16_encode(np.array([x]))[0]) == code
+
+
+def test_quantize_f16_mode_keeps_v_as_its_binary16_rounding(orc):
+    """pv="f16": V's codes are its binary16 rounding (exact for fp16 inputs),
+    the INT8 Q and K parts are those of the E4M3 mode."""
+    q, k, v = workloads.random_inputs(1, 2, 2, 300, 64, "f16", seed=8)
+    z8 = orc.quantize(q, k, v)
+    z16 = orc.quantize(q, k, v, pv="f16")
+    np.testing.assert_array_equal(z16["v_f16"], v.numpy().view(np.uint16))
+    for key in ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean"):
+        np.testing.assert_array_equal(z16[key], z8[key])
+    _, _, vb = workloads.random_inputs(1, 2, 2, 300, 64, "bf16", seed=8)
+    zb = orc.quantize(q, k, vb, pv="f16")
+    np.testing.assert_array_equal(zb["v_f16"],
+                                  vb.to(torch.float32).numpy().astype(np.float16).view(np.uint16))
 
 
 def _deq(codes, scale, blk, n):
