@@ -6,6 +6,7 @@ already resident in HBM: the prep kernels (K mean, smoothing, INT8 Q/K, FP8 V)
 followed by the fused attention kernel, i.e. one sage_attn_fwd call.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu]
+                    [--granularity block|thread] [--pv e4m3|f16]
 
 Prints one JSON line.  `value` is TOPS = 4*B*Hq*N^2*d / t (halved for causal)
 for the whole step; `roofline` prices the attention kernel alone (its average
@@ -38,6 +39,8 @@ def parse():
                    help="1..5; 3 is the non-causal N=17550 video-diffusion shape")
     p.add_argument("--granularity", choices=("block", "thread"), default="block",
                    help="Q/K scale granularity: block (128 rows / 64 keys) or thread (per row / 32 keys)")
+    p.add_argument("--pv", choices=("e4m3", "f16"), default="e4m3",
+                   help="P.V format: e4m3 (FP8 P and V, the default) or f16 (binary16 P and V)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
     p.add_argument("--contrast", action="store_true",
@@ -52,9 +55,11 @@ def parse():
     return p.parse_args()
 
 
-def measured_traffic(kernel_source):
-    """HBM bytes per attention launch from the committed byte-counter summary,
-    or None when the kernel source changed since the counters were taken."""
+def measured_traffic(kernel_source, granularity, pv):
+    """(workload, HBM bytes per attention launch) from the committed
+    byte-counter summary taken with this granularity and P.V format, or
+    (None, None) when the kernel source changed since the counters were
+    taken."""
     import glob
     import hashlib
     src = open(kernel_source, "rb").read()
@@ -62,7 +67,8 @@ def measured_traffic(kernel_source):
     for path in glob.glob(os.path.join(ROOT, "profiles", "attn_fwd_*_counters.json")):
         with open(path) as f:
             d = json.load(f)
-        if d.get("kernel_source_sha256") == digest:
+        if (d.get("kernel_source_sha256") == digest and d.get("granularity", "block") == granularity
+                and d.get("pv_format", "e4m3") == pv):
             return d.get("workload"), d.get("traffic_bytes_per_launch")
     return None, None
 
@@ -117,7 +123,7 @@ def prep_flushed(sage, qd, kd, vd, z, steps, torch):
     return times[len(times) // 2]
 
 
-def cpu_baseline(w, q, k, v, rows_wanted, bq, bk):
+def cpu_baseline(w, q, k, v, rows_wanted, bq, bk, pv):
     """The oracle as it stands: its prep over the whole input, pro-rated to the
     sampled rows, plus its attention over the sampled rows."""
     import numpy as np
@@ -127,7 +133,7 @@ def cpu_baseline(w, q, k, v, rows_wanted, bq, bk):
 
     oracle.build()
     t0 = time.perf_counter()
-    oz = oracle.quantize(q, k, v, bq=bq, bk=bk)
+    oz = oracle.quantize(q, k, v, bq=bq, bk=bk, pv=pv)
     t_prep = time.perf_counter() - t0
     total_rows = w.B * w.Hq * w.N
     if rows_wanted <= 0:
@@ -176,11 +182,12 @@ def main():
     out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
     ws = sage.workspace_for(qd, kd)
     z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d,
-                                  granularity=args.granularity)
-    qb, kb = sage.GRANULARITY[args.granularity]
+                                  granularity=args.granularity, pv=args.pv)
+    opts = sage.options(args.granularity, args.pv)
+    qb, kb = opts.q_block, opts.k_block
 
     def step():
-        sage.sage_attn_fwd_granular(qd, kd, vd, out, w.causal, w.sm_scale, qb, kb, ws)
+        sage.sage_attn_fwd_ex(qd, kd, vd, out, w.causal, w.sm_scale, opts, ws)
 
     for _ in range(args.warmup):
         step()
@@ -194,7 +201,8 @@ def main():
     ms_attn = timed(lambda: sage.sage_attn_fwd_quantized(z, out, w.B, w.Hq, w.Hkv, w.N, w.d,
                                                          w.causal, w.sm_scale), args.steps, torch)
     traffic_wl, traffic = measured_traffic(
-        os.path.join(ROOT, "bit_quantized_attention_02_amd", "csrc", "attn_fwd.hip"))
+        os.path.join(ROOT, "bit_quantized_attention_02_amd", "csrc", "attn_fwd.hip"), args.granularity,
+        args.pv)
     if traffic_wl != w.name:
         traffic = None
     tops = w.ops / (ms_step * 1e-3) / 1e12
@@ -206,10 +214,10 @@ def main():
         "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 (QK^T, i32 acc) + e4m3 values (P.V, f32 acc)", "data": "synthetic",
+        "dtype": f"i8 (QK^T, i32 acc) + {args.pv} values (P.V, f32 acc)", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "input_dtype": w.dtype, "sm_scale": w.sm_scale,
-                   "q_block": qb, "k_block": kb, "parallelism": "single GPU"},
+                   "q_block": qb, "k_block": kb, "pv_format": args.pv, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd", "ms_per_launch": round(ms_attn, 4)},
@@ -224,7 +232,7 @@ def main():
     if args.contrast:
         line["contrast"] = contrast_sdpa(w, qd, kd, vd, args.steps, torch)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, qb, kb)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, qb, kb, args.pv)
     print(json.dumps(line), flush=True)
 
 

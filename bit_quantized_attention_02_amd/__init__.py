@@ -26,8 +26,11 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ER
 SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_BQ, SAGE_BK, SAGE_BN, SAGE_NPAD = 128, 64, 128, 256
 SAGE_BQ_THREAD, SAGE_BK_THREAD = 1, 32
+SAGE_PV_E4M3, SAGE_PV_F16 = 0, 1
 # (q_block, k_block) of the two quantization granularities
 GRANULARITY = {"block": (SAGE_BQ, SAGE_BK), "thread": (SAGE_BQ_THREAD, SAGE_BK_THREAD)}
+# P.V formats: FP8 E4M3 P and V, or binary16 P and V (both accumulated in FP32)
+PV_FORMAT = {"e4m3": SAGE_PV_E4M3, "f16": SAGE_PV_F16}
 
 
 class sage_config(ctypes.Structure):
@@ -37,8 +40,13 @@ class sage_config(ctypes.Structure):
 
 class sage_qkv_quant(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_e4m3", "v_scale", "v_inv",
-                 "k_part", "v_part", "sync")] + [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32)]
+                ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v16", "v_scale", "v_inv",
+                 "k_part", "v_part", "sync")] + [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32),
+                                                 ("pv_format", ctypes.c_int32)]
+
+
+class sage_options(ctypes.Structure):
+    _fields_ = [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32), ("pv_format", ctypes.c_int32)]
 
 
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -51,13 +59,16 @@ _lib.sage_attn_fwd_quantized.argtypes = [ctypes.POINTER(sage_qkv_quant), _P, _I,
 _lib.sage_attn_fwd.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]
 _lib.sage_attn_fwd_granular.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P,
                                         _S, _P]
+_lib.sage_attn_fwd_ex.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                  ctypes.POINTER(sage_options), _P, _S, _P]
 _lib.sage_get_config.argtypes = [ctypes.POINTER(sage_config)]
 _lib.sage_v_key_position.argtypes = [_I]
 _lib.sage_status_string.restype = ctypes.c_char_p
 _lib.sage_status_string.argtypes = [_I]
 
 EXPORTED = ["sage_workspace_bytes", "sage_workspace_carve", "sage_quantize",
-            "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_attn_fwd_granular", "sage_get_config",
+            "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_attn_fwd_granular", "sage_attn_fwd_ex",
+            "sage_get_config",
             "sage_v_key_position", "sage_status_string"]
 
 
@@ -116,12 +127,15 @@ def sage_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
 
 
 def sage_workspace_carve(workspace: torch.Tensor | int | None, ws_bytes: int, B: int, Hq: int,
-                         Hkv: int, N: int, d: int, granularity: str = "block") -> sage_qkv_quant:
-    """The C call, then (q_block, k_block) set to the chosen granularity."""
+                         Hkv: int, N: int, d: int, granularity: str = "block",
+                         pv: str = "e4m3") -> sage_qkv_quant:
+    """The C call, then (q_block, k_block) and pv_format set to the chosen
+    granularity and P.V format."""
     z = sage_qkv_quant()
     ptr = workspace.data_ptr() if isinstance(workspace, torch.Tensor) else workspace
     _check(_lib.sage_workspace_carve(ptr, ws_bytes, B, Hq, Hkv, N, d, ctypes.byref(z)))
     z.q_block, z.k_block = GRANULARITY[granularity]
+    z.pv_format = PV_FORMAT[pv]
     return z
 
 
@@ -156,7 +170,22 @@ def sage_attn_fwd_granular(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ou
                                        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def sage_attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                     causal: bool, sm_scale: float, opts: sage_options, workspace: torch.Tensor,
+                     stream=None) -> None:
+    B, Hq, Hkv, N, d = _shape(q, k)
+    _check(_lib.sage_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, int(causal),
+                                 float(sm_scale), _dtype_code(q), ctypes.byref(opts), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 # ------------------------------------------------------------------ helpers
+
+def options(granularity: str = "block", pv: str = "e4m3") -> sage_options:
+    """sage_options from the names of a granularity and a P.V format."""
+    qb, kb = GRANULARITY[granularity]
+    return sage_options(qb, kb, PV_FORMAT[pv])
+
 
 def workspace_for(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
     """Allocate a workspace (torch-owned device bytes) for these shapes."""
@@ -169,11 +198,11 @@ def workspace_for(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
 
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
          sm_scale: float | None = None, workspace: torch.Tensor | None = None,
-         granularity: str = "block") -> torch.Tensor:
+         granularity: str = "block", pv: str = "e4m3") -> torch.Tensor:
     """Drop-in attention: [B,Hq,N,d] fp16/bf16 Q and [B,Hkv,N,d] K,V on the GPU
     -> FP32 [B,Hq,N,d], on the current stream.  granularity: "block" (one Q
     scale per 128 rows, one K scale per 64 keys) or "thread" (per row, per 32
-    keys)."""
+    keys); pv: "e4m3" (FP8 P and V) or "f16" (binary16 P and V)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     for t in (q, k, v):
@@ -182,17 +211,18 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = workspace_for(q, k)
-    qb, kb = GRANULARITY[granularity]
-    sage_attn_fwd_granular(q, k, v, out, causal, sm_scale, qb, kb, workspace)
+    sage_attn_fwd_ex(q, k, v, out, causal, sm_scale, options(granularity, pv), workspace)
     return out
 
 
 def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, Hkv: int,
                    N: int, d: int) -> dict:
     """Copy the quantized operands out of `workspace` (carved into `z`) to host
-    tensors in the plain [B,H,N,d] layout, the V block permutation undone and
-    V given back as E4M3 codes (the workspace holds their binary16 values,
-    which convert back exactly).  Layout only; `*_pad` hold rows N..N_p-1."""
+    tensors in the plain [B,H,N,d] layout, the V block permutation undone.  V
+    comes back as its binary16 values (v_half) and as codes: E4M3 codes
+    (v_fp8; the binary16 values convert back exactly) or, for the binary16
+    P.V format, the binary16 bit patterns (v_f16).  Layout only; `*_pad` hold
+    rows N..N_p-1."""
     Np = -(-N // SAGE_NPAD) * SAGE_NPAD
     base = workspace.data_ptr()
     torch.cuda.synchronize()
@@ -207,13 +237,16 @@ def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, 
 
     q_full = host(z.q_i8, (B, Hq, Np, d), torch.int8)
     k_full = host(z.k_i8, (B, Hkv, Np, d), torch.int8)
-    vb = host(z.v_e4m3, (B, Hkv, Np // SAGE_BN, d, SAGE_BN), torch.float16)
+    vb = host(z.v16, (B, Hkv, Np // SAGE_BN, d, SAGE_BN), torch.float16)
     perm = torch.tensor([sage_v_key_position(j) for j in range(SAGE_BN)], dtype=torch.long)
     v_half = vb[..., perm].permute(0, 1, 2, 4, 3).reshape(B, Hkv, Np, d)
-    v_full = v_half.to(torch.float8_e4m3fn).view(torch.uint8)
+    if z.pv_format == SAGE_PV_F16:
+        v_codes = dict(v_f16=v_half.view(torch.int16)[:, :, :N].contiguous())
+    else:
+        v_codes = dict(v_fp8=v_half.to(torch.float8_e4m3fn).view(torch.uint8)[:, :, :N].contiguous())
     return dict(
-        q_i8=q_full[:, :, :N].contiguous(), k_i8=k_full[:, :, :N].contiguous(),
-        v_fp8=v_full[:, :, :N].contiguous(), v_half=v_half[:, :, :N].contiguous(),
+        **v_codes, q_i8=q_full[:, :, :N].contiguous(), k_i8=k_full[:, :, :N].contiguous(),
+        v_half=v_half[:, :, :N].contiguous(),
         q_pad=q_full[:, :, N:].contiguous(), k_pad=k_full[:, :, N:].contiguous(),
         v_pad=v_half[:, :, N:].contiguous(),
         q_scale=host(z.q_scale, (B, Hq, Np // z.q_block), torch.float32),

@@ -27,6 +27,10 @@
 //      time and each piece goes to the matrix core at once, so the
 //      conversions of one piece run while the products of the previous one
 //      are in flight.
+// The binary16 P.V variant (the SageAttention article's own P.V, with FP32
+// accumulation) differs only in step 3: P16 = f16(2^(acc*c - m)), one
+// rounding instead of the E4M3 round trip, and V holds V's binary16 rounding
+// with scale 1.
 // The reference max is raised lazily, only when a block's maximum exceeds it
 // by more than 8 (log2 units), so O is rescaled rarely.
 // The P operand a lane feeds to P.V is exactly the scores it computed, so
@@ -40,6 +44,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 static_assert(SAGE_BQ == 128 && SAGE_BQ_THREAD == 1 && SAGE_BK == 64 && SAGE_BK_THREAD == 32,
               "the launch maps the two granularities to q_shift 7/0 and 2/4 K scales per block");
@@ -53,13 +59,13 @@ struct AttnArgs {
     const float* q_scale;
     const int8_t* k_i8;
     const float* k_scale;
-    const uint16_t* v_e4m3;
+    const uint16_t* v16;
     const float* v_scale;
     float* out;
     int B, Hq, Hkv, N, Np, G, nqt;
     int q_shift;  // log2 of the query rows per Q scale (7 or 0)
     float qk;    // f32(sm_scale * log2 e)
-    float l448;  // f32(log2 448)
+    float l448;  // f32(log2 448), or 0 for binary16 P
 };
 
 // XOR swizzle of the 16-byte chunks of one K-tile row (d bytes long): the 16
@@ -140,11 +146,12 @@ __device__ inline int max_across_halves(int x) {
 }
 
 // One key block for one wave (32 query rows).  MASKED: some keys of the
-// block are excluded (causal diagonal, or keys >= N).
+// block are excluded (causal diagonal, or keys >= N).  PV16: P is rounded to
+// binary16 directly (l448 is then 0) instead of through E4M3.
 // KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
 // 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
 // log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
-template <int D, int KSPLIT, bool CAUSAL, bool MASKED>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED>
 __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const uint16_t* __restrict__ lv,
                                            const v4i (&qf)[D / 32], int T, int row, int N,
@@ -253,17 +260,24 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                         y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[v], ct, bt));
                         if (MASKED && S[t][v] == INT32_MIN) y[i] = 0.0f;
                     }
-                    // the first conversion writes the low half; the high half
-                    // of its destination is then written by the second, so the
-                    // register's old contents never matter (the builtin would
-                    // zero it first)
-                    int code;
-                    asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(code) : "v"(y[0]), "v"(y[1]));
-                    code = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], code, true);
-                    quad[2 * g] =
-                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false));
-                    quad[2 * g + 1] =
-                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
+                    if (PV16) {
+                        // round to nearest even, two values per conversion
+                        const v2f lo = {y[0], y[1]}, hi = {y[2], y[3]};
+                        quad[2 * g] = __builtin_bit_cast(int, __builtin_convertvector(lo, v2h));
+                        quad[2 * g + 1] = __builtin_bit_cast(int, __builtin_convertvector(hi, v2h));
+                    } else {
+                        // the first conversion writes the low half; the high
+                        // half of its destination is then written by the
+                        // second, so the register's old contents never matter
+                        // (the builtin would zero it first)
+                        int code;
+                        asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(code) : "v"(y[0]), "v"(y[1]));
+                        code = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], code, true);
+                        quad[2 * g] = __builtin_bit_cast(
+                            int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false));
+                        quad[2 * g + 1] = __builtin_bit_cast(
+                            int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
+                    }
                 }
                 P[s] = __builtin_bit_cast(v8h, quad);
                 rs = __builtin_amdgcn_mfma_f32_16x16x32_f16(rsel, P[s], rs, 0, 0, 0);
@@ -285,7 +299,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
     lsum = __builtin_fmaf(rs[0], w, lsum);
 }
 
-template <int D, int KSPLIT, bool CAUSAL, int WAVES, int WAVES_PER_SIMD>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, int WAVES, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs a) {
     constexpr int KS = D / 32;
     constexpr int CT = D / 32;
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     const int wave_last = CAUSAL ? min(nkb - 1, (rbase + 31) / SAGE_BN) : nkb - 1;
 
     const uint8_t* kbase = (const uint8_t*)a.k_i8 + (long long)bg * a.Np * D;
-    const uint16_t* vbase = a.v_e4m3 + (long long)bg * a.Np * D;
+    const uint16_t* vbase = a.v16 + (long long)bg * a.Np * D;
     const float* ksc = a.k_scale + (long long)bg * (a.Np / (SAGE_BN / KSPLIT));
 
     // Q fragments (B operand of Q.K^T): query row r32, bytes [32*ks + 16*h, +16).
@@ -368,8 +382,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         float c[KSPLIT];
 #pragma unroll
         for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-        attn_block<D, KSPLIT, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
-                                             a.l448, h, r32, rsel, mref, lsum, O);
+        attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N,
+                                                   c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -383,11 +397,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 #pragma unroll
         for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
         if (T < n_full)
-            attn_block<D, KSPLIT, CAUSAL, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
-                                                 a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
+                                                       a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         else if (T <= wave_last)
-            attn_block<D, KSPLIT, CAUSAL, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
-                                                a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, PV16, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
+                                                      a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -437,38 +451,49 @@ constexpr int attn_waves_per_simd() {
 // Explicit instantiations: with the packed-FP32 feature switched off on the
 // command line, this compiler otherwise leaves the host stubs of some of these
 // kernels undefined.
-#define SAGE_ATTN_INST(D, KSPLIT, CAUSAL) \
-    template __global__ void attn_fwd<D, KSPLIT, CAUSAL, attn_waves<D>(), attn_waves_per_simd<D>()>(AttnArgs);
-SAGE_ATTN_INST(64, 2, false)
-SAGE_ATTN_INST(64, 2, true)
-SAGE_ATTN_INST(64, 4, false)
-SAGE_ATTN_INST(64, 4, true)
-SAGE_ATTN_INST(128, 2, false)
-SAGE_ATTN_INST(128, 2, true)
-SAGE_ATTN_INST(128, 4, false)
-SAGE_ATTN_INST(128, 4, true)
+#define SAGE_ATTN_INST(D, KSPLIT, CAUSAL, PV16)                                                  \
+    template __global__ void attn_fwd<D, KSPLIT, CAUSAL, PV16, attn_waves<D>(), attn_waves_per_simd<D>()>( \
+        AttnArgs);
+#define SAGE_ATTN_INST_PV(D, KSPLIT, CAUSAL) \
+    SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true)
+SAGE_ATTN_INST_PV(64, 2, false)
+SAGE_ATTN_INST_PV(64, 2, true)
+SAGE_ATTN_INST_PV(64, 4, false)
+SAGE_ATTN_INST_PV(64, 4, true)
+SAGE_ATTN_INST_PV(128, 2, false)
+SAGE_ATTN_INST_PV(128, 2, true)
+SAGE_ATTN_INST_PV(128, 4, false)
+SAGE_ATTN_INST_PV(128, 4, true)
+#undef SAGE_ATTN_INST_PV
 #undef SAGE_ATTN_INST
 
-template <int D, int KSPLIT, bool CAUSAL>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WAVES = attn_waves<D>();
     constexpr int WPS = attn_waves_per_simd<D>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, WAVES, WPS>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int total = a.B * a.Hq * a.nqt;
-    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, WAVES, WPS>), dim3(total), dim3(64 * WAVES), lds,
-                       st, a);
+    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>), dim3(total), dim3(64 * WAVES),
+                       lds, st, a);
     return hipGetLastError();
 }
 
+template <int D, int KSPLIT, bool PV16>
+static hipError_t launch_attn_p(AttnArgs a, int causal, hipStream_t st) {
+    return causal ? launch_attn_t<D, KSPLIT, true, PV16>(a, st)
+                  : launch_attn_t<D, KSPLIT, false, PV16>(a, st);
+}
+
 template <int D, int KSPLIT>
-static hipError_t launch_attn_d(AttnArgs a, int causal, hipStream_t st) {
-    return causal ? launch_attn_t<D, KSPLIT, true>(a, st) : launch_attn_t<D, KSPLIT, false>(a, st);
+static hipError_t launch_attn_d(AttnArgs a, int causal, bool pv16, hipStream_t st) {
+    return pv16 ? launch_attn_p<D, KSPLIT, true>(a, causal, st)
+                : launch_attn_p<D, KSPLIT, false>(a, causal, st);
 }
 
 hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal,
@@ -478,7 +503,7 @@ hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int 
     a.q_scale = z->q_scale;
     a.k_i8 = z->k_i8;
     a.k_scale = z->k_scale;
-    a.v_e4m3 = z->v_e4m3;
+    a.v16 = z->v16;
     a.v_scale = z->v_scale;
     a.out = out;
     a.B = s.B;
@@ -492,8 +517,10 @@ hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int 
     a.qk = qk;
     a.l448 = l448;
     const bool fine_k = z->k_block == SAGE_BK_THREAD;  // 4 K scales per block, else 2
-    if (s.d == 64) return fine_k ? launch_attn_d<64, 4>(a, causal, st) : launch_attn_d<64, 2>(a, causal, st);
-    return fine_k ? launch_attn_d<128, 4>(a, causal, st) : launch_attn_d<128, 2>(a, causal, st);
+    const bool pv16 = z->pv_format == SAGE_PV_F16;
+    if (s.d == 64)
+        return fine_k ? launch_attn_d<64, 4>(a, causal, pv16, st) : launch_attn_d<64, 2>(a, causal, pv16, st);
+    return fine_k ? launch_attn_d<128, 4>(a, causal, pv16, st) : launch_attn_d<128, 2>(a, causal, pv16, st);
 }
 
 }  // namespace sage

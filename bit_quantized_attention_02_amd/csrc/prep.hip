@@ -1,7 +1,8 @@
 // The prep step of 8-bit quantized attention: K channel mean and smoothing,
 // per-block INT8 of Q and smoothed K, per-channel E4M3 of V (SageAttention
 // article: smoothing K and per-block INT8 Q/K; SageAttention2 summary: E4M3
-// for V).  Memory-bound: every kernel streams 16-byte loads and does its
+// for V), or V's binary16 rounding for the binary16 P.V of the SageAttention
+// article.  Memory-bound: every kernel streams 16-byte loads and does its
 // reductions in registers, wavefront shuffles and LDS.
 //
 //   prep_q      per (q head, 128-row block): Q absmax per scale group (the
@@ -9,7 +10,8 @@
 //               and INT8 codes;
 //               one extra work-group clears the per-head arrival counters.
 //   prep_stats  per (kv head, 512-row chunk): partial statistics (float64 K
-//               channel sums, V channel absmax).  The head's last work-group
+//               channel sums, V channel absmax unless V goes to binary16).
+//               The head's last work-group
 //               to arrive (an atomic counter; nobody waits) reduces the
 //               partials in a fixed chunk order (deterministic) into the K
 //               mean and the V scales.
@@ -17,7 +19,8 @@
 //               (the block, or each 32-row half at the thread-level
 //               granularity), scales, codes;
 //               per (kv head, 128-key block) V E4M3 codes, stored as the
-//               binary16 values they denote and transposed to the attention
+//               binary16 values they denote (or V's own binary16 rounding),
+//               and transposed to the attention
 //               kernel's channel-major, permuted-key layout.  Heads are
 //               visited in the reverse order of prep_stats so the second read
 //               of K and V finds the most recent heads still in the
@@ -101,7 +104,19 @@ __device__ inline void v_codes_to_tile(const float (&x)[8], const float* inv, in
     }
 }
 
-// Copies a transposed V tile from LDS to its place in v_e4m3 (streaming
+// V's binary16 rounding (nearest even, clamped to +-65504 first so that
+// out-of-range bf16 values saturate) of x[i], i = 0..7, into the transposed
+// V tile.
+template <int D>
+__device__ inline void v_f16_to_tile(const float (&x)[8], int col, int pos, uint16_t* vt) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const _Float16 h = (_Float16)fminf(fmaxf(x[i], -65504.0f), 65504.0f);
+        vt[(col + i) * SAGE_BN + pos] = __builtin_bit_cast(uint16_t, h);
+    }
+}
+
+// Copies a transposed V tile from LDS to its place in v16 (streaming
 // stores: the tile is not read again by this step).
 template <int D>
 __device__ inline void store_v_tile(const uint16_t* vt, uint16_t* dst, int tid) {
@@ -170,7 +185,7 @@ template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_stats(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s,
     double* __restrict__ k_part, float* __restrict__ v_part, int* __restrict__ cnt,
-    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
+    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv, int pv16) {
     constexpr int CPR = D / 8;
     constexpr int RPI = kThreads / CPR;
     __shared__ double ssum[RPI][D];
@@ -192,13 +207,15 @@ __global__ __launch_bounds__(kThreads) void prep_stats(
     }
     for (int r = r0 + rr; r < r1; r += RPI) {
         const long long off = head + (long long)r * D + cg * 8;
-        float fk[8], fv[8];
+        float fk[8];
         unpack8<In>(*reinterpret_cast<const uint4*>(k + off), fk);
-        unpack8<In>(*reinterpret_cast<const uint4*>(v + off), fv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            sum[i] += (double)fk[i];
-            mx[i] = fmaxf(mx[i], fabsf(fv[i]));
+        for (int i = 0; i < 8; ++i) sum[i] += (double)fk[i];
+        if (!pv16) {  // binary16 V needs no channel scale
+            float fv[8];
+            unpack8<In>(*reinterpret_cast<const uint4*>(v + off), fv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(fv[i]));
         }
     }
 #pragma unroll
@@ -239,15 +256,15 @@ __global__ __launch_bounds__(kThreads) void prep_stats(
     }
     const long long o = (long long)bg * D + tid;
     k_mean[o] = (float)(t / (double)s.N);
-    v_scale[o] = m / 448.0f;
-    v_inv[o] = m > 0.0f ? 448.0f / m : 0.0f;
+    v_scale[o] = pv16 ? 1.0f : m / 448.0f;
+    v_inv[o] = pv16 ? 1.0f : (m > 0.0f ? 448.0f / m : 0.0f);
 }
 
 template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_pack(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s, int bk,
     const float* __restrict__ k_mean, const float* __restrict__ v_inv,
-    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint16_t* __restrict__ v_e4m3) {
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint16_t* __restrict__ v16, int pv16) {
     constexpr int CPR = D / 8;
     __shared__ float rmax[64], gmax[64];
     __shared__ __attribute__((aligned(16))) uint16_t vt[D * SAGE_BN];
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
         return;
     }
 
-    // V block T: codes of 128 keys x D channels, transposed through LDS.
+    // V block T: 128 keys x D channels, transposed through LDS.
     const int T = j - nkb;
     constexpr int NCH = SAGE_BN * CPR / kThreads;
 #pragma unroll
@@ -314,10 +331,13 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = 0.0f;
         }
-        v_codes_to_tile<D>(x, v_inv + (long long)bg * D + col, col, v_key_position(key), vt);
+        if (pv16)
+            v_f16_to_tile<D>(x, col, v_key_position(key), vt);
+        else
+            v_codes_to_tile<D>(x, v_inv + (long long)bg * D + col, col, v_key_position(key), vt);
     }
     __syncthreads();
-    store_v_tile<D>(vt, v_e4m3 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN), tid);
+    store_v_tile<D>(vt, v16 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN), tid);
 }
 
 // ------------------------------------------------------------ launchers
@@ -330,15 +350,16 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nchunk = s.part_chunks();
+    const int pv16 = z->pv_format == SAGE_PV_F16;
     hipLaunchKernelGGL((prep_stats<In, D>), dim3(s.B * s.Hkv * nchunk), dim3(kThreads), 0, st,
                        (const uint16_t*)k, (const uint16_t*)v, s, z->k_part, z->v_part, z->sync,
-                       z->k_mean, z->v_scale, z->v_inv);
+                       z->k_mean, z->v_scale, z->v_inv, pv16);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int per_head = s.Np / 64 + s.Np / SAGE_BN;
     hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
                        (const uint16_t*)k, (const uint16_t*)v, s, (int)z->k_block, z->k_mean,
-                       z->v_inv, z->k_i8, z->k_scale, z->v_e4m3);
+                       z->v_inv, z->k_i8, z->k_scale, z->v16, pv16);
     return hipGetLastError();
 }
 

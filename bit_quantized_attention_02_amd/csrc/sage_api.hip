@@ -33,7 +33,7 @@ static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout: each region starts on a 256-byte boundary.
 struct Layout {
-    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v_e4m3, v_scale, v_inv, k_part, v_part, sync, total;
+    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v16, v_scale, v_inv, k_part, v_part, sync, total;
 };
 
 static Layout layout(const Shape& s) {
@@ -47,7 +47,7 @@ static Layout layout(const Shape& s) {
     const size_t Bq = (size_t)s.B * s.Hq, Bkv = (size_t)s.B * s.Hkv;
     L.q_i8 = take((size_t)s.q_elems());
     L.k_i8 = take((size_t)s.kv_elems());
-    L.v_e4m3 = take((size_t)s.kv_elems() * sizeof(uint16_t));
+    L.v16 = take((size_t)s.kv_elems() * sizeof(uint16_t));
     // scales sized for the finer of the two granularities
     L.q_scale = take(Bq * (s.Np / SAGE_BQ_THREAD) * sizeof(float));
     L.k_scale = take(Bkv * (s.Np / SAGE_BK_THREAD) * sizeof(float));
@@ -66,13 +66,16 @@ static bool granularity_ok(int q_block, int k_block) {
            (q_block == SAGE_BQ_THREAD && k_block == SAGE_BK_THREAD);
 }
 
+static bool pv_format_ok(int f) { return f == SAGE_PV_E4M3 || f == SAGE_PV_F16; }
+
 static int check_quant(const sage_qkv_quant* z) {
     if (!z) return SAGE_ERR_INVALID_ARG;
-    if (!granularity_ok(z->q_block, z->k_block)) return SAGE_ERR_UNSUPPORTED;
-    if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v_e4m3 ||
+    if (!granularity_ok(z->q_block, z->k_block) || !pv_format_ok(z->pv_format))
+        return SAGE_ERR_UNSUPPORTED;
+    if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v16 ||
         !z->v_scale || !z->v_inv || !z->k_part || !z->v_part || !z->sync)
         return SAGE_ERR_INVALID_ARG;
-    if (!aligned(z->q_i8, 16) || !aligned(z->k_i8, 16) || !aligned(z->v_e4m3, 16) ||
+    if (!aligned(z->q_i8, 16) || !aligned(z->k_i8, 16) || !aligned(z->v16, 16) ||
         !aligned(z->v_scale, 16) || !aligned(z->k_part, 8))
         return SAGE_ERR_INVALID_ARG;
     return SAGE_OK;
@@ -99,7 +102,7 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->k_i8 = (int8_t*)(base + L.k_i8);
     out->k_scale = (float*)(base + L.k_scale);
     out->k_mean = (float*)(base + L.k_mean);
-    out->v_e4m3 = (uint16_t*)(base + L.v_e4m3);
+    out->v16 = (uint16_t*)(base + L.v16);
     out->v_scale = (float*)(base + L.v_scale);
     out->v_inv = (float*)(base + L.v_inv);
     out->k_part = (double*)(base + L.k_part);
@@ -107,6 +110,7 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->sync = (int32_t*)(base + L.sync);
     out->q_block = SAGE_BQ;
     out->k_block = SAGE_BK;
+    out->pv_format = SAGE_PV_E4M3;
     return SAGE_OK;
 }
 
@@ -134,21 +138,23 @@ int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq
     rc = check_quant(src);
     if (rc != SAGE_OK) return rc;
     const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
-    // the exponent factor and log2(448) are rounded once to float32 here, as
-    // the method's spec defines them
+    // the exponent factor and log2 of the P block maximum's code (448 for
+    // E4M3, 1 for binary16) are rounded once to float32 here, as the method's
+    // spec defines them
     const float qk = (float)((double)sm_scale * 1.4426950408889634);
-    const float l448 = (float)log2(448.0);
+    const float l448 = src->pv_format == SAGE_PV_F16 ? 0.0f : (float)log2(448.0);
     hipError_t e = sage::launch_attn(src, out, s, causal, qk, l448, (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
-int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* out, int B, int Hq,
-                           int Hkv, int N, int d, int causal, float sm_scale, int dtype,
-                           int q_block, int k_block, void* workspace, size_t ws_bytes,
-                           void* stream) {
+int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                     int N, int d, int causal, float sm_scale, int dtype, const sage_options* opts,
+                     void* workspace, size_t ws_bytes, void* stream) {
     int rc = check_shape(B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
-    if (!granularity_ok(q_block, k_block)) return SAGE_ERR_UNSUPPORTED;
+    if (!opts) return SAGE_ERR_INVALID_ARG;
+    if (!granularity_ok(opts->q_block, opts->k_block) || !pv_format_ok(opts->pv_format))
+        return SAGE_ERR_UNSUPPORTED;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
     if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
@@ -158,11 +164,21 @@ int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* o
     sage_qkv_quant z;
     rc = sage_workspace_carve(workspace, ws_bytes, B, Hq, Hkv, N, d, &z);
     if (rc != SAGE_OK) return rc;
-    z.q_block = q_block;
-    z.k_block = k_block;
+    z.q_block = opts->q_block;
+    z.k_block = opts->k_block;
+    z.pv_format = opts->pv_format;
     rc = sage_quantize(q, k, v, dtype, B, Hq, Hkv, N, d, &z, stream);
     if (rc != SAGE_OK) return rc;
     return sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, causal, sm_scale, stream);
+}
+
+int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                           int Hkv, int N, int d, int causal, float sm_scale, int dtype,
+                           int q_block, int k_block, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    const sage_options o = {q_block, k_block, SAGE_PV_E4M3};
+    return sage_attn_fwd_ex(q, k, v, out, B, Hq, Hkv, N, d, causal, sm_scale, dtype, &o, workspace,
+                            ws_bytes, stream);
 }
 
 int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
@@ -192,8 +208,8 @@ const char* sage_status_string(int status) {
         case SAGE_OK: return "ok";
         case SAGE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad flag or size)";
         case SAGE_ERR_UNSUPPORTED:
-            return "unsupported shape or granularity (d must be 64 or 128, Hq % Hkv == 0, N <= 2^20; "
-                   "(q_block, k_block) = (128, 64) or (1, 32))";
+            return "unsupported shape or option (d must be 64 or 128, Hq % Hkv == 0, N <= 2^20; "
+                   "(q_block, k_block) = (128, 64) or (1, 32); P.V format E4M3 (0) or binary16 (1))";
         case SAGE_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
         case SAGE_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";

@@ -35,6 +35,13 @@
  *     the block's P8.V8 product, exact products summed in FP32 by the matrix
  *     core; level 2 adds it, weighted by 2^(m - reference max), into FP32
  *     registers.  The row sum is the same weighted sum of the quantized P.
+ *   - P.V format (sage_qkv_quant.pv_format).  SAGE_PV_E4M3 is the above.
+ *     SAGE_PV_F16 is the SageAttention article's own P.V (paragraph on the P, V
+ *     product: P and V stay FP16): V is its binary16 rounding (round to nearest
+ *     even, saturating at +-65504) with no scale, and P is
+ *     f16(2^fmaf(acc, c, -m)), so the block's largest element is exactly 1.
+ *     The article accumulates in FP16; the binary16 matrix cores here
+ *     accumulate in FP32 only, so both levels stay FP32.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -71,11 +78,14 @@ extern "C" {
 #define SAGE_MAX_N (1 << 20)
 #define SAGE_BQ_THREAD 1  /* query rows per Q scale, thread-level granularity */
 #define SAGE_BK_THREAD 32 /* keys per K scale, thread-level granularity */
+#define SAGE_PV_E4M3 0    /* P and V as FP8 E4M3 (the default) */
+#define SAGE_PV_F16 1     /* P and V as binary16 */
 
 typedef enum {
     SAGE_OK = 0,
     SAGE_ERR_INVALID_ARG = -1, /* null or misaligned pointer, bad flag, bad size */
-    SAGE_ERR_UNSUPPORTED = -2, /* d not in {64,128}, Hq % Hkv != 0, N too large */
+    SAGE_ERR_UNSUPPORTED = -2, /* d not in {64,128}, Hq % Hkv != 0, N too large, unknown
+                                  granularity or P.V format */
     SAGE_ERR_WORKSPACE = -3,   /* workspace too small or misaligned */
     SAGE_ERR_HIP = -4          /* a HIP launch failed */
 } sage_status;
@@ -97,14 +107,15 @@ typedef struct {
  *   k_i8    int8 [B, Hkv, N_p, d]           codes of K - k_mean
  *   k_scale f32  [B, Hkv, N_p / bk]
  *   k_mean  f32  [B, Hkv, d]
- *   v_e4m3  binary16 [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: the E4M3 codes of V,
- *           each stored as the binary16 number it denotes (exact: every E4M3
- *           value is a binary16 value), so the P.V product can run on the
- *           binary16 matrix core with exact products.  For each block of
- *           SAGE_BN keys and each channel, the block's values in the key order
- *           of sage_v_key_position()
- *   v_scale f32  [B, Hkv, d]                absmax / 448 per channel
- *   v_inv   f32  [B, Hkv, d]                448 / absmax (0 for a zero channel)
+ *   v16     binary16 [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: the V operand of
+ *           P.V.  With SAGE_PV_E4M3, the E4M3 codes of V, each stored as the
+ *           binary16 number it denotes (exact: every E4M3 value is a binary16
+ *           value), so the product runs on the binary16 matrix core with exact
+ *           products; with SAGE_PV_F16, V's own binary16 rounding.  For each
+ *           block of SAGE_BN keys and each channel, the block's values in the
+ *           key order of sage_v_key_position()
+ *   v_scale f32  [B, Hkv, d]                absmax / 448 per channel (1 with SAGE_PV_F16)
+ *   v_inv   f32  [B, Hkv, d]                448 / absmax, 0 for a zero channel (1 with SAGE_PV_F16)
  *   k_part, v_part: per-chunk partial statistics used by sage_quantize.
  *   sync    int32 [B * Hkv]: per-kv-head arrival counters of the statistics
  *           kernel of sage_quantize, which clears them itself on every call.
@@ -115,7 +126,7 @@ typedef struct {
     int8_t* k_i8;
     float* k_scale;
     float* k_mean;
-    uint16_t* v_e4m3;
+    uint16_t* v16;
     float* v_scale;
     float* v_inv;
     double* k_part;
@@ -123,7 +134,16 @@ typedef struct {
     int32_t* sync;
     int32_t q_block; /* query rows per Q scale: SAGE_BQ (set by sage_workspace_carve) or SAGE_BQ_THREAD */
     int32_t k_block; /* keys per K scale: SAGE_BK (set by sage_workspace_carve) or SAGE_BK_THREAD */
+    int32_t pv_format; /* SAGE_PV_E4M3 (set by sage_workspace_carve) or SAGE_PV_F16; the
+                          attention call must see the value the quantize call saw */
 } sage_qkv_quant;
+
+/* Method options of sage_attn_fwd_ex. */
+typedef struct {
+    int32_t q_block;   /* SAGE_BQ or SAGE_BQ_THREAD */
+    int32_t k_block;   /* SAGE_BK or SAGE_BK_THREAD (paired with q_block as above) */
+    int32_t pv_format; /* SAGE_PV_E4M3 or SAGE_PV_F16 */
+} sage_options;
 
 /* Bytes of workspace sage_quantize/sage_attn_fwd need for this shape (0 when
  * the shape is invalid). */
@@ -131,17 +151,18 @@ size_t sage_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /* Split `workspace` (device memory, 256-byte aligned, ws_bytes long) into the
  * views above, with the per-block granularity (q_block = SAGE_BQ, k_block =
- * SAGE_BK); the caller may then switch both to SAGE_BQ_THREAD and
- * SAGE_BK_THREAD (the workspace holds the scales of either).  The quantize and
- * attention calls given the struct read the granularity from it; any other
- * pair of values makes them return SAGE_ERR_UNSUPPORTED.  Host-only; no HIP
- * call. */
+ * SAGE_BK) and E4M3 P.V; the caller may then switch both block sizes to
+ * SAGE_BQ_THREAD and SAGE_BK_THREAD (the workspace holds the scales of
+ * either) and pv_format to SAGE_PV_F16.  The quantize and attention calls
+ * given the struct read these fields; any other values make them return
+ * SAGE_ERR_UNSUPPORTED.  Host-only; no HIP call. */
 int sage_workspace_carve(void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
                          sage_qkv_quant* out);
 
 /*
  * The prep step (K mean, smoothing, per-block INT8 of Q and K, per-channel
- * FP8 of V) from fp16/bf16 Q, K, V into the views of `dst`.  Memory-bound; runs
+ * FP8 of V, or V's binary16 rounding with SAGE_PV_F16) from fp16/bf16 Q, K, V
+ * into the views of `dst`.  Memory-bound; runs
  * as three kernels on `stream`: Q codes; K/V statistics, whose last
  * work-group per kv head forms the K mean and V scales; K/V codes.
  */
@@ -161,7 +182,7 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
                   int N, int d, int causal, float sm_scale, int dtype, void* workspace,
                   size_t ws_bytes, void* stream);
 
-/* sage_attn_fwd with the quantization granularity chosen by the caller:
+/* sage_attn_fwd (E4M3 P.V) with the quantization granularity chosen by the caller:
  * (q_block, k_block) = (SAGE_BQ, SAGE_BK) is sage_attn_fwd itself,
  * (SAGE_BQ_THREAD, SAGE_BK_THREAD) the thread-level granularity; any other
  * pair returns SAGE_ERR_UNSUPPORTED. */
@@ -170,10 +191,17 @@ int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* o
                            int q_block, int k_block, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* sage_attn_fwd with every method option chosen by the caller (opts must not
+ * be NULL): the quantization granularity and the P.V format.  Options outside
+ * the values listed in sage_options return SAGE_ERR_UNSUPPORTED. */
+int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                     int N, int d, int causal, float sm_scale, int dtype, const sage_options* opts,
+                     void* workspace, size_t ws_bytes, void* stream);
+
 /* Block sizes and format constants of this build. */
 int sage_get_config(sage_config* c);
 
-/* Position of key j (0 <= j < SAGE_BN) inside a block's row of v_e4m3; -1 if j
+/* Position of key j (0 <= j < SAGE_BN) inside a block's row of v16; -1 if j
  * is out of range.  Describes the layout only (for callers that read the
  * quantized V back). */
 int sage_v_key_position(int j);

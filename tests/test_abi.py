@@ -72,7 +72,7 @@ def test_carve_checks_alignment_and_size(sage):
     ptrs = [getattr(z, f) for f, t in sage.sage_qkv_quant._fields_ if t is ctypes.c_void_p]
     assert len(ptrs) == 11
     assert all(p % 256 == 0 for p in ptrs) and len(set(ptrs)) == len(ptrs)
-    assert (z.q_block, z.k_block) == (128, 64)
+    assert (z.q_block, z.k_block, z.pv_format) == (128, 64, sage.SAGE_PV_E4M3)
     assert max(ptrs) < fake + need
     assert _carve(sage, fake, need - 1, shape)[0] == sage.SAGE_ERR_WORKSPACE
     assert _carve(sage, fake + 16, need, shape)[0] == sage.SAGE_ERR_WORKSPACE
@@ -118,7 +118,7 @@ def test_entry_points_reject_bad_arguments_before_any_hip_call(sage):
     assert L.sage_quantize(fake, fake, fake, 3, 1, 4, 2, 300, 64, zp, None) == sage.SAGE_ERR_INVALID_ARG
     assert L.sage_quantize(fake, fake, fake, 0, 1, 4, 2, 300, 128 + 64, zp, None) == sage.SAGE_ERR_UNSUPPORTED
     bad = sage.sage_qkv_quant.from_buffer_copy(z)
-    bad.v_e4m3 = None
+    bad.v16 = None
     assert L.sage_quantize(fake, fake, fake, 0, 1, 4, 2, 300, 64, ctypes.byref(bad), None) == sage.SAGE_ERR_INVALID_ARG
     # sage_attn_fwd_quantized
     f = ctypes.c_float
@@ -153,3 +153,38 @@ def test_granularity_is_validated(sage):
             assert L.sage_attn_fwd_quantized(zp, fake, *shape, 0, f(0.125), None) == bad
     z = sage.sage_workspace_carve(fake, need, *shape, granularity="thread")
     assert (z.q_block, z.k_block) == (sage.SAGE_BQ_THREAD, sage.SAGE_BK_THREAD)
+
+
+def test_pv_format_is_validated(sage):
+    """SAGE_PV_E4M3 (0) and SAGE_PV_F16 (1) are accepted by sage_attn_fwd_ex
+    and the struct-taking calls; other values, and a NULL options pointer, are
+    rejected before any HIP call."""
+    L = sage._lib
+    fake = 1 << 40
+    shape = (1, 4, 2, 300, 64)
+    need = sage.sage_workspace_bytes(*shape)
+    f = ctypes.c_float
+    bad = sage.SAGE_ERR_UNSUPPORTED
+    for granularity in ("block", "thread"):
+        for pv, ok in ((0, True), (1, True), (2, False), (-1, False)):
+            o = sage.options(granularity)
+            o.pv_format = pv
+            rc = L.sage_attn_fwd_ex(fake, fake, fake, None, *shape, 0, f(0.125), 0, ctypes.byref(o),
+                                    fake, need, None)
+            # options are checked before the pointers: valid ones get as far
+            # as the null `out`
+            assert rc == (sage.SAGE_ERR_INVALID_ARG if ok else bad)
+            if not ok:
+                z = sage.sage_workspace_carve(fake, need, *shape, granularity=granularity)
+                z.pv_format = pv
+                zp = ctypes.byref(z)
+                assert L.sage_quantize(fake, fake, fake, 0, *shape, zp, None) == bad
+                assert L.sage_attn_fwd_quantized(zp, fake, *shape, 0, f(0.125), None) == bad
+    o = sage.options("block", "e4m3")
+    o.k_block = 32
+    assert L.sage_attn_fwd_ex(fake, fake, fake, fake, *shape, 0, f(0.125), 0, ctypes.byref(o), fake,
+                              need, None) == bad
+    assert L.sage_attn_fwd_ex(fake, fake, fake, fake, *shape, 0, f(0.125), 0, None, fake, need,
+                              None) == sage.SAGE_ERR_INVALID_ARG
+    z = sage.sage_workspace_carve(fake, need, *shape, pv="f16")
+    assert z.pv_format == sage.SAGE_PV_F16

@@ -2,8 +2,10 @@
 
 Prep outputs (codes, scales, K mean) must be bit-exact.  The attention output
 must lie within the oracle's interval (the set of outputs reachable by the P
-codes that sit within 2^-20 of an E4M3 rounding midpoint, where the hardware
-exp2 may round either way) up to max-abs 2e-3 and rel-L1 1e-3.
+codes that sit within 2^-20 of an E4M3 or binary16 rounding midpoint, where
+the hardware exp2 may round either way) up to max-abs 2e-3 and rel-L1 1e-3.
+Both P.V formats (E4M3 and binary16) and both quantization granularities are
+covered.
 """
 import math
 import sys
@@ -32,12 +34,12 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(sage, q, k, v, causal, sm_scale, granularity="block"):
+def run_gpu(sage, q, k, v, causal, sm_scale, granularity="block", pv="e4m3"):
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     ws = sage.workspace_for(qd, kd)
-    z = sage.sage_workspace_carve(ws, ws.numel(), B, Hq, Hkv, N, d, granularity=granularity)
+    z = sage.sage_workspace_carve(ws, ws.numel(), B, Hq, Hkv, N, d, granularity=granularity, pv=pv)
     sage.sage_quantize(qd, kd, vd, z)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     sage.sage_attn_fwd_quantized(z, out, B, Hq, Hkv, N, d, causal, sm_scale)
@@ -49,15 +51,21 @@ def run_gpu(sage, q, k, v, causal, sm_scale, granularity="block"):
 def check_prep(orc, quant, oz):
     np.testing.assert_array_equal(quant["q_i8"].numpy(), oz["q_i8"])
     np.testing.assert_array_equal(quant["k_i8"].numpy(), oz["k_i8"])
-    np.testing.assert_array_equal(quant["v_fp8"].numpy(), oz["v_fp8"])
     np.testing.assert_array_equal(quant["k_mean"].numpy(), oz["k_mean"])
-    np.testing.assert_array_equal(quant["v_scale"].numpy(), oz["v_scale"])
+    if oz["pv"] == "f16":
+        # V's binary16 rounding, bit for bit, and no V scale
+        np.testing.assert_array_equal(quant["v_f16"].numpy().view(np.uint16), oz["v_f16"])
+        assert (quant["v_scale"].numpy() == 1.0).all()
+    else:
+        np.testing.assert_array_equal(quant["v_fp8"].numpy(), oz["v_fp8"])
+        np.testing.assert_array_equal(quant["v_scale"].numpy(), oz["v_scale"])
     nqb, nkb = oz["q_scale"].shape[-1], oz["k_scale"].shape[-1]
     np.testing.assert_array_equal(quant["q_scale"].numpy()[..., :nqb], oz["q_scale"])
     np.testing.assert_array_equal(quant["k_scale"].numpy()[..., :nkb], oz["k_scale"])
     assert not quant["q_pad"].any() and not quant["k_pad"].any() and not quant["v_pad"].any()
-    # the binary16 copies denote exactly the E4M3 values of the codes
-    np.testing.assert_array_equal(quant["v_half"].to(torch.float64).numpy(), orc.e4m3_decode(oz["v_fp8"]))
+    # the binary16 V operand denotes exactly the values of the codes
+    vals = orc.f16_decode(oz["v_f16"]) if oz["pv"] == "f16" else orc.e4m3_decode(oz["v_fp8"])
+    np.testing.assert_array_equal(quant["v_half"].to(torch.float64).numpy(), vals)
 
 
 def check_attn(orc, out_rows, oz, causal, sm_scale, rows):
@@ -78,23 +86,24 @@ def _rows_of(out, rows, d):
     return out.reshape(-1, d).cpu().numpy()[rows]
 
 
-def quantize_as(orc, q, k, v, granularity):
+def quantize_as(orc, q, k, v, granularity, pv="e4m3"):
     bq, bk = {"block": (128, 64), "thread": (1, 32)}[granularity]
-    return orc.quantize(q, k, v, bq=bq, bk=bk)
+    return orc.quantize(q, k, v, bq=bq, bk=bk, pv=pv)
 
 
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
 @pytest.mark.parametrize("granularity", ["block", "thread"])
 @pytest.mark.parametrize("recipe", [1, 2, 3, 4, 5])
-def test_parity_reduced_workloads(sage, orc, recipe, granularity):
+def test_parity_reduced_workloads(sage, orc, recipe, granularity, pv):
     """Each workload's recipe at a size the oracle covers in full: several
     128-row tiles and a ragged tail (N = 700)."""
     w0 = workloads.WORKLOADS[recipe]
     w = w0.resized(B=2, Hq=2 * (w0.Hq // w0.Hkv), Hkv=2, N=700)
     _say(f"case recipe={recipe} shape={(w.B, w.Hq, w.Hkv, w.N, w.d)} causal={w.causal} "
-         f"granularity={granularity}")
+         f"granularity={granularity} pv={pv}")
     q, k, v = workloads.generate(w, seed=1000 + recipe)
-    out, quant = run_gpu(sage, q, k, v, w.causal, w.sm_scale, granularity)
-    oz = quantize_as(orc, q, k, v, granularity)
+    out, quant = run_gpu(sage, q, k, v, w.causal, w.sm_scale, granularity, pv)
+    oz = quantize_as(orc, q, k, v, granularity, pv)
     check_prep(orc, quant, oz)
     rows = np.arange(w.B * w.Hq * w.N)
     check_attn(orc, out.reshape(-1, w.d).cpu().numpy(), oz, w.causal, w.sm_scale, rows)
@@ -105,11 +114,12 @@ def test_parity_reduced_workloads(sage, orc, recipe, granularity):
 @pytest.mark.parametrize("causal", [False, True])
 def test_parity_edge_lengths(sage, orc, N, d, causal):
     granularity = "thread" if N in (17, 129, 300) else "block"
-    _say(f"case N={N} d={d} causal={causal} granularity={granularity}")
+    pv = "f16" if N in (2, 64, 129, 256) else "e4m3"
+    _say(f"case N={N} d={d} causal={causal} granularity={granularity} pv={pv}")
     q, k, v = workloads.random_inputs(1, 4, 2, N, d, "f16" if d == 64 else "bf16",
                                       seed=N * 7 + d + causal, scale=1.5)
-    out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d), granularity)
-    oz = quantize_as(orc, q, k, v, granularity)
+    out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d), granularity, pv)
+    oz = quantize_as(orc, q, k, v, granularity, pv)
     check_prep(orc, quant, oz)
     check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 1 / math.sqrt(d), None)
 
@@ -124,10 +134,12 @@ def test_degenerate_inputs(sage, orc):
     v[0, 0, :, 3] = 0.0
     k[0, 0, 100] = 12.0
     q[0, 1, :, :] = q[0, 1, :, :].abs()
-    for causal, granularity in ((False, "block"), (True, "block"), (True, "thread")):
-        _say(f"case degenerate causal={causal} granularity={granularity}")
-        out, quant = run_gpu(sage, q, k, v, causal, 0.125, granularity)
-        oz = quantize_as(orc, q, k, v, granularity)
+    for causal, granularity, pv in ((False, "block", "e4m3"), (True, "block", "e4m3"),
+                                    (True, "thread", "e4m3"), (False, "block", "f16"),
+                                    (True, "thread", "f16")):
+        _say(f"case degenerate causal={causal} granularity={granularity} pv={pv}")
+        out, quant = run_gpu(sage, q, k, v, causal, 0.125, granularity, pv)
+        oz = quantize_as(orc, q, k, v, granularity, pv)
         check_prep(orc, quant, oz)
         check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 0.125, None)
 
@@ -161,37 +173,46 @@ def test_prep_on_a_used_workspace(sage, orc, d):
     check_prep(orc, results[1], orc.quantize(q, k, v))
 
 
-def test_sage_attn_fwd_matches_two_step_path(sage):
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
+def test_sage_attn_fwd_matches_two_step_path(sage, pv):
     w = workloads.WORKLOADS[2].resized(B=1, Hq=4, Hkv=4, N=515)
     q, k, v = (t.cuda() for t in workloads.generate(w, seed=3))
-    one = sage.attn(q, k, v, causal=True)
-    two, _ = run_gpu(sage, q.cpu(), k.cpu(), v.cpu(), True, w.sm_scale)
+    one = sage.attn(q, k, v, causal=True, pv=pv)
+    two, _ = run_gpu(sage, q.cpu(), k.cpu(), v.cpu(), True, w.sm_scale, pv=pv)
     torch.cuda.synchronize()
     assert torch.equal(one, two)
+    if pv == "e4m3":
+        ws = sage.workspace_for(q, k)
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        sage.sage_attn_fwd(q, k, v, out, True, w.sm_scale, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(one, out)
 
 
-@pytest.mark.parametrize("index,granularity", [(1, "block"), (2, "block"), (3, "block"), (4, "block"),
-                                               (5, "block"), (3, "thread"), (4, "thread"),
-                                               (5, "thread")])
-def test_parity_full_size_workloads(sage, orc, index, granularity):
+@pytest.mark.parametrize("index,granularity,pv", [
+    (1, "block", "e4m3"), (2, "block", "e4m3"), (3, "block", "e4m3"), (4, "block", "e4m3"),
+    (5, "block", "e4m3"), (3, "thread", "e4m3"), (4, "thread", "e4m3"), (5, "thread", "e4m3"),
+    (2, "block", "f16"), (3, "block", "f16"), (4, "block", "f16"), (5, "block", "f16"),
+    (5, "thread", "f16")])
+def test_parity_full_size_workloads(sage, orc, index, granularity, pv):
     """Each workload at its full size, through sage_attn_fwd as the benchmark
     times it: the prep outputs are compared in full (bit-exact), the attention
     output on sampled rows the oracle computes one by one (first and last row
     of the first and last head, 256 seeded rows, and for the peaked-row recipe
     some of the x20 rows)."""
     w = workloads.WORKLOADS[index]
-    _say(f"case full-size workload {index} {w.name} granularity={granularity}")
+    _say(f"case full-size workload {index} {w.name} granularity={granularity} pv={pv}")
     q, k, v = workloads.generate(w)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
     ws = sage.workspace_for(qd, kd)
-    qb, kb = sage.GRANULARITY[granularity]
-    sage.sage_attn_fwd_granular(qd, kd, vd, out, w.causal, w.sm_scale, qb, kb, ws)
+    sage.sage_attn_fwd_ex(qd, kd, vd, out, w.causal, w.sm_scale, sage.options(granularity, pv), ws)
     torch.cuda.synchronize()
-    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d, granularity=granularity)
+    z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d, granularity=granularity,
+                                  pv=pv)
     quant = sage.read_quantized(z, ws, w.B, w.Hq, w.Hkv, w.N, w.d)
     del qd, kd, vd
-    oz = quantize_as(orc, q, k, v, granularity)
+    oz = quantize_as(orc, q, k, v, granularity, pv)
     check_prep(orc, quant, oz)
     rows = workloads.sample_rows(w, 256, seed=11)
     if w.recipe == 4:
