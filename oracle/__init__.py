@@ -68,9 +68,11 @@ def _load():
         lib.oracle_f16_encode_array.argtypes = [P, l, P]
         lib.oracle_f16_decode_array.argtypes = [P, l, P]
         lib.oracle_quantize.argtypes = [P, P, P, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
-        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, f, dd, P,
-                                      l, P, P, P, P]
-        lib.oracle_attn_f64.argtypes = [P, P, P, i, i, i, i, i, i, dd, P, l, P]
+        lib.oracle_quantize_q.argtypes = [P, i, i, i, i, i, P, P]
+        lib.oracle_quantize_kv.argtypes = [P, P, i, i, i, i, i, i, P, P, P, P, P]
+        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, i, f, dd,
+                                      P, l, P, P, P, P]
+        lib.oracle_attn_f64.argtypes = [P, P, P, i, i, i, i, i, i, i, dd, P, l, P]
         lib.oracle_num_threads.restype = i
         _lib = lib
     return _lib
@@ -125,75 +127,99 @@ def f16_decode(c) -> np.ndarray:
 PV_FORMATS = ("e4m3", "f16")
 
 
-def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True, pv: str = "e4m3") -> dict:
-    """The prep step on [B,H,N,d] inputs.  Returns codes in the plain logical
-    layout [B,H,N,d] and the scales (see oracle_quantize in oracle.c).  With
-    pv="f16" it also returns v_f16, the binary16 codes of V, which attn_q then
-    uses (no V scale)."""
+def quantize_q(q, bq: int = BQ) -> dict:
+    """The Q half of the prep step on [B,Hq,Nq,d]: INT8 codes and one scale
+    per bq rows (see oracle_quantize_q in oracle.c)."""
+    q = to_f32(q)
+    B, Hq, Nq, d = q.shape
+    r = dict(q_i8=np.empty((B, Hq, Nq, d), np.int8),
+             q_scale=np.empty((B, Hq, -(-Nq // bq)), np.float32))
+    _load().oracle_quantize_q(_ptr(q), B, Hq, Nq, d, bq, _ptr(r["q_i8"]), _ptr(r["q_scale"]))
+    r.update(B=B, Hq=Hq, Nq=Nq, d=d, bq=bq)
+    return r
+
+
+def quantize_kv(k, v, bk: int = BK, smooth: bool = True, pv: str = "e4m3") -> dict:
+    """The K/V half of the prep step on [B,Hkv,Nk,d] (a quantized KV cache):
+    K mean, smoothed INT8 K with one scale per bk keys, and V as E4M3 codes
+    with per-channel scales, or with pv="f16" also v_f16, the binary16 codes
+    of V, which attn_q then uses (no V scale)."""
     if pv not in PV_FORMATS:
         raise ValueError(f"pv must be one of {PV_FORMATS}")
-    q, k, v = to_f32(q), to_f32(k), to_f32(v)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    nqb, nkb = -(-N // bq), -(-N // bk)
-    r = dict(
-        q_i8=np.empty((B, Hq, N, d), np.int8), q_scale=np.empty((B, Hq, nqb), np.float32),
-        k_i8=np.empty((B, Hkv, N, d), np.int8), k_scale=np.empty((B, Hkv, nkb), np.float32),
-        k_mean=np.empty((B, Hkv, d), np.float32), v_fp8=np.empty((B, Hkv, N, d), np.uint8),
-        v_scale=np.empty((B, Hkv, d), np.float32))
-    _load().oracle_quantize(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, bq, bk, int(smooth),
-                            _ptr(r["q_i8"]), _ptr(r["q_scale"]), _ptr(r["k_i8"]),
-                            _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(r["v_fp8"]),
-                            _ptr(r["v_scale"]))
+    k, v = to_f32(k), to_f32(v)
+    B, Hkv, Nk, d = k.shape
+    r = dict(k_i8=np.empty((B, Hkv, Nk, d), np.int8),
+             k_scale=np.empty((B, Hkv, -(-Nk // bk)), np.float32),
+             k_mean=np.empty((B, Hkv, d), np.float32), v_fp8=np.empty((B, Hkv, Nk, d), np.uint8),
+             v_scale=np.empty((B, Hkv, d), np.float32))
+    _load().oracle_quantize_kv(_ptr(k), _ptr(v), B, Hkv, Nk, d, bk, int(smooth), _ptr(r["k_i8"]),
+                               _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(r["v_fp8"]),
+                               _ptr(r["v_scale"]))
     if pv == "f16":
         r["v_f16"] = f16_encode(v)
-    r.update(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, bq=bq, bk=bk, pv=pv)
+    r.update(B=B, Hkv=Hkv, Nk=Nk, d=d, bk=bk, pv=pv)
+    return r
+
+
+def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True, pv: str = "e4m3") -> dict:
+    """The prep step on [B,H,N,d] inputs (both halves, same N).  Returns codes
+    in the plain logical layout [B,H,N,d] and the scales (see oracle_quantize
+    in oracle.c)."""
+    r = quantize_q(q, bq)
+    r.update(quantize_kv(k, v, bk, smooth, pv))
+    r["N"] = r["Nk"]
     return r
 
 
 def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
            tau: float = TAU, interval: bool = True):
-    """Quantized attention from the prep outputs `qz` for the given flattened
-    rows (None = all), in the P.V format qz["pv"] was made for.  Returns
-    (out, lo, hi, flagged), float64 [nrows, d]."""
+    """Quantized attention from the prep outputs `qz` (quantize, or the merged
+    dicts of quantize_q and quantize_kv: Nq query rows at the last Nq of Nk
+    positions) for the given flattened rows (None = all), in the P.V format
+    qz["pv"] was made for.  Returns (out, lo, hi, flagged), float64 [nrows, d]."""
     f16 = qz.get("pv", "e4m3") == "f16"
     v_codes = qz["v_f16"] if f16 else qz["v_fp8"]
     v_scale = None if f16 else qz["v_scale"]
-    B, Hq, Hkv, N, d = qz["B"], qz["Hq"], qz["Hkv"], qz["N"], qz["d"]
+    B, Hq, Hkv, Nq, Nk, d = qz["B"], qz["Hq"], qz["Hkv"], qz["Nq"], qz["Nk"], qz["d"]
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
     if rows is not None:
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         nrows = rows.size
     else:
-        nrows = B * Hq * N
+        nrows = B * Hq * Nq
     out = np.empty((nrows, d), np.float64)
     lo = np.empty((nrows, d), np.float64) if interval else None
     hi = np.empty((nrows, d), np.float64) if interval else None
     flagged = np.empty(nrows, np.int64) if interval else None
     _load().oracle_attn_q(_ptr(qz["q_i8"]), _ptr(qz["q_scale"]), _ptr(qz["k_i8"]),
                           _ptr(qz["k_scale"]), _ptr(v_codes), _ptr(v_scale), int(f16),
-                          B, Hq, Hkv, N, d, qz["bq"], qz["bk"], bn, int(causal),
+                          B, Hq, Hkv, Nq, Nk, d, qz["bq"], qz["bk"], bn, int(causal),
                           float(sm_scale), float(tau), _ptr(rows), nrows,
                           _ptr(out), _ptr(lo), _ptr(hi), _ptr(flagged))
     return out, lo, hi, flagged
 
 
 def attn_f64(q, k, v, causal: bool, sm_scale: float, rows=None) -> np.ndarray:
-    """Full-precision softmax(QK^T*sm_scale)V in float64 for the given rows."""
+    """Full-precision softmax(QK^T*sm_scale)V in float64 for the given rows;
+    q [B,Hq,Nq,d] sits at the last Nq of the Nk positions of k, v."""
     q = np.ascontiguousarray(np.asarray(to_f32(q) if isinstance(q, torch.Tensor) else q,
                                         dtype=np.float64))
     k = np.ascontiguousarray(np.asarray(to_f32(k) if isinstance(k, torch.Tensor) else k,
                                         dtype=np.float64))
     v = np.ascontiguousarray(np.asarray(to_f32(v) if isinstance(v, torch.Tensor) else v,
                                         dtype=np.float64))
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
     if rows is not None:
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         nrows = rows.size
     else:
-        nrows = B * Hq * N
+        nrows = B * Hq * Nq
     out = np.empty((nrows, d), np.float64)
-    _load().oracle_attn_f64(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, int(causal),
+    _load().oracle_attn_f64(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Nq, Nk, d, int(causal),
                             float(sm_scale), _ptr(rows), nrows, _ptr(out))
     return out
 

@@ -175,7 +175,9 @@ static void quant_block_i8(const float* x, long count, int8_t* out, float* scale
 /*
  * The prep step: K mean and smoothing, per-block INT8 of Q and smoothed K,
  * per-channel E4M3 of V.  Inputs are float32 copies of the fp16/bf16 tensors
- * (the up-conversion is exact), layout [B, H, N, d].
+ * (the up-conversion is exact), layout [B, H, N, d].  The Q half and the K/V
+ * half are independent (a KV cache is the K/V half over the cached tokens,
+ * and a short query the Q half over its own rows).
  *
  * Outputs (all caller-allocated):
  *   q_i8 [B,Hq,N,d], q_scale [B,Hq,ceil(N/bq)]
@@ -183,14 +185,11 @@ static void quant_block_i8(const float* x, long count, int8_t* out, float* scale
  *   v_fp8 [B,Hkv,N,d] (E4M3 codes), v_scale [B,Hkv,d]
  * smooth = 0 skips the K mean (ablation only; k_mean is then all zero).
  */
-void oracle_quantize(const float* q, const float* k, const float* v,
-                     int B, int Hq, int Hkv, int N, int d, int bq, int bk, int smooth,
-                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
-                     float* k_mean, uint8_t* v_fp8, float* v_scale) {
+void oracle_quantize_q(const float* q, int B, int Hq, int N, int d, int bq, int8_t* q_i8,
+                       float* q_scale) {
     const long nd = (long)N * d;
-    const int nqb = (N + bq - 1) / bq, nkb = (N + bk - 1) / bk;
-
-    /* Q: one scale per (b, h, block of bq rows). */
+    const int nqb = (N + bq - 1) / bq;
+    /* one scale per (b, h, block of bq rows) */
 #pragma omp parallel for collapse(2) schedule(static)
     for (int bh = 0; bh < B * Hq; ++bh)
         for (int t = 0; t < nqb; ++t) {
@@ -198,6 +197,13 @@ void oracle_quantize(const float* q, const float* k, const float* v,
             quant_block_i8(q + bh * nd + r0 * d, (r1 - r0) * d, q_i8 + bh * nd + r0 * d,
                            q_scale + (long)bh * nqb + t);
         }
+}
+
+void oracle_quantize_kv(const float* k, const float* v, int B, int Hkv, int N, int d, int bk,
+                        int smooth, int8_t* k_i8, float* k_scale, float* k_mean, uint8_t* v_fp8,
+                        float* v_scale) {
+    const long nd = (long)N * d;
+    const int nkb = (N + bk - 1) / bk;
 
 #pragma omp parallel for schedule(static)
     for (int bg = 0; bg < B * Hkv; ++bg) {
@@ -243,12 +249,23 @@ void oracle_quantize(const float* q, const float* k, const float* v,
     }
 }
 
+void oracle_quantize(const float* q, const float* k, const float* v,
+                     int B, int Hq, int Hkv, int N, int d, int bq, int bk, int smooth,
+                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                     float* k_mean, uint8_t* v_fp8, float* v_scale) {
+    oracle_quantize_q(q, B, Hq, N, d, bq, q_i8, q_scale);
+    oracle_quantize_kv(k, v, B, Hkv, N, d, bk, smooth, k_i8, k_scale, k_mean, v_fp8, v_scale);
+}
+
 /* ------------------------------------------------- quantised attention */
 
 /*
- * Quantised attention for a list of query rows (flattened (b*Hq + h)*N + i;
- * rows == NULL means every row).  For each row, with g = h / (Hq/Hkv) and the
- * allowed keys j <= i (causal) or all j < N:
+ * Quantised attention of Nq query rows per head against Nk keys, for a list of
+ * query rows (flattened (b*Hq + h)*Nq + i; rows == NULL means every row).
+ * Query row i sits at key position i + Nk - Nq (the last Nq positions of the
+ * sequence: Nq = Nk is self-attention, Nq < Nk a short query against a longer
+ * KV cache).  For each row, with g = h / (Hq/Hkv) and the allowed keys
+ * j <= i + Nk - Nq (causal) or all j < Nk:
  *
  *   acc_j = sum_c q_i8[i,c] * k_i8[j,c]                       (exact integer)
  *   c_j   = f32( f32(sq * sk[j/bk]) * f32(sm_scale*log2 e) )   (float32)
@@ -275,12 +292,13 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  */
 void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                    const float* k_scale, const void* v_codes, const float* v_scale, int pv_f16,
-                   int B, int Hq, int Hkv, int N, int d, int bq, int bk, int bn, int causal,
-                   float sm_scale, double tau, const int64_t* rows, long nrows,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int bq, int bk, int bn,
+                   int causal, float sm_scale, double tau, const int64_t* rows, long nrows,
                    double* out, double* out_lo, double* out_hi, int64_t* flagged) {
-    const long nd = (long)N * d;
+    const long qnd = (long)Nq * d, nd = (long)Nk * d;
+    const int N = Nk; /* keys */
     const int G = Hq / Hkv;
-    const int nqb = (N + bq - 1) / bq, nkb = (N + bk - 1) / bk;
+    const int nqb = (Nq + bq - 1) / bq, nkb = (N + bk - 1) / bk;
     const float qk = (float)((double)sm_scale * 1.4426950408889634); /* log2(e) */
     /* the P block scale: the block maximum maps to 448 (E4M3) or to 1 (binary16) */
     const float l448 = pv_f16 ? 0.0f : (float)log2(448.0);
@@ -294,7 +312,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
         dec[i] = pv_f16 ? oracle_f16_decode((uint16_t)i) : oracle_e4m3_decode((uint8_t)i);
     const uint8_t* v8 = (const uint8_t*)v_codes;
     const uint16_t* v16 = (const uint16_t*)v_codes;
-    if (rows == NULL) nrows = (long)B * Hq * N;
+    if (rows == NULL) nrows = (long)B * Hq * Nq;
 
 #pragma omp parallel
     {
@@ -310,17 +328,18 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
 #pragma omp for schedule(dynamic, 1)
         for (long ri = 0; ri < nrows; ++ri) {
             long row = rows ? (long)rows[ri] : ri;
-            long bh = row / N;
-            int i = (int)(row % N);
+            long bh = row / Nq;
+            int i = (int)(row % Nq);
             int b = (int)(bh / Hq), h = (int)(bh % Hq);
             int g = h / G;
-            const int8_t* qrow = q_i8 + bh * nd + (long)i * d;
+            const int8_t* qrow = q_i8 + bh * qnd + (long)i * d;
             const int8_t* kh = k_i8 + ((long)b * Hkv + g) * nd;
             const long vhead = ((long)b * Hkv + g) * nd;
             const float* svh = v_scale ? v_scale + ((long)b * Hkv + g) * d : NULL;
             const float sq = q_scale[bh * nqb + i / bq];
             const float* skh = k_scale + ((long)b * Hkv + g) * nkb;
-            int jmax = causal ? i : N - 1;
+            /* causal needs Nq <= Nk, so that every row keeps key 0 */
+            int jmax = causal ? i + (Nk - Nq) : N - 1;
             int nt = jmax / bn + 1;
 
             /* scores */
@@ -426,29 +445,31 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
 
 /*
  * softmax(Q K^T * sm_scale) V in float64 for a list of rows (same row
- * indexing as oracle_attn_q), with the causal mask j <= i when asked.
- * Inputs are float64 [B,H,N,d].
+ * indexing as oracle_attn_q: Nq query rows at the last Nq of Nk positions),
+ * with the causal mask j <= i + Nk - Nq when asked.  Inputs are float64,
+ * q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d].
  */
 void oracle_attn_f64(const double* q, const double* k, const double* v, int B, int Hq,
-                     int Hkv, int N, int d, int causal, double sm_scale,
+                     int Hkv, int Nq, int Nk, int d, int causal, double sm_scale,
                      const int64_t* rows, long nrows, double* out) {
-    const long nd = (long)N * d;
+    const long qnd = (long)Nq * d, nd = (long)Nk * d;
+    const int N = Nk;
     const int G = Hq / Hkv;
-    if (rows == NULL) nrows = (long)B * Hq * N;
+    if (rows == NULL) nrows = (long)B * Hq * Nq;
 #pragma omp parallel
     {
         double* s = (double*)malloc(sizeof(double) * (size_t)N);
 #pragma omp for schedule(dynamic, 1)
         for (long ri = 0; ri < nrows; ++ri) {
             long row = rows ? (long)rows[ri] : ri;
-            long bh = row / N;
-            int i = (int)(row % N);
+            long bh = row / Nq;
+            int i = (int)(row % Nq);
             int b = (int)(bh / Hq), h = (int)(bh % Hq);
             int g = h / G;
-            const double* qr = q + bh * nd + (long)i * d;
+            const double* qr = q + bh * qnd + (long)i * d;
             const double* kh = k + ((long)b * Hkv + g) * nd;
             const double* vh = v + ((long)b * Hkv + g) * nd;
-            int jmax = causal ? i : N - 1;
+            int jmax = causal ? i + (Nk - Nq) : N - 1;
             double m = -INFINITY;
             for (int j = 0; j <= jmax; ++j) {
                 double t = 0.0;

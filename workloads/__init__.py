@@ -39,17 +39,28 @@ class Workload:
     dtype: str          # "f16" or "bf16"
     causal: bool
     recipe: int         # which distribution recipe (1..5)
+    Nq: int = 0         # query rows per head against N keys (0: N, self-attention)
 
     @property
     def sm_scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     @property
+    def q_rows(self) -> int:
+        """Query rows per head (N for self-attention)."""
+        return self.Nq if self.Nq else self.N
+
+    @property
     def ops(self) -> float:
-        """Algorithmic operation count of the two contractions, 4*B*Hq*N^2*d,
-        halved for causal attention."""
-        o = 4.0 * self.B * self.Hq * self.N * self.N * self.d
-        return o / 2 if self.causal else o
+        """Algorithmic operation count of the two contractions: 4*d per allowed
+        (query, key) pair, i.e. 4*B*Hq*N^2*d halved for causal self-attention.
+        Query row i of a short query sits at position N - Nq + i."""
+        if not self.Nq:
+            o = 4.0 * self.B * self.Hq * self.N * self.N * self.d
+            return o / 2 if self.causal else o
+        nq, nk = self.Nq, self.N
+        pairs = nq * nk - nq * (nq - 1) / 2 if self.causal else nq * nk
+        return 4.0 * self.B * self.Hq * pairs * self.d
 
     def resized(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -61,6 +72,16 @@ WORKLOADS = {
     3: Workload(3, "video_diffusion_b2_h30_n17550_d64_f16", 2, 30, 30, 17550, 64, "f16", False, 3),
     4: Workload(4, "long_context_gqa_causal_b1_hq32_hkv8_n32768_d128_bf16", 1, 32, 8, 32768, 128, "bf16", True, 4),
     5: Workload(5, "image_gen_heavy_tail_b8_h24_n4096_d64_f16", 8, 24, 24, 4096, 64, "f16", False, 5),
+}
+
+
+# Short queries against a long KV cache (decode): N is the number of cached
+# keys, Nq the query rows per head (at the last Nq positions).
+DECODE_WORKLOADS = {
+    6: Workload(6, "long_context_gqa_decode_b1_hq32_hkv8_nq1_nk32768_d128_bf16", 1, 32, 8, 32768, 128,
+                "bf16", True, 4, Nq=1),
+    7: Workload(7, "llm_decode_gqa_b8_hq32_hkv8_nq1_nk8192_d128_bf16", 8, 32, 8, 8192, 128, "bf16",
+                True, 2, Nq=1),
 }
 
 
@@ -96,12 +117,13 @@ def _t3(rng, shape):
 
 def generate(w: Workload, seed: int | None = None):
     """Return (q, k, v) as contiguous CPU torch tensors of the workload dtype,
-    laid out [B, H, N, d]."""
+    laid out [B, H, rows, d]: q has w.q_rows rows per head, k and v w.N."""
     if seed is None:
         seed = SEED_BASE + w.index
     rng = np.random.Generator(np.random.PCG64(seed))
     B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
-    qs, ks = (B, Hq, N, d), (B, Hkv, N, d)
+    Nq = w.q_rows
+    qs, ks = (B, Hq, Nq, d), (B, Hkv, N, d)
     r = w.recipe
     if r == 1:
         q = rng.standard_normal(qs, dtype=np.float32)
@@ -110,7 +132,7 @@ def generate(w: Workload, seed: int | None = None):
         v = rng.standard_normal(ks, dtype=np.float32)
     elif r == 2:
         q = rng.standard_normal(qs, dtype=np.float32)
-        q *= rng.lognormal(0.0, 0.5, size=(B, Hq, N, 1)).astype(np.float32)
+        q *= rng.lognormal(0.0, 0.5, size=(B, Hq, Nq, 1)).astype(np.float32)
         k = rng.standard_normal(ks, dtype=np.float32)
         k += _bias_all_plus_outliers(rng, B, Hkv, d)
         v = rng.standard_normal(ks, dtype=np.float32)
@@ -122,10 +144,10 @@ def generate(w: Workload, seed: int | None = None):
         v *= rng.lognormal(0.0, 1.0, size=(B, Hkv, 1, d)).astype(np.float32)
     elif r == 4:
         q = rng.standard_normal(qs, dtype=np.float32)
-        n_hot = int(round(0.01 * N))
+        n_hot = int(round(0.01 * Nq))
         for b in range(B):
             for h in range(Hq):
-                rows = rng.choice(N, size=n_hot, replace=False)
+                rows = rng.choice(Nq, size=n_hot, replace=False)
                 q[b, h, rows, :] *= 20.0
         k = rng.standard_normal(ks, dtype=np.float32)
         k += _bias_all_plus_outliers(rng, B, Hkv, d)
@@ -156,13 +178,15 @@ def random_inputs(B, Hq, Hkv, N, d, dtype="f16", seed=0, scale=1.0):
 
 
 def sample_rows(w: Workload, count: int, seed: int = 7):
-    """A deterministic sample of flattened query-row indices (b*Hq + h)*N + i,
+    """A deterministic sample of flattened query-row indices (b*Hq + h)*rows + i
+    (rows = w.q_rows),
     always including the first and last row of every head touched and, for
     recipe 4, some of the x20 rows (found by the caller from the data)."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    total = w.B * w.Hq * w.N
+    n = w.q_rows
+    total = w.B * w.Hq * n
     rows = set(int(x) for x in rng.choice(total, size=min(count, total), replace=False))
     for bh in (0, w.B * w.Hq - 1):
-        rows.add(bh * w.N)
-        rows.add(bh * w.N + w.N - 1)
+        rows.add(bh * n)
+        rows.add(bh * n + n - 1)
     return np.array(sorted(rows), dtype=np.int64)
