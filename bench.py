@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--prep-flush", action="store_true",
                    help="also time the prep step alone with a 512 MB write between launches, so the "
                         "last-level cache holds none of its inputs")
+    p.add_argument("--decode", type=int, default=0, metavar="WORKLOAD",
+                   help="instead of the default line, time the short-query path over a quantized KV "
+                        "cache on decode workload 6 or 7 (one JSON line of its own, HBM-bound)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="instead of the benchmark, run a plain device-to-device copy of BYTES "
                         "bytes 5 times: a known-size reference for hardware byte counters")
@@ -156,6 +159,84 @@ def cpu_baseline(w, q, k, v, rows_wanted, bq, bk, pv):
                       f"(prep {t_prep:.2f} s, attention {t_attn:.2f} s)"}
 
 
+def decode_bytes(w, k_block):
+    """Bytes one short-query launch must move with this cache format: INT8 K
+    (1 B), binary16 V (2 B) and the K scales of the cache; the query in and
+    the FP32 output."""
+    kv = w.B * w.Hkv * w.N * w.d
+    return (3 * kv + w.B * w.Hkv * (-(-w.N // k_block)) * 4 + w.B * w.Hkv * w.d * 4
+            + w.B * w.Hq * w.q_rows * w.d * (2 + 4))
+
+
+def cpu_baseline_decode(w, q, k, v, bk, pv):
+    """The oracle's short-query attention over every query row, its K/V
+    quantization not counted (the cache is built once)."""
+    import oracle
+
+    oracle.build()
+    z = oracle.quantize_q(q, bq=1)
+    z.update(oracle.quantize_kv(k, v, bk=bk, pv=pv))
+    t0 = time.perf_counter()
+    oracle.attn_q(z, w.causal, w.sm_scale, interval=False)
+    first = time.perf_counter() - t0
+    # repeat the whole pass for about 10 s of CPU work
+    reps = max(1, min(5000, int(10.0 / max(first, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.attn_q(z, w.causal, w.sm_scale, interval=False)
+    t = (time.perf_counter() - t0) / reps
+    return {"value": decode_bytes(w, bk) / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"all {w.B * w.Hq * w.q_rows} query rows of the workload, "
+                                        f"{reps} passes, {t * 1e3:.2f} ms each (the cache "
+                                        f"quantization is not timed)"}
+
+
+def bench_decode(args, sage, workloads, torch):
+    w = workloads.DECODE_WORKLOADS[args.decode]
+    q, k, v = workloads.generate(w)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    cache = sage.KVCache(kd, vd, granularity=args.granularity, pv=args.pv)
+    nbytes = sage.sage_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.q_rows, w.N, w.d)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+
+    def step():
+        sage.sage_attn_decode(qd, cache.z, out, w.Hkv, w.N, w.causal, w.sm_scale, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = timed(step, args.steps, torch)
+    wall = time.perf_counter() - t0
+    ms_cache = timed(lambda: sage.sage_kv_quantize(kd, vd, cache.z), max(3, args.steps // 10), torch)
+    kb = cache.z.k_block
+    nb = decode_bytes(w, kb)
+    gbs = nb / (ms * 1e-3) / 1e9
+    fp16_kv = 2 * 2 * w.B * w.Hkv * w.N * w.d
+    line = {
+        "metric": "short-query attention over a quantized KV cache, GB/s of cache read (1 GPU)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": f"i8 (QK^T, i32 acc) + {args.pv} values (P.V, f32 acc)", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.q_rows, "Nk": w.N,
+                   "d": w.d, "causal": w.causal, "input_dtype": w.dtype, "k_block": kb,
+                   "pv_format": args.pv, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_decode (+ decode_merge)", "bytes_per_launch": nb},
+        "cache": {"bytes": int(cache.buf.numel()), "fp16_kv_bytes": fp16_kv,
+                  "ratio": round(cache.buf.numel() / fp16_kv, 4),
+                  "quantize_ms": round(ms_cache, 4)},
+        "tops": round(w.ops / (ms * 1e-3) / 1e12, 2),
+        "timed_wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_decode(w, q, k, v, kb, args.pv)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -167,6 +248,9 @@ def main():
     import bit_quantized_attention_02_amd as sage
     import workloads
 
+    if args.decode:
+        bench_decode(args, sage, workloads, torch)
+        return
     if args.copy_probe:
         src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -61,6 +61,14 @@ _lib.sage_attn_fwd_granular.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, 
                                         _S, _P]
 _lib.sage_attn_fwd_ex.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                   ctypes.POINTER(sage_options), _P, _S, _P]
+_lib.sage_kv_cache_bytes.restype = _S
+_lib.sage_kv_cache_bytes.argtypes = [_I, _I, _I, _I]
+_lib.sage_kv_cache_carve.argtypes = [_P, _S, _I, _I, _I, _I, ctypes.POINTER(sage_qkv_quant)]
+_lib.sage_kv_quantize.argtypes = [_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(sage_qkv_quant), _P]
+_lib.sage_decode_workspace_bytes.restype = _S
+_lib.sage_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+_lib.sage_attn_decode.argtypes = [_P, _I, ctypes.POINTER(sage_qkv_quant), _P, _I, _I, _I, _I, _I, _I,
+                                  _I, _F, _P, _S, _P]
 _lib.sage_get_config.argtypes = [ctypes.POINTER(sage_config)]
 _lib.sage_v_key_position.argtypes = [_I]
 _lib.sage_status_string.restype = ctypes.c_char_p
@@ -68,7 +76,8 @@ _lib.sage_status_string.argtypes = [_I]
 
 EXPORTED = ["sage_workspace_bytes", "sage_workspace_carve", "sage_quantize",
             "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_attn_fwd_granular", "sage_attn_fwd_ex",
-            "sage_get_config",
+            "sage_kv_cache_bytes", "sage_kv_cache_carve", "sage_kv_quantize",
+            "sage_decode_workspace_bytes", "sage_attn_decode", "sage_get_config",
             "sage_v_key_position", "sage_status_string"]
 
 
@@ -179,6 +188,40 @@ def sage_attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def sage_kv_cache_bytes(B: int, Hkv: int, Nk: int, d: int) -> int:
+    return int(_lib.sage_kv_cache_bytes(B, Hkv, Nk, d))
+
+
+def sage_kv_cache_carve(buf: torch.Tensor | int | None, nbytes: int, B: int, Hkv: int, Nk: int,
+                        d: int, granularity: str = "block", pv: str = "e4m3") -> sage_qkv_quant:
+    """The C call, then k_block and pv_format set to the chosen K granularity
+    ("block": 64 keys per scale, "thread": 32) and P.V format."""
+    z = sage_qkv_quant()
+    ptr = buf.data_ptr() if isinstance(buf, torch.Tensor) else buf
+    _check(_lib.sage_kv_cache_carve(ptr, nbytes, B, Hkv, Nk, d, ctypes.byref(z)))
+    z.k_block = GRANULARITY[granularity][1]
+    z.pv_format = PV_FORMAT[pv]
+    return z
+
+
+def sage_kv_quantize(k: torch.Tensor, v: torch.Tensor, cache: sage_qkv_quant, stream=None) -> None:
+    B, Hkv, Nk, d = k.shape
+    _check(_lib.sage_kv_quantize(_ptr(k), _ptr(v), _dtype_code(k), B, Hkv, Nk, d, ctypes.byref(cache),
+                                 _stream(stream)))
+
+
+def sage_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(_lib.sage_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
+
+
+def sage_attn_decode(q: torch.Tensor, cache: sage_qkv_quant, out: torch.Tensor, Hkv: int, Nk: int,
+                     causal: bool, sm_scale: float, workspace: torch.Tensor, stream=None) -> None:
+    B, Hq, Nq, d = q.shape
+    _check(_lib.sage_attn_decode(_ptr(q), _dtype_code(q), ctypes.byref(cache), _ptr(out), B, Hq, Hkv,
+                                 Nq, Nk, d, int(causal), float(sm_scale), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 # ------------------------------------------------------------------ helpers
 
 def options(granularity: str = "block", pv: str = "e4m3") -> sage_options:
@@ -215,6 +258,43 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     return out
 
 
+class KVCache:
+    """A quantized KV cache in torch-owned device memory: the K/V half of the
+    prep step over [B, Hkv, Nk, d] fp16/bf16 K and V, quantized once."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, granularity: str = "block",
+                 pv: str = "e4m3", stream=None):
+        for t in (k, v):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("K, V must be contiguous device tensors")
+        self.B, self.Hkv, self.Nk, self.d = k.shape
+        nbytes = sage_kv_cache_bytes(self.B, self.Hkv, self.Nk, self.d)
+        if nbytes == 0:
+            raise SageError(SAGE_ERR_UNSUPPORTED)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+        self.z = sage_kv_cache_carve(self.buf, nbytes, self.B, self.Hkv, self.Nk, self.d,
+                                     granularity, pv)
+        sage_kv_quantize(k, v, self.z, stream)
+
+    def attend(self, q: torch.Tensor, causal: bool = True, sm_scale: float | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """softmax(Q K^T sm_scale) V for q [B, Hq, Nq, d] at the last Nq of the
+        Nk positions -> FP32 [B, Hq, Nq, d]."""
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(q.shape[-1])
+        if not q.is_cuda or not q.is_contiguous():
+            raise ValueError("Q must be a contiguous device tensor")
+        B, Hq, Nq, d = q.shape
+        if workspace is None:
+            nbytes = sage_decode_workspace_bytes(B, Hq, self.Hkv, Nq, self.Nk, d)
+            if nbytes == 0:
+                raise SageError(SAGE_ERR_UNSUPPORTED)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        sage_attn_decode(q, self.z, out, self.Hkv, self.Nk, causal, sm_scale, workspace, stream)
+        return out
+
+
 def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, Hkv: int,
                    N: int, d: int) -> dict:
     """Copy the quantized operands out of `workspace` (carved into `z`) to host
@@ -222,7 +302,7 @@ def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, 
     comes back as its binary16 values (v_half) and as codes: E4M3 codes
     (v_fp8; the binary16 values convert back exactly) or, for the binary16
     P.V format, the binary16 bit patterns (v_f16).  Layout only; `*_pad` hold
-    rows N..N_p-1."""
+    rows N..N_p-1.  For a KV cache (no Q fields) the Q entries are left out."""
     Np = -(-N // SAGE_NPAD) * SAGE_NPAD
     base = workspace.data_ptr()
     torch.cuda.synchronize()
@@ -235,7 +315,6 @@ def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, 
         off = addr - base
         return workspace[off:off + nbytes].cpu().view(dtype).reshape(shape)
 
-    q_full = host(z.q_i8, (B, Hq, Np, d), torch.int8)
     k_full = host(z.k_i8, (B, Hkv, Np, d), torch.int8)
     vb = host(z.v16, (B, Hkv, Np // SAGE_BN, d, SAGE_BN), torch.float16)
     perm = torch.tensor([sage_v_key_position(j) for j in range(SAGE_BN)], dtype=torch.long)
@@ -244,12 +323,14 @@ def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, 
         v_codes = dict(v_f16=v_half.view(torch.int16)[:, :, :N].contiguous())
     else:
         v_codes = dict(v_fp8=v_half.to(torch.float8_e4m3fn).view(torch.uint8)[:, :, :N].contiguous())
-    return dict(
-        **v_codes, q_i8=q_full[:, :, :N].contiguous(), k_i8=k_full[:, :, :N].contiguous(),
-        v_half=v_half[:, :, :N].contiguous(),
-        q_pad=q_full[:, :, N:].contiguous(), k_pad=k_full[:, :, N:].contiguous(),
-        v_pad=v_half[:, :, N:].contiguous(),
-        q_scale=host(z.q_scale, (B, Hq, Np // z.q_block), torch.float32),
+    r = dict(
+        **v_codes, k_i8=k_full[:, :, :N].contiguous(), v_half=v_half[:, :, :N].contiguous(),
+        k_pad=k_full[:, :, N:].contiguous(), v_pad=v_half[:, :, N:].contiguous(),
         k_scale=host(z.k_scale, (B, Hkv, Np // z.k_block), torch.float32),
         k_mean=host(z.k_mean, (B, Hkv, d), torch.float32),
         v_scale=host(z.v_scale, (B, Hkv, d), torch.float32))
+    if z.q_i8 is not None:
+        q_full = host(z.q_i8, (B, Hq, Np, d), torch.int8)
+        r.update(q_i8=q_full[:, :, :N].contiguous(), q_pad=q_full[:, :, N:].contiguous(),
+                 q_scale=host(z.q_scale, (B, Hq, Np // z.q_block), torch.float32))
+    return r

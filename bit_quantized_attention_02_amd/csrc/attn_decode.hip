@@ -1,0 +1,328 @@
+// Short-query attention over a quantized KV cache (decode) for CDNA4 (gfx950).
+//
+// The cache holds the K/V half of the prep step (smoothed INT8 K with its
+// scales, V as binary16 in the P.V format's values), quantized once.  A short
+// query -- Nq rows per q head, sitting at the last Nq of the Nk positions --
+// attends to it with the same per-block computation as the prefill kernel
+// (attn_block.h).  The query rows are quantized here, one INT8 scale per row.
+//
+// Work decomposition (flash-decoding): one work-group is one wave, and owns 32
+// packed query rows of one (batch, kv head) -- the G q heads that share the kv
+// head times the Nq rows, so K and V are read once for all of them -- and one
+// chunk of consecutive key blocks.  Each chunk leaves its (reference max, row
+// sum, unnormalised O) per row; decode_merge combines the chunks of a row with
+// weights 2^(reference max - overall max), a third accumulation level in FP32
+// over the two of the block computation.  With a single chunk the kernel
+// writes the output itself.
+#include "attn_block.h"
+
+namespace sage {
+
+struct DecodeArgs {
+    const uint16_t* q;      // [B, Hq, Nq, d], fp16 or bf16 bits
+    const int8_t* k_i8;     // cache, [B, Hkv, Np, d]
+    const float* k_scale;   // [B, Hkv, Np / k_block]
+    const uint16_t* v16;    // [B, Hkv, Np / SAGE_BN, d, SAGE_BN]
+    const float* v_scale;   // [B, Hkv, d]
+    float* out;             // [B, Hq, Nq, d]
+    float* part_o;          // [B * Hq * Nq, nchunk, d]
+    float* part_ml;         // [B * Hq * Nq, nchunk, 2]: reference max, row sum
+    int B, Hq, Hkv, Nq, Nk, Np, G;
+    int rows_per_head;      // G * Nq packed rows per kv head
+    int row_tiles;          // ceil(rows_per_head / 32)
+    int nchunk, chunk_blocks;
+    float qk, l448;
+};
+
+// INT8 codes of one query row, quantized with one scale for the row.  Lane
+// (r32, h) holds elements [32 ks + 16 h, +16) of its row for each ks, i.e.
+// exactly the bytes of its Q.K^T operand; the two lanes of a row agree on the
+// row's absmax through one permlane32 swap.  The codes and the scale use the
+// float32 operations of the prep step: scale = absmax / 127, codes
+// rne(x * (127 / absmax)) clamped to +-127.
+template <typename In, int D>
+__device__ inline float quantize_q_row(const uint16_t* __restrict__ qrow, bool valid, int h,
+                                       v4i (&qf)[D / 32]) {
+    constexpr int KS = D / 32;
+    float x[KS][16];
+    float am = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float f[8];
+            if (valid) {
+                const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 16 * h + 8 * half);
+                unpack8<In>(u, f);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[ks][8 * half + e] = f[e];
+                am = fmaxf(am, fabsf(f[e]));
+            }
+        }
+    }
+    // non-negative floats order like their bit patterns
+    am = __builtin_bit_cast(float, max_across_halves(__builtin_bit_cast(int, am)));
+    const float inv = am > 0.0f ? 127.0f / am : 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        int w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float r = __builtin_rintf(x[ks][e] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            w[e >> 2] |= ((int)(uint8_t)(int8_t)(int)r) << (8 * (e & 3));
+        }
+        const v4i c = {w[0], w[1], w[2], w[3]};
+        qf[ks] = c;
+    }
+    return am / 127.0f;
+}
+
+template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
+__global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
+    constexpr int CT = D / 32;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t* const lk0 = smem;
+    uint8_t* const lk1 = smem + SAGE_BN * D;
+    uint16_t* const lv0 = reinterpret_cast<uint16_t*>(smem + 2 * SAGE_BN * D);
+    uint16_t* const lv1 = lv0 + D * SAGE_BN;
+
+    const int lane = threadIdx.x;
+    const int h = lane >> 5, r32 = lane & 31;
+    const v8h rsel = row_sum_selector(lane);
+
+    // work-group -> (batch and kv head, chunk, row tile); row tiles of one
+    // chunk are neighbours so they meet the same K/V tiles in the cache
+    int idx = blockIdx.x;
+    const int rt = idx % a.row_tiles;
+    idx /= a.row_tiles;
+    const int chunk = idx % a.nchunk;
+    const int bg = idx / a.nchunk;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+
+    // this lane's packed row: q head g*G + p / Nq, query row i = p % Nq
+    const int p = rt * 32 + r32;
+    const bool valid = p < a.rows_per_head;
+    const int hq = g * a.G + (valid ? p / a.Nq : 0);
+    const int i = valid ? p % a.Nq : 0;
+    const long long grow = ((long long)b * a.Hq + hq) * a.Nq + i;  // row of out
+    // the row's last allowed key (causal: bottom-right aligned)
+    const int pos = CAUSAL && valid ? a.Nk - a.Nq + i : a.Nk - 1;
+
+    v4i qf[D / 32];
+    const float sq = quantize_q_row<In, D>(a.q + grow * D, valid, h, qf);
+
+    const int nkb = (a.Nk + SAGE_BN - 1) / SAGE_BN;
+    const int T0 = chunk * a.chunk_blocks;
+    const int T1 = min(nkb, T0 + a.chunk_blocks);
+    // blocks below this need no mask for any lane: no padding keys and no key
+    // past the smallest causal limit (Nk - Nq)
+    const int first_masked = CAUSAL ? min(a.Nk / SAGE_BN, (a.Nk - a.Nq + 1) / SAGE_BN) : a.Nk / SAGE_BN;
+
+    const uint8_t* kbase = (const uint8_t*)a.k_i8 + (long long)bg * a.Np * D;
+    const uint16_t* vbase = a.v16 + (long long)bg * a.Np * D;
+    const float* ksc = a.k_scale + (long long)bg * (a.Np / (SAGE_BN / KSPLIT));
+
+    v16f O[CT];
+    float mref = -INFINITY, lsum = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) O[ct][v] = 0.0f;
+
+    typedef float kvec __attribute__((ext_vector_type(KSPLIT)));
+    kvec kscale = *reinterpret_cast<const kvec*>(ksc + KSPLIT * T0);
+    const TileLoader<D, 1> tiles(kbase, vbase, a.Np, 0, lane);
+    tiles.load(T0, lk0, lv0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int T = T0; T < T1; ++T) {
+        const bool odd = (T - T0) & 1;
+        const bool more = T + 1 < T1;
+        // the next block's K scales before its tile copy (waits count in
+        // issue order)
+        const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
+        if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, 0);
+        float c[KSPLIT];
+#pragma unroll
+        for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * kscale[gg]) * a.qk;
+        if (T < first_masked)
+            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
+                                                       a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
+        else
+            attn_block<D, KSPLIT, CAUSAL, PV16, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
+                                                      a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
+        kscale = knext;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    if (!valid) return;
+    // O[ct][v] is channel 32ct + 8(v/4) + 4h + v%4
+    if (a.nchunk == 1) {
+        const float* sv = a.v_scale + (long long)bg * D;
+        const float inv_l = 1.0f / lsum;
+        float* op = a.out + grow * D;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const int ch = 32 * ct + 8 * k4 + 4 * h;
+                const float4 s4 = *reinterpret_cast<const float4*>(sv + ch);
+                float4 o;
+                o.x = O[ct][4 * k4 + 0] * s4.x * inv_l;
+                o.y = O[ct][4 * k4 + 1] * s4.y * inv_l;
+                o.z = O[ct][4 * k4 + 2] * s4.z * inv_l;
+                o.w = O[ct][4 * k4 + 3] * s4.w * inv_l;
+                *reinterpret_cast<float4*>(op + ch) = o;
+            }
+        return;
+    }
+    const long long part = grow * a.nchunk + chunk;
+    float* po = a.part_o + part * D;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const int ch = 32 * ct + 8 * k4 + 4 * h;
+            const float4 o = {O[ct][4 * k4 + 0], O[ct][4 * k4 + 1], O[ct][4 * k4 + 2], O[ct][4 * k4 + 3]};
+            *reinterpret_cast<float4*>(po + ch) = o;
+        }
+    if (h == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(mref, lsum);
+}
+
+// One work-group per query row, one thread per channel: out = O * s_V / l
+// over the row's chunks, each weighted by 2^(its reference max - the largest).
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
+    const long long row = blockIdx.x;  // (b * Hq + hq) * Nq + i
+    const int c = threadIdx.x;
+    const int hq = (int)((row / a.Nq) % a.Hq), b = (int)(row / ((long long)a.Nq * a.Hq));
+    const int bg = b * a.Hkv + hq / a.G;
+    const float* ml = a.part_ml + row * a.nchunk * 2;
+    float M = -INFINITY;
+    for (int k = 0; k < a.nchunk; ++k) M = fmaxf(M, ml[2 * k]);
+    float o = 0.0f, l = 0.0f;
+    for (int k = 0; k < a.nchunk; ++k) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * k] - M);  // 0 for an empty chunk
+        o = __builtin_fmaf(a.part_o[(row * a.nchunk + k) * D + c], w, o);
+        l = __builtin_fmaf(ml[2 * k + 1], w, l);
+    }
+    a.out[row * D + c] = o * a.v_scale[(long long)bg * D + c] * (1.0f / l);
+}
+
+#define SAGE_DECODE_INST(In, D, KSPLIT, CAUSAL, PV16) \
+    template __global__ void attn_decode<In, D, KSPLIT, CAUSAL, PV16>(DecodeArgs);
+#define SAGE_DECODE_INST_PV(In, D, KSPLIT, CAUSAL) \
+    SAGE_DECODE_INST(In, D, KSPLIT, CAUSAL, false) SAGE_DECODE_INST(In, D, KSPLIT, CAUSAL, true)
+#define SAGE_DECODE_INST_C(In, D, KSPLIT) \
+    SAGE_DECODE_INST_PV(In, D, KSPLIT, false) SAGE_DECODE_INST_PV(In, D, KSPLIT, true)
+#define SAGE_DECODE_INST_K(In, D) SAGE_DECODE_INST_C(In, D, 2) SAGE_DECODE_INST_C(In, D, 4)
+SAGE_DECODE_INST_K(_Float16, 64)
+SAGE_DECODE_INST_K(_Float16, 128)
+SAGE_DECODE_INST_K(Bf16Tag, 64)
+SAGE_DECODE_INST_K(Bf16Tag, 128)
+#undef SAGE_DECODE_INST_K
+#undef SAGE_DECODE_INST_C
+#undef SAGE_DECODE_INST_PV
+#undef SAGE_DECODE_INST
+template __global__ void decode_merge<64>(DecodeArgs);
+template __global__ void decode_merge<128>(DecodeArgs);
+
+// Chunking: enough work-groups to keep every CU streaming the cache (three
+// one-wave work-groups fit a CU's LDS at d = 64, one at d = 128), in chunks of
+// at least kMinChunkBlocks blocks so that filling each work-group's two-tile
+// pipeline stays a small part of its work.
+constexpr int kMinChunkBlocks = 4;
+
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    DecodePlan pl;
+    const int G = Hq / Hkv;
+    pl.row_tiles = (G * Nq + 31) / 32;
+    const int nkb = (Nk + SAGE_BN - 1) / SAGE_BN;
+    const long long units = (long long)B * Hkv * pl.row_tiles;
+    const long long target = 2LL * 256 * (d == 64 ? 3 : 1);
+    long long want = (target + units - 1) / units;
+    int per = (int)((nkb + want - 1) / want);
+    if (per < kMinChunkBlocks) per = kMinChunkBlocks;
+    if (per > nkb) per = nkb;
+    pl.chunk_blocks = per;
+    pl.nchunk = (nkb + per - 1) / per;
+    return pl;
+}
+
+template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+    constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)attn_decode<In, D, KSPLIT, CAUSAL, PV16>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const long long grid = (long long)a.B * a.Hkv * a.nchunk * a.row_tiles;
+    hipLaunchKernelGGL((attn_decode<In, D, KSPLIT, CAUSAL, PV16>), dim3((unsigned)grid), dim3(64), lds,
+                       st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nchunk == 1) return e;
+    hipLaunchKernelGGL((decode_merge<D>), dim3((unsigned)((long long)a.B * a.Hq * a.Nq)), dim3(D), 0,
+                       st, a);
+    return hipGetLastError();
+}
+
+template <typename In, int D, int KSPLIT>
+static hipError_t launch_decode_k(const DecodeArgs& a, int causal, bool pv16, hipStream_t st) {
+    if (causal)
+        return pv16 ? launch_decode_t<In, D, KSPLIT, true, true>(a, st)
+                    : launch_decode_t<In, D, KSPLIT, true, false>(a, st);
+    return pv16 ? launch_decode_t<In, D, KSPLIT, false, true>(a, st)
+                : launch_decode_t<In, D, KSPLIT, false, false>(a, st);
+}
+
+template <typename In, int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, bool fine_k, int causal, bool pv16,
+                                  hipStream_t st) {
+    return fine_k ? launch_decode_k<In, D, 4>(a, causal, pv16, st)
+                  : launch_decode_k<In, D, 2>(a, causal, pv16, st);
+}
+
+hipError_t launch_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out,
+                         float* part_o, float* part_ml, int B, int Hq, int Hkv, int Nq, int Nk,
+                         int d, int causal, float qk, float l448, hipStream_t st) {
+    const DecodePlan pl = decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    DecodeArgs a;
+    a.q = (const uint16_t*)q;
+    a.k_i8 = cache->k_i8;
+    a.k_scale = cache->k_scale;
+    a.v16 = cache->v16;
+    a.v_scale = cache->v_scale;
+    a.out = out;
+    a.part_o = part_o;
+    a.part_ml = part_ml;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.Np = make_shape(B, Hq, Hkv, Nk, d).Np;
+    a.G = Hq / Hkv;
+    a.rows_per_head = a.G * Nq;
+    a.row_tiles = pl.row_tiles;
+    a.nchunk = pl.nchunk;
+    a.chunk_blocks = pl.chunk_blocks;
+    a.qk = qk;
+    a.l448 = l448;
+    const bool fine_k = cache->k_block == SAGE_BK_THREAD;
+    const bool pv16 = cache->pv_format == SAGE_PV_F16;
+    if (dtype == SAGE_F16)
+        return d == 64 ? launch_decode_d<_Float16, 64>(a, fine_k, causal, pv16, st)
+                       : launch_decode_d<_Float16, 128>(a, fine_k, causal, pv16, st);
+    return d == 64 ? launch_decode_d<Bf16Tag, 64>(a, fine_k, causal, pv16, st)
+                   : launch_decode_d<Bf16Tag, 128>(a, fine_k, causal, pv16, st);
+}
+
+}  // namespace sage

@@ -340,7 +340,30 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     store_v_tile<D>(vt, v16 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN), tid);
 }
 
+// Clears the arrival counters when the K/V half runs without prep_q (whose
+// extra work-group clears them otherwise).
+__global__ __launch_bounds__(kThreads) void clear_words(int* __restrict__ w, int n) {
+    for (int i = threadIdx.x; i < n; i += kThreads) w[i] = 0;
+}
+
 // ------------------------------------------------------------ launchers
+template <typename In, int D>
+static hipError_t launch_prep_kv_t(const void* k, const void* v, const Shape& s,
+                                   const sage_qkv_quant* z, hipStream_t st) {
+    const int nchunk = s.part_chunks();
+    const int pv16 = z->pv_format == SAGE_PV_F16;
+    hipLaunchKernelGGL((prep_stats<In, D>), dim3(s.B * s.Hkv * nchunk), dim3(kThreads), 0, st,
+                       (const uint16_t*)k, (const uint16_t*)v, s, z->k_part, z->v_part, z->sync,
+                       z->k_mean, z->v_scale, z->v_inv, pv16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int per_head = s.Np / 64 + s.Np / SAGE_BN;
+    hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
+                       (const uint16_t*)k, (const uint16_t*)v, s, (int)z->k_block, z->k_mean,
+                       z->v_inv, z->k_i8, z->k_scale, z->v16, pv16);
+    return hipGetLastError();
+}
+
 template <typename In, int D>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const Shape& s,
                                 const sage_qkv_quant* z, hipStream_t st) {
@@ -349,18 +372,7 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
                        (int)z->q_block, z->q_i8, z->q_scale, z->sync);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nchunk = s.part_chunks();
-    const int pv16 = z->pv_format == SAGE_PV_F16;
-    hipLaunchKernelGGL((prep_stats<In, D>), dim3(s.B * s.Hkv * nchunk), dim3(kThreads), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, s, z->k_part, z->v_part, z->sync,
-                       z->k_mean, z->v_scale, z->v_inv, pv16);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int per_head = s.Np / 64 + s.Np / SAGE_BN;
-    hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, s, (int)z->k_block, z->k_mean,
-                       z->v_inv, z->k_i8, z->k_scale, z->v16, pv16);
-    return hipGetLastError();
+    return launch_prep_kv_t<In, D>(k, v, s, z, st);
 }
 
 hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, const Shape& s,
@@ -370,6 +382,18 @@ hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, c
                          : launch_prep_t<_Float16, 128>(q, k, v, s, z, st);
     return s.d == 64 ? launch_prep_t<Bf16Tag, 64>(q, k, v, s, z, st)
                      : launch_prep_t<Bf16Tag, 128>(q, k, v, s, z, st);
+}
+
+hipError_t launch_prep_kv(const void* k, const void* v, int dtype, const Shape& s,
+                          const sage_qkv_quant* z, hipStream_t st) {
+    hipLaunchKernelGGL(clear_words, dim3(1), dim3(kThreads), 0, st, z->sync, sync_words(s));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (dtype == SAGE_F16)
+        return s.d == 64 ? launch_prep_kv_t<_Float16, 64>(k, v, s, z, st)
+                         : launch_prep_kv_t<_Float16, 128>(k, v, s, z, st);
+    return s.d == 64 ? launch_prep_kv_t<Bf16Tag, 64>(k, v, s, z, st)
+                     : launch_prep_kv_t<Bf16Tag, 128>(k, v, s, z, st);
 }
 
 int prep_sync_words(const Shape& s) { return sync_words(s); }

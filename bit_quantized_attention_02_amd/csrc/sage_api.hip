@@ -8,8 +8,13 @@
 namespace sage {
 hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, const Shape& s,
                        const sage_qkv_quant* z, hipStream_t st);
+hipError_t launch_prep_kv(const void* k, const void* v, int dtype, const Shape& s,
+                          const sage_qkv_quant* z, hipStream_t st);
 hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal, float qk,
                        float l448, hipStream_t st);
+hipError_t launch_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out,
+                         float* part_o, float* part_ml, int B, int Hq, int Hkv, int Nq, int Nk,
+                         int d, int causal, float qk, float l448, hipStream_t st);
 int prep_sync_words(const Shape& s);
 }  // namespace sage
 
@@ -31,12 +36,13 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace layout: each region starts on a 256-byte boundary.
+// Workspace layout: each region starts on a 256-byte boundary.  A KV cache
+// (with_q false) has no Q regions.
 struct Layout {
     size_t q_i8, q_scale, k_i8, k_scale, k_mean, v16, v_scale, v_inv, k_part, v_part, sync, total;
 };
 
-static Layout layout(const Shape& s) {
+static Layout layout(const Shape& s, bool with_q = true) {
     Layout L;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -45,11 +51,11 @@ static Layout layout(const Shape& s) {
         return o;
     };
     const size_t Bq = (size_t)s.B * s.Hq, Bkv = (size_t)s.B * s.Hkv;
-    L.q_i8 = take((size_t)s.q_elems());
+    L.q_i8 = with_q ? take((size_t)s.q_elems()) : 0;
     L.k_i8 = take((size_t)s.kv_elems());
     L.v16 = take((size_t)s.kv_elems() * sizeof(uint16_t));
     // scales sized for the finer of the two granularities
-    L.q_scale = take(Bq * (s.Np / SAGE_BQ_THREAD) * sizeof(float));
+    L.q_scale = with_q ? take(Bq * (s.Np / SAGE_BQ_THREAD) * sizeof(float)) : 0;
     L.k_scale = take(Bkv * (s.Np / SAGE_BK_THREAD) * sizeof(float));
     L.k_mean = take(Bkv * s.d * sizeof(float));
     L.v_scale = take(Bkv * s.d * sizeof(float));
@@ -67,6 +73,49 @@ static bool granularity_ok(int q_block, int k_block) {
 }
 
 static bool pv_format_ok(int f) { return f == SAGE_PV_E4M3 || f == SAGE_PV_F16; }
+
+// The K/V half of a sage_qkv_quant (all a KV cache has).
+static int check_cache(const sage_qkv_quant* z) {
+    if (!z) return SAGE_ERR_INVALID_ARG;
+    if ((z->k_block != SAGE_BK && z->k_block != SAGE_BK_THREAD) || !pv_format_ok(z->pv_format))
+        return SAGE_ERR_UNSUPPORTED;
+    if (!z->k_i8 || !z->k_scale || !z->k_mean || !z->v16 || !z->v_scale || !z->v_inv ||
+        !z->k_part || !z->v_part || !z->sync)
+        return SAGE_ERR_INVALID_ARG;
+    if (!aligned(z->k_i8, 16) || !aligned(z->v16, 16) || !aligned(z->k_scale, 16) ||
+        !aligned(z->v_scale, 16) || !aligned(z->k_part, 8))
+        return SAGE_ERR_INVALID_ARG;
+    return SAGE_OK;
+}
+
+// Shape of a short query (Nq rows per q head) against Nk cached keys.
+static int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (Nq < 1) return SAGE_ERR_INVALID_ARG;
+    int rc = check_shape(B, Hq, Hkv, Nk, d);
+    if (rc != SAGE_OK) return rc;
+    if (Nq > SAGE_MAX_N) return SAGE_ERR_UNSUPPORTED;
+    const sage::DecodePlan pl = sage::decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    if ((long long)B * Hkv * pl.nchunk * pl.row_tiles >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
+    if ((long long)B * Hq * Nq >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
+    return SAGE_OK;
+}
+
+// Decode workspace: the per-chunk partials, (rows x chunks x d) and
+// (rows x chunks x 2) floats; at least 256 bytes so that 0 means "invalid".
+struct DecodeLayout {
+    size_t part_o, part_ml, total;
+};
+
+static DecodeLayout decode_layout(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    const sage::DecodePlan pl = sage::decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    DecodeLayout L;
+    const size_t parts = pl.nchunk > 1 ? (size_t)B * Hq * Nq * pl.nchunk : 0;
+    L.part_o = 0;
+    L.part_ml = round256(parts * d * sizeof(float));
+    L.total = L.part_ml + round256(parts * 2 * sizeof(float));
+    if (L.total < 256) L.total = 256;
+    return L;
+}
 
 static int check_quant(const sage_qkv_quant* z) {
     if (!z) return SAGE_ERR_INVALID_ARG;
@@ -186,6 +235,77 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
                   size_t ws_bytes, void* stream) {
     return sage_attn_fwd_granular(q, k, v, out, B, Hq, Hkv, N, d, causal, sm_scale, dtype, SAGE_BQ,
                                   SAGE_BK, workspace, ws_bytes, stream);
+}
+
+size_t sage_kv_cache_bytes(int B, int Hkv, int Nk, int d) {
+    if (check_shape(B, Hkv, Hkv, Nk, d) != SAGE_OK) return 0;
+    return layout(sage::make_shape(B, Hkv, Hkv, Nk, d), false).total;
+}
+
+int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, sage_qkv_quant* out) {
+    int rc = check_shape(B, Hkv, Hkv, Nk, d);
+    if (rc != SAGE_OK) return rc;
+    if (!out) return SAGE_ERR_INVALID_ARG;
+    if (!buf || !aligned(buf, 256)) return SAGE_ERR_WORKSPACE;
+    const Layout L = layout(sage::make_shape(B, Hkv, Hkv, Nk, d), false);
+    if (bytes < L.total) return SAGE_ERR_WORKSPACE;
+    char* base = (char*)buf;
+    out->q_i8 = NULL;
+    out->q_scale = NULL;
+    out->k_i8 = (int8_t*)(base + L.k_i8);
+    out->k_scale = (float*)(base + L.k_scale);
+    out->k_mean = (float*)(base + L.k_mean);
+    out->v16 = (uint16_t*)(base + L.v16);
+    out->v_scale = (float*)(base + L.v_scale);
+    out->v_inv = (float*)(base + L.v_inv);
+    out->k_part = (double*)(base + L.k_part);
+    out->v_part = (float*)(base + L.v_part);
+    out->sync = (int32_t*)(base + L.sync);
+    out->q_block = SAGE_BQ_THREAD;
+    out->k_block = SAGE_BK;
+    out->pv_format = SAGE_PV_E4M3;
+    return SAGE_OK;
+}
+
+int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
+                     const sage_qkv_quant* cache, void* stream) {
+    int rc = check_shape(B, Hkv, Hkv, Nk, d);
+    if (rc != SAGE_OK) return rc;
+    if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
+    if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return SAGE_ERR_INVALID_ARG;
+    rc = check_cache(cache);
+    if (rc != SAGE_OK) return rc;
+    const Shape s = sage::make_shape(B, Hkv, Hkv, Nk, d);
+    hipError_t e = sage::launch_prep_kv(k, v, dtype, s, cache, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (check_decode_shape(B, Hq, Hkv, Nq, Nk, d) != SAGE_OK) return 0;
+    return decode_layout(B, Hq, Hkv, Nq, Nk, d).total;
+}
+
+int sage_attn_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_decode_shape(B, Hq, Hkv, Nq, Nk, d);
+    if (rc != SAGE_OK) return rc;
+    if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+    if (causal && Nq > Nk) return SAGE_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
+    rc = check_cache(cache);
+    if (rc != SAGE_OK) return rc;
+    const DecodeLayout L = decode_layout(B, Hq, Hkv, Nq, Nk, d);
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return SAGE_ERR_WORKSPACE;
+    const float qk = (float)((double)sm_scale * 1.4426950408889634);
+    const float l448 = cache->pv_format == SAGE_PV_F16 ? 0.0f : (float)log2(448.0);
+    char* base = (char*)workspace;
+    hipError_t e = sage::launch_decode(q, dtype, cache, out, (float*)(base + L.part_o),
+                                       (float*)(base + L.part_ml), B, Hq, Hkv, Nq, Nk, d, causal, qk,
+                                       l448, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
 int sage_get_config(sage_config* c) {

@@ -27,6 +27,15 @@ inline Shape make_shape(int B, int Hq, int Hkv, int N, int d) {
     return s;
 }
 
+// Split of a short-query attention over a KV cache into work-groups: row
+// tiles of 32 packed (q head, query row) pairs per kv head, and chunks of
+// chunk_blocks consecutive key blocks (nchunk of them).  A pure function of
+// the shape, so the host can size the workspace with it.
+struct DecodePlan {
+    int row_tiles, nchunk, chunk_blocks;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
 // Position of key j inside a block's V row.  The attention kernel's 32x32
 // Q.K^T tiles leave, in lane half h (lanes 32h..32h+31), the scores of keys
 // 8i + 4h + j (i, j = 0..3) of each 32-key tile.  Each 16-key step of P.V

@@ -198,6 +198,56 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, in
                      int N, int d, int causal, float sm_scale, int dtype, const sage_options* opts,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * ---- Short queries against a quantized KV cache (decode).
+ *
+ * A KV cache is the K/V half of sage_qkv_quant (the q_i8 and q_scale fields
+ * are NULL), quantized once: K smoothed with its channel mean over the Nk
+ * cached tokens and coded INT8 with one scale per k_block keys, V coded per
+ * channel in the pv_format's values -- the operands the attention kernel
+ * reads, at 3 bytes per K+V element pair instead of 4 for fp16/bf16 (the
+ * memory claim of the Berkeley brief's checklist).  Appending tokens means
+ * quantizing the cache again (the K mean and the V scales are global over
+ * the cached tokens).
+ */
+
+/* Bytes of a KV cache for [B, Hkv, Nk, d] (0 when the shape is invalid). */
+size_t sage_kv_cache_bytes(int B, int Hkv, int Nk, int d);
+
+/* Split `buf` (device memory, 256-byte aligned, `bytes` long) into the K/V
+ * views of `cache`; q_i8 and q_scale become NULL, k_block SAGE_BK and
+ * pv_format SAGE_PV_E4M3, which the caller may switch to SAGE_BK_THREAD and
+ * SAGE_PV_F16 before quantizing.  Host-only; no HIP call. */
+int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d,
+                        sage_qkv_quant* cache);
+
+/* The K/V half of sage_quantize: K mean, smoothing, INT8 K, V codes, from
+ * fp16/bf16 K, V [B, Hkv, Nk, d] into `cache`.  Runs as three kernels on
+ * `stream` (counter clearing, statistics, codes). */
+int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
+                     const sage_qkv_quant* cache, void* stream);
+
+/* Workspace bytes sage_attn_decode needs for this shape (at least 256; 0 when
+ * the shape is invalid). */
+size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/*
+ * out = softmax(Q K^T sm_scale) V for a short query q [B, Hq, Nq, d]
+ * (fp16/bf16, `dtype`) against the Nk keys of `cache`, as the method computes
+ * it, FP32 output [B, Hq, Nq, d].  The Nq query rows sit at the last Nq of
+ * the Nk positions: causal = 1 lets row i see keys j <= Nk - Nq + i (a mask
+ * aligned to the bottom right; it needs Nq <= Nk), causal = 0 every key.
+ * Each query row is quantized to INT8 with a scale of its own (as at the
+ * thread-level granularity); the cache's k_block and pv_format apply.  The
+ * key range is split into chunks whose partial results (reference max, row
+ * sum, unnormalised output; a third FP32 accumulation level) are merged by a
+ * second kernel in `workspace` (device memory, 256-byte aligned) when there is
+ * more than one chunk.
+ */
+int sage_attn_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
+                     void* workspace, size_t ws_bytes, void* stream);
+
 /* Block sizes and format constants of this build. */
 int sage_get_config(sage_config* c);
 

@@ -188,3 +188,61 @@ def test_pv_format_is_validated(sage):
                               None) == sage.SAGE_ERR_INVALID_ARG
     z = sage.sage_workspace_carve(fake, need, *shape, pv="f16")
     assert z.pv_format == sage.SAGE_PV_F16
+
+
+def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
+    """The KV-cache and short-query calls: sizes, carving (no Q regions) and
+    argument checks before any HIP call."""
+    L = sage._lib
+    fake = 1 << 40
+    f = ctypes.c_float
+    assert sage.sage_kv_cache_bytes(1, 2, 300, 64) > 0
+    assert sage.sage_kv_cache_bytes(1, 2, 300, 80) == 0
+    assert sage.sage_kv_cache_bytes(1, 2, 0, 64) == 0
+    # a cache is smaller than a full workspace of the same shape (no Q)
+    assert sage.sage_kv_cache_bytes(1, 2, 300, 64) < sage.sage_workspace_bytes(1, 2, 2, 300, 64)
+    need = sage.sage_kv_cache_bytes(1, 2, 300, 64)
+    z = sage.sage_kv_cache_carve(fake, need, 1, 2, 300, 64)
+    assert z.q_i8 is None and z.q_scale is None
+    ptrs = [getattr(z, n) for n in ("k_i8", "k_scale", "k_mean", "v16", "v_scale", "v_inv", "k_part",
+                                    "v_part", "sync")]
+    assert all(p % 256 == 0 for p in ptrs) and max(ptrs) < fake + need
+    assert (z.k_block, z.pv_format) == (64, 0)
+    with pytest.raises(sage.SageError):
+        sage.sage_kv_cache_carve(fake, need - 1, 1, 2, 300, 64)
+    zp = ctypes.byref(z)
+    # sage_kv_quantize
+    assert L.sage_kv_quantize(fake, None, 0, 1, 2, 300, 64, zp, None) == sage.SAGE_ERR_INVALID_ARG
+    assert L.sage_kv_quantize(fake, fake, 2, 1, 2, 300, 64, zp, None) == sage.SAGE_ERR_INVALID_ARG
+    assert L.sage_kv_quantize(fake, fake, 0, 1, 2, 300, 96, zp, None) == sage.SAGE_ERR_UNSUPPORTED
+    bad = sage.sage_qkv_quant.from_buffer_copy(z)
+    bad.k_block = 128
+    assert L.sage_kv_quantize(fake, fake, 0, 1, 2, 300, 64, ctypes.byref(bad), None) == sage.SAGE_ERR_UNSUPPORTED
+    # decode workspace
+    assert sage.sage_decode_workspace_bytes(1, 8, 2, 1, 300, 64) >= 256
+    assert sage.sage_decode_workspace_bytes(1, 8, 2, 0, 300, 64) == 0
+    assert sage.sage_decode_workspace_bytes(1, 7, 2, 1, 300, 64) == 0
+    wsb = sage.sage_decode_workspace_bytes(1, 8, 2, 1, 300, 64)
+
+    def dec(q=fake, dt=0, c=zp, out=fake, B=1, Hq=8, Hkv=2, Nq=1, Nk=300, d=64, causal=1, sm=0.125,
+            ws=fake, n=wsb):
+        return L.sage_attn_decode(q, dt, c, out, B, Hq, Hkv, Nq, Nk, d, causal, f(sm), ws, n, None)
+
+    assert dec(q=None) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(q=fake + 8) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(out=None) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(c=None) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(dt=3) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(Nq=0) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(Nq=301) == sage.SAGE_ERR_INVALID_ARG  # causal needs Nq <= Nk
+    assert dec(causal=2) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(sm=0.0) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(Hq=7) == sage.SAGE_ERR_UNSUPPORTED
+    assert dec(d=96) == sage.SAGE_ERR_UNSUPPORTED
+    assert dec(ws=None) == sage.SAGE_ERR_WORKSPACE
+    assert dec(ws=fake + 64) == sage.SAGE_ERR_WORKSPACE
+    assert dec(n=wsb - 1) == sage.SAGE_ERR_WORKSPACE
+    assert dec(c=ctypes.byref(bad)) == sage.SAGE_ERR_UNSUPPORTED
+    bad2 = sage.sage_qkv_quant.from_buffer_copy(z)
+    bad2.pv_format = 5
+    assert dec(c=ctypes.byref(bad2)) == sage.SAGE_ERR_UNSUPPORTED
