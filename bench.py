@@ -159,13 +159,13 @@ def cpu_baseline(w, q, k, v, rows_wanted, bq, bk, pv):
                       f"(prep {t_prep:.2f} s, attention {t_attn:.2f} s)"}
 
 
-def decode_bytes(w, k_block):
+def decode_bytes(w, k_block, pv):
     """Bytes one short-query launch must move with this cache format: INT8 K
-    (1 B), binary16 V (2 B) and the K scales of the cache; the query in and
-    the FP32 output."""
+    (1 B), V as E4M3 codes (1 B) or binary16 (2 B), the K scales and V scales
+    of the cache; the query in and the FP32 output."""
     kv = w.B * w.Hkv * w.N * w.d
-    return (3 * kv + w.B * w.Hkv * (-(-w.N // k_block)) * 4 + w.B * w.Hkv * w.d * 4
-            + w.B * w.Hq * w.q_rows * w.d * (2 + 4))
+    return ((2 if pv == "e4m3" else 3) * kv + w.B * w.Hkv * (-(-w.N // k_block)) * 4
+            + w.B * w.Hkv * w.d * 4 + w.B * w.Hq * w.q_rows * w.d * (2 + 4))
 
 
 def cpu_baseline_decode(w, q, k, v, bk, pv):
@@ -185,7 +185,7 @@ def cpu_baseline_decode(w, q, k, v, bk, pv):
     for _ in range(reps):
         oracle.attn_q(z, w.causal, w.sm_scale, interval=False)
     t = (time.perf_counter() - t0) / reps
-    return {"value": decode_bytes(w, bk) / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+    return {"value": decode_bytes(w, bk, pv) / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": f"all {w.B * w.Hq * w.q_rows} query rows of the workload, "
                                         f"{reps} passes, {t * 1e3:.2f} ms each (the cache "
                                         f"quantization is not timed)"}
@@ -211,7 +211,7 @@ def bench_decode(args, sage, workloads, torch):
     wall = time.perf_counter() - t0
     ms_cache = timed(lambda: sage.sage_kv_quantize(kd, vd, cache.z), max(3, args.steps // 10), torch)
     kb = cache.z.k_block
-    nb = decode_bytes(w, kb)
+    nb = decode_bytes(w, kb, args.pv)
     gbs = nb / (ms * 1e-3) / 1e9
     fp16_kv = 2 * 2 * w.B * w.Hkv * w.N * w.d
     line = {

@@ -45,6 +45,12 @@ class sage_qkv_quant(ctypes.Structure):
                                                  ("pv_format", ctypes.c_int32)]
 
 
+class sage_kv_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("k_i8", "k_scale", "k_mean", "v", "v_scale", "v_inv", "k_part", "v_part", "sync")] + \
+               [("k_block", ctypes.c_int32), ("pv_format", ctypes.c_int32)]
+
+
 class sage_options(ctypes.Structure):
     _fields_ = [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32), ("pv_format", ctypes.c_int32)]
 
@@ -62,12 +68,12 @@ _lib.sage_attn_fwd_granular.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, 
 _lib.sage_attn_fwd_ex.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                   ctypes.POINTER(sage_options), _P, _S, _P]
 _lib.sage_kv_cache_bytes.restype = _S
-_lib.sage_kv_cache_bytes.argtypes = [_I, _I, _I, _I]
-_lib.sage_kv_cache_carve.argtypes = [_P, _S, _I, _I, _I, _I, ctypes.POINTER(sage_qkv_quant)]
-_lib.sage_kv_quantize.argtypes = [_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(sage_qkv_quant), _P]
+_lib.sage_kv_cache_bytes.argtypes = [_I, _I, _I, _I, _I]
+_lib.sage_kv_cache_carve.argtypes = [_P, _S, _I, _I, _I, _I, _I, _I, ctypes.POINTER(sage_kv_cache)]
+_lib.sage_kv_quantize.argtypes = [_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(sage_kv_cache), _P]
 _lib.sage_decode_workspace_bytes.restype = _S
 _lib.sage_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
-_lib.sage_attn_decode.argtypes = [_P, _I, ctypes.POINTER(sage_qkv_quant), _P, _I, _I, _I, _I, _I, _I,
+_lib.sage_attn_decode.argtypes = [_P, _I, ctypes.POINTER(sage_kv_cache), _P, _I, _I, _I, _I, _I, _I,
                                   _I, _F, _P, _S, _P]
 _lib.sage_get_config.argtypes = [ctypes.POINTER(sage_config)]
 _lib.sage_v_key_position.argtypes = [_I]
@@ -188,23 +194,22 @@ def sage_attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def sage_kv_cache_bytes(B: int, Hkv: int, Nk: int, d: int) -> int:
-    return int(_lib.sage_kv_cache_bytes(B, Hkv, Nk, d))
+def sage_kv_cache_bytes(B: int, Hkv: int, Nk: int, d: int, pv: str = "e4m3") -> int:
+    return int(_lib.sage_kv_cache_bytes(B, Hkv, Nk, d, PV_FORMAT[pv]))
 
 
 def sage_kv_cache_carve(buf: torch.Tensor | int | None, nbytes: int, B: int, Hkv: int, Nk: int,
-                        d: int, granularity: str = "block", pv: str = "e4m3") -> sage_qkv_quant:
-    """The C call, then k_block and pv_format set to the chosen K granularity
-    ("block": 64 keys per scale, "thread": 32) and P.V format."""
-    z = sage_qkv_quant()
+                        d: int, granularity: str = "block", pv: str = "e4m3") -> sage_kv_cache:
+    """The C call with the K granularity ("block": 64 keys per scale,
+    "thread": 32) and the P.V format by name."""
+    z = sage_kv_cache()
     ptr = buf.data_ptr() if isinstance(buf, torch.Tensor) else buf
-    _check(_lib.sage_kv_cache_carve(ptr, nbytes, B, Hkv, Nk, d, ctypes.byref(z)))
-    z.k_block = GRANULARITY[granularity][1]
-    z.pv_format = PV_FORMAT[pv]
+    _check(_lib.sage_kv_cache_carve(ptr, nbytes, B, Hkv, Nk, d, GRANULARITY[granularity][1],
+                                    PV_FORMAT[pv], ctypes.byref(z)))
     return z
 
 
-def sage_kv_quantize(k: torch.Tensor, v: torch.Tensor, cache: sage_qkv_quant, stream=None) -> None:
+def sage_kv_quantize(k: torch.Tensor, v: torch.Tensor, cache: sage_kv_cache, stream=None) -> None:
     B, Hkv, Nk, d = k.shape
     _check(_lib.sage_kv_quantize(_ptr(k), _ptr(v), _dtype_code(k), B, Hkv, Nk, d, ctypes.byref(cache),
                                  _stream(stream)))
@@ -214,7 +219,7 @@ def sage_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: 
     return int(_lib.sage_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
 
 
-def sage_attn_decode(q: torch.Tensor, cache: sage_qkv_quant, out: torch.Tensor, Hkv: int, Nk: int,
+def sage_attn_decode(q: torch.Tensor, cache: sage_kv_cache, out: torch.Tensor, Hkv: int, Nk: int,
                      causal: bool, sm_scale: float, workspace: torch.Tensor, stream=None) -> None:
     B, Hq, Nq, d = q.shape
     _check(_lib.sage_attn_decode(_ptr(q), _dtype_code(q), ctypes.byref(cache), _ptr(out), B, Hq, Hkv,
@@ -268,7 +273,7 @@ class KVCache:
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("K, V must be contiguous device tensors")
         self.B, self.Hkv, self.Nk, self.d = k.shape
-        nbytes = sage_kv_cache_bytes(self.B, self.Hkv, self.Nk, self.d)
+        nbytes = sage_kv_cache_bytes(self.B, self.Hkv, self.Nk, self.d, pv)
         if nbytes == 0:
             raise SageError(SAGE_ERR_UNSUPPORTED)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
@@ -295,6 +300,47 @@ class KVCache:
         return out
 
 
+def _host_view(buf: torch.Tensor, addr: int, shape, dtype) -> torch.Tensor:
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    off = addr - buf.data_ptr()
+    return buf[off:off + nbytes].cpu().view(dtype).reshape(shape)
+
+
+def _unpermute_v(vb: torch.Tensor, B: int, H: int, Np: int, d: int) -> torch.Tensor:
+    """[B, H, Np/128, d, 128] blocks with keys in sage_v_key_position order ->
+    [B, H, Np, d]."""
+    perm = torch.tensor([sage_v_key_position(j) for j in range(SAGE_BN)], dtype=torch.long)
+    return vb[..., perm].permute(0, 1, 2, 4, 3).reshape(B, H, Np, d)
+
+
+def read_kv_cache(c: sage_kv_cache, buf: torch.Tensor, B: int, Hkv: int, Nk: int, d: int) -> dict:
+    """Copy a KV cache (carved from `buf`) to host tensors in the plain
+    [B,Hkv,Nk,d] layout: K codes, scales and mean, and V as E4M3 code bytes
+    (v_fp8) or binary16 bit patterns (v_f16), plus the values (v_half).
+    Layout only; `*_pad` hold rows Nk..N_p-1."""
+    Np = -(-Nk // SAGE_NPAD) * SAGE_NPAD
+    torch.cuda.synchronize()
+    k_full = _host_view(buf, c.k_i8, (B, Hkv, Np, d), torch.int8)
+    f16 = c.pv_format == SAGE_PV_F16
+    vb = _host_view(buf, c.v, (B, Hkv, Np // SAGE_BN, d, SAGE_BN), torch.int16 if f16 else torch.uint8)
+    v_full = _unpermute_v(vb, B, Hkv, Np, d)
+    if f16:
+        codes = dict(v_f16=v_full[:, :, :Nk].contiguous())
+        v_half = v_full.view(torch.float16)
+    else:
+        codes = dict(v_fp8=v_full[:, :, :Nk].contiguous())
+        v_half = v_full.view(torch.float8_e4m3fn).to(torch.float16)
+    return dict(
+        **codes, k_i8=k_full[:, :, :Nk].contiguous(), v_half=v_half[:, :, :Nk].contiguous(),
+        k_pad=k_full[:, :, Nk:].contiguous(), v_pad=v_full[:, :, Nk:].contiguous(),
+        k_scale=_host_view(buf, c.k_scale, (B, Hkv, Np // c.k_block), torch.float32),
+        k_mean=_host_view(buf, c.k_mean, (B, Hkv, d), torch.float32),
+        v_scale=_host_view(buf, c.v_scale, (B, Hkv, d), torch.float32))
+
+
 def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, Hkv: int,
                    N: int, d: int) -> dict:
     """Copy the quantized operands out of `workspace` (carved into `z`) to host
@@ -302,35 +348,27 @@ def read_quantized(z: sage_qkv_quant, workspace: torch.Tensor, B: int, Hq: int, 
     comes back as its binary16 values (v_half) and as codes: E4M3 codes
     (v_fp8; the binary16 values convert back exactly) or, for the binary16
     P.V format, the binary16 bit patterns (v_f16).  Layout only; `*_pad` hold
-    rows N..N_p-1.  For a KV cache (no Q fields) the Q entries are left out."""
+    rows N..N_p-1."""
     Np = -(-N // SAGE_NPAD) * SAGE_NPAD
-    base = workspace.data_ptr()
     torch.cuda.synchronize()
 
     def host(addr, shape, dtype):
-        n = 1
-        for s in shape:
-            n *= s
-        nbytes = n * torch.empty((), dtype=dtype).element_size()
-        off = addr - base
-        return workspace[off:off + nbytes].cpu().view(dtype).reshape(shape)
+        return _host_view(workspace, addr, shape, dtype)
 
     k_full = host(z.k_i8, (B, Hkv, Np, d), torch.int8)
     vb = host(z.v16, (B, Hkv, Np // SAGE_BN, d, SAGE_BN), torch.float16)
-    perm = torch.tensor([sage_v_key_position(j) for j in range(SAGE_BN)], dtype=torch.long)
-    v_half = vb[..., perm].permute(0, 1, 2, 4, 3).reshape(B, Hkv, Np, d)
+    v_half = _unpermute_v(vb, B, Hkv, Np, d)
     if z.pv_format == SAGE_PV_F16:
         v_codes = dict(v_f16=v_half.view(torch.int16)[:, :, :N].contiguous())
     else:
         v_codes = dict(v_fp8=v_half.to(torch.float8_e4m3fn).view(torch.uint8)[:, :, :N].contiguous())
-    r = dict(
-        **v_codes, k_i8=k_full[:, :, :N].contiguous(), v_half=v_half[:, :, :N].contiguous(),
-        k_pad=k_full[:, :, N:].contiguous(), v_pad=v_half[:, :, N:].contiguous(),
+    q_full = host(z.q_i8, (B, Hq, Np, d), torch.int8)
+    return dict(
+        **v_codes, q_i8=q_full[:, :, :N].contiguous(), k_i8=k_full[:, :, :N].contiguous(),
+        v_half=v_half[:, :, :N].contiguous(),
+        q_pad=q_full[:, :, N:].contiguous(), k_pad=k_full[:, :, N:].contiguous(),
+        v_pad=v_half[:, :, N:].contiguous(),
+        q_scale=host(z.q_scale, (B, Hq, Np // z.q_block), torch.float32),
         k_scale=host(z.k_scale, (B, Hkv, Np // z.k_block), torch.float32),
         k_mean=host(z.k_mean, (B, Hkv, d), torch.float32),
         v_scale=host(z.v_scale, (B, Hkv, d), torch.float32))
-    if z.q_i8 is not None:
-        q_full = host(z.q_i8, (B, Hq, Np, d), torch.int8)
-        r.update(q_i8=q_full[:, :, :N].contiguous(), q_pad=q_full[:, :, N:].contiguous(),
-                 q_scale=host(z.q_scale, (B, Hq, Np // z.q_block), torch.float32))
-    return r

@@ -58,55 +58,86 @@ constexpr int kSeedBits = 0x4B400000;  // its float32 bit pattern
 // lanes of one LDS read phase (16 consecutive rows, same chunk) land on 16
 // different 16-byte bank groups.
 template <int D>
-__device__ inline int kswz(int row) {
+__host__ __device__ constexpr int kswz(int row) {
     return D == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
 }
-// and of one V-tile row (a channel, 128 binary16 = 16 chunks)
-__device__ inline int vswz(int ch) { return ch & 15; }
+// and of one V-tile row (a channel: 128 binary16 = 16 chunks, or 128 E4M3
+// bytes = 8 chunks).  With bytes, the 32 lanes of one 8-byte read phase
+// (32 channels, same chunk) cover 32 of the 64 banks twice: a 2-way conflict,
+// the least a 16-byte swizzle allows for 8-byte reads.
+__host__ __device__ constexpr int vswz(int ch) { return ch & 15; }
+__host__ __device__ constexpr int vswz8(int ch) { return (ch >> 1) & 7; }
+template <int VB>
+__host__ __device__ constexpr int vswz_b(int ch) {
+    return VB == 2 ? vswz(ch) : vswz8(ch);
+}
 
-// Copies key blocks (K: 128 rows x D bytes, V: D rows x 128 binary16) of one
-// kv head into LDS with buffer loads that write LDS directly.  Each lane's
-// byte offsets inside a block are fixed, so a block costs no vector ALU work:
-// the block's base goes in the scalar offset.
-template <int D, int WAVES>
+// Smallest number of load steps after which a lane's swizzled offset repeats,
+// shifted by whole steps: each step moves `step` rows down the tile, and the
+// swizzle is periodic in the row.
+template <int VB, bool IS_K, int D>
+constexpr int swizzle_period(int step, int steps) {
+    for (int p = 1; p < steps; p *= 2) {
+        bool same = true;
+        for (int row = 0; row < 256; ++row)
+            if ((IS_K ? kswz<D>(row + p * step) : vswz_b<VB>(row + p * step)) !=
+                (IS_K ? kswz<D>(row) : vswz_b<VB>(row)))
+                same = false;
+        if (same) return p;
+    }
+    return steps;
+}
+
+// Copies key blocks (K: 128 rows x D bytes, V: D rows x 128 values of VB
+// bytes, binary16 or E4M3) of one kv head into LDS with buffer loads that
+// write LDS directly.  Load step r copies LDS chunks [r NT, (r+1) NT); a
+// lane's global offset in step r is its offset in step r % P (P the swizzle
+// period) plus whole steps, which go in the scalar offset with the block's
+// base, so a block costs no vector ALU work and only P offset registers per
+// tile.
+template <int D, int WAVES, int VB = 2>
 struct TileLoader {
     static constexpr int NT = 64 * WAVES;
-    static constexpr int KR = SAGE_BN * D / 16 / NT;      // 16-byte chunks per lane, K
-    static constexpr int VR = D * SAGE_BN * 2 / 16 / NT;  // and V
-    static_assert(KR * NT * 16 == SAGE_BN * D && VR * NT * 16 == D * SAGE_BN * 2,
+    static constexpr int KR = SAGE_BN * D / 16 / NT;       // 16-byte chunks per lane, K
+    static constexpr int VR = D * SAGE_BN * VB / 16 / NT;  // and V
+    static constexpr int VCH = SAGE_BN * VB / 16;          // 16-byte chunks per V row
+    static_assert(KR * NT * 16 == SAGE_BN * D && VR * NT * 16 == D * SAGE_BN * VB,
                   "tile must split evenly over the work-group");
+    static constexpr int KP = swizzle_period<VB, true, D>(NT * 16 / D, KR);
+    static constexpr int VP = swizzle_period<VB, false, D>(NT / VCH, VR);
+    static_assert(KR % KP == 0 && VR % VP == 0, "load steps must cover whole periods");
     __amdgpu_buffer_rsrc_t krs, vrs;
-    uint32_t koff[KR], voff[VR];
+    uint32_t koff[KP], voff[VP];
 
-    __device__ TileLoader(const uint8_t* kg, const uint16_t* vg, int head_rows, int wave, int lane) {
+    __device__ TileLoader(const uint8_t* kg, const void* vg, int head_rows, int wave, int lane) {
         krs = __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_rows * D, 0x00020000);
-        vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_rows * D * 2, 0x00020000);
+        vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_rows * D * VB, 0x00020000);
 #pragma unroll
-        for (int r = 0; r < KR; ++r) {
+        for (int r = 0; r < KP; ++r) {
             // LDS chunk p of the K tile holds chunk p ^ swizzle of its row
             const int p = r * NT + wave * 64 + lane;
             const int row = p / (D / 16), qs = p % (D / 16);
             koff[r] = row * D + ((qs ^ kswz<D>(row)) << 4);
         }
 #pragma unroll
-        for (int r = 0; r < VR; ++r) {
+        for (int r = 0; r < VP; ++r) {
             const int p = r * NT + wave * 64 + lane;
-            const int c = p >> 4, qs = p & 15;
-            voff[r] = c * (SAGE_BN * 2) + ((qs ^ vswz(c)) << 4);
+            const int c = p / VCH, qs = p % VCH;
+            voff[r] = c * (SAGE_BN * VB) + ((qs ^ vswz_b<VB>(c)) << 4);
         }
     }
 
-    __device__ inline void load(int T, uint8_t* lk, uint16_t* lv, int wave) const {
+    __device__ inline void load(int T, uint8_t* lk, void* lv, int wave) const {
 #pragma unroll
         for (int r = 0; r < KR; ++r)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 krs, (__attribute__((address_space(3))) void*)(lk + (r * NT + wave * 64) * 16), 16,
-                koff[r], T * SAGE_BN * D, 0, 0);
+                koff[r % KP], T * SAGE_BN * D + (r / KP) * KP * NT * 16, 0, 0);
 #pragma unroll
         for (int r = 0; r < VR; ++r)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 vrs, (__attribute__((address_space(3))) void*)((uint8_t*)lv + (r * NT + wave * 64) * 16),
-                16, voff[r], T * SAGE_BN * D * 2, 0, 0);
+                16, voff[r % VP], T * SAGE_BN * D * VB + (r / VP) * VP * NT * 16, 0, 0);
     }
 };
 
@@ -133,13 +164,15 @@ __device__ inline int max_across_halves(int x) {
 
 // One key block for one wave (32 query rows).  MASKED: some keys of the
 // block are excluded (causal diagonal, or keys >= N).  PV16: P is rounded to
-// binary16 directly (l448 is then 0) instead of through E4M3.
+// binary16 directly (l448 is then 0) instead of through E4M3.  V8: the V tile
+// holds E4M3 code bytes (a KV cache), converted to binary16 -- exactly -- as
+// each fragment is read.
 // KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
 // 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
 // log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false>
 __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
-                                           const uint16_t* __restrict__ lv,
+                                           const void* __restrict__ lv,
                                            const v4i (&qf)[D / 32], int T, int row, int N,
                                            const float (&c)[KSPLIT], float l448, int h, int r32,
                                            const v8h& rsel, float& mref, float& lsum,
@@ -271,7 +304,21 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
 #pragma unroll
             for (int j = 0; j < CG; ++j) {
                 const int ch = 32 * (pass * CG + j) + r32;
-                const v8h vf = *reinterpret_cast<const v8h*>(lv + ch * SAGE_BN + (((2 * s + h) ^ vswz(ch)) << 3));
+                v8h vf;
+                if (V8) {
+                    // keys 16s + 8h .. +8 of the channel: 8 code bytes
+                    const uint2 raw = *reinterpret_cast<const uint2*>(
+                        (const uint8_t*)lv + ch * SAGE_BN + ((s ^ vswz8(ch)) << 4) + 8 * h);
+                    const v4i w = {
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.x, 1.0f, false)),
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.x, 1.0f, true)),
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.y, 1.0f, false)),
+                        __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.y, 1.0f, true))};
+                    vf = __builtin_bit_cast(v8h, w);
+                } else {
+                    vf = *reinterpret_cast<const v8h*>((const uint16_t*)lv + ch * SAGE_BN +
+                                                       (((2 * s + h) ^ vswz(ch)) << 3));
+                }
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[s], acc[j], 0, 0, 0);
             }
         }

@@ -1,7 +1,11 @@
 // Short-query attention over a quantized KV cache (decode) for CDNA4 (gfx950).
 //
 // The cache holds the K/V half of the prep step (smoothed INT8 K with its
-// scales, V as binary16 in the P.V format's values), quantized once.  A short
+// scales; V as E4M3 code bytes, or binary16 for the binary16 P.V), quantized
+// once.  E4M3 V tiles stay one byte per value in LDS and are converted to
+// binary16 (exactly) as each P.V fragment is read, so a block moves 2 bytes
+// per K+V element pair from HBM and LDS holds two work-groups per CU even at
+// d = 128.  A short
 // query -- Nq rows per q head, sitting at the last Nq of the Nk positions --
 // attends to it with the same per-block computation as the prefill kernel
 // (attn_block.h).  The query rows are quantized here, one INT8 scale per row.
@@ -22,7 +26,7 @@ struct DecodeArgs {
     const uint16_t* q;      // [B, Hq, Nq, d], fp16 or bf16 bits
     const int8_t* k_i8;     // cache, [B, Hkv, Np, d]
     const float* k_scale;   // [B, Hkv, Np / k_block]
-    const uint16_t* v16;    // [B, Hkv, Np / SAGE_BN, d, SAGE_BN]
+    const void* v;          // [B, Hkv, Np / SAGE_BN, d, SAGE_BN], E4M3 bytes or binary16
     const float* v_scale;   // [B, Hkv, d]
     float* out;             // [B, Hq, Nq, d]
     float* part_o;          // [B * Hq * Nq, nchunk, d]
@@ -83,14 +87,22 @@ __device__ inline float quantize_q_row(const uint16_t* __restrict__ qrow, bool v
     return am / 127.0f;
 }
 
+// V element bytes in the cache: binary16 for the binary16 P.V, else E4M3.
+template <bool PV16>
+constexpr int cache_vb() {
+    return PV16 ? 2 : 1;
+}
+
 template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
 __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     constexpr int CT = D / 32;
+    constexpr int VB = cache_vb<PV16>();
+    constexpr bool V8 = VB == 1;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* const lk0 = smem;
     uint8_t* const lk1 = smem + SAGE_BN * D;
-    uint16_t* const lv0 = reinterpret_cast<uint16_t*>(smem + 2 * SAGE_BN * D);
-    uint16_t* const lv1 = lv0 + D * SAGE_BN;
+    uint8_t* const lv0 = smem + 2 * SAGE_BN * D;
+    uint8_t* const lv1 = lv0 + D * SAGE_BN * VB;
 
     const int lane = threadIdx.x;
     const int h = lane >> 5, r32 = lane & 31;
@@ -125,7 +137,7 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     const int first_masked = CAUSAL ? min(a.Nk / SAGE_BN, (a.Nk - a.Nq + 1) / SAGE_BN) : a.Nk / SAGE_BN;
 
     const uint8_t* kbase = (const uint8_t*)a.k_i8 + (long long)bg * a.Np * D;
-    const uint16_t* vbase = a.v16 + (long long)bg * a.Np * D;
+    const uint8_t* vbase = (const uint8_t*)a.v + (long long)bg * a.Np * D * VB;
     const float* ksc = a.k_scale + (long long)bg * (a.Np / (SAGE_BN / KSPLIT));
 
     v16f O[CT];
@@ -137,7 +149,7 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
 
     typedef float kvec __attribute__((ext_vector_type(KSPLIT)));
     kvec kscale = *reinterpret_cast<const kvec*>(ksc + KSPLIT * T0);
-    const TileLoader<D, 1> tiles(kbase, vbase, a.Np, 0, lane);
+    const TileLoader<D, 1, VB> tiles(kbase, vbase, a.Np, 0, lane);
     tiles.load(T0, lk0, lv0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -152,11 +164,11 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
 #pragma unroll
         for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * kscale[gg]) * a.qk;
         if (T < first_masked)
-            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
-                                                       a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, PV16, false, V8>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
+                                                           a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
         else
-            attn_block<D, KSPLIT, CAUSAL, PV16, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
-                                                      a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, PV16, true, V8>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
+                                                          a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -196,24 +208,70 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     if (h == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(mref, lsum);
 }
 
-// One work-group per query row, one thread per channel: out = O * s_V / l
-// over the row's chunks, each weighted by 2^(its reference max - the largest).
+// One work-group of 256 threads per query row: out = O * s_V / l over the
+// row's chunks, each weighted by 2^(its reference max - the largest).  The
+// chunk weights are formed once (one thread per chunk), then every
+// (chunk, channel) partial is read by its own thread, so all loads are in
+// flight together, and the sums are reduced in LDS.
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a) {
+    constexpr int GROUPS = kMergeThreads / D;  // chunk groups summed in parallel
+    __shared__ float red[kMergeThreads];
+    __shared__ float wgt[kMergeThreads];
+    __shared__ float s_M, s_l;
     const long long row = blockIdx.x;  // (b * Hq + hq) * Nq + i
-    const int c = threadIdx.x;
+    const int t = threadIdx.x;
     const int hq = (int)((row / a.Nq) % a.Hq), b = (int)(row / ((long long)a.Nq * a.Hq));
     const int bg = b * a.Hkv + hq / a.G;
     const float* ml = a.part_ml + row * a.nchunk * 2;
-    float M = -INFINITY;
-    for (int k = 0; k < a.nchunk; ++k) M = fmaxf(M, ml[2 * k]);
-    float o = 0.0f, l = 0.0f;
-    for (int k = 0; k < a.nchunk; ++k) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * k] - M);  // 0 for an empty chunk
-        o = __builtin_fmaf(a.part_o[(row * a.nchunk + k) * D + c], w, o);
+    const float* po = a.part_o + row * a.nchunk * D;
+
+    // the largest reference max (an empty chunk has -inf)
+    float m = -INFINITY;
+    for (int k = t; k < a.nchunk; k += kMergeThreads) m = fmaxf(m, ml[2 * k]);
+    red[t] = m;
+    __syncthreads();
+    for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
+        if (t < o) red[t] = fmaxf(red[t], red[t + o]);
+        __syncthreads();
+    }
+    if (t == 0) s_M = red[0];
+    __syncthreads();
+    const float M = s_M;
+
+    // row sum; the chunk weights of the first kMergeThreads chunks stay in LDS
+    float l = 0.0f;
+    for (int k = t; k < a.nchunk; k += kMergeThreads) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * k] - M);
+        if (k < kMergeThreads) wgt[k] = w;
         l = __builtin_fmaf(ml[2 * k + 1], w, l);
     }
-    a.out[row * D + c] = o * a.v_scale[(long long)bg * D + c] * (1.0f / l);
+    __syncthreads();
+    red[t] = l;
+    __syncthreads();
+    for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
+        if (t < o) red[t] += red[t + o];
+        __syncthreads();
+    }
+    if (t == 0) s_l = red[0];
+    __syncthreads();
+
+    // O: thread t sums channel t % D over chunks k = t / D (mod GROUPS)
+    const int c = t % D, grp = t / D;
+    float o = 0.0f;
+    for (int k = grp; k < a.nchunk; k += GROUPS) {
+        const float w = k < kMergeThreads ? wgt[k] : __builtin_amdgcn_exp2f(ml[2 * k] - M);
+        o = __builtin_fmaf(po[(long long)k * D + c], w, o);
+    }
+    __syncthreads();
+    red[t] = o;
+    __syncthreads();
+    if (grp == 0) {
+        for (int g2 = 1; g2 < GROUPS; ++g2) o += red[g2 * D + c];
+        a.out[row * D + c] = o * a.v_scale[(long long)bg * D + c] * (1.0f / s_l);
+    }
 }
 
 #define SAGE_DECODE_INST(In, D, KSPLIT, CAUSAL, PV16) \
@@ -234,8 +292,10 @@ SAGE_DECODE_INST_K(Bf16Tag, 128)
 template __global__ void decode_merge<64>(DecodeArgs);
 template __global__ void decode_merge<128>(DecodeArgs);
 
-// Chunking: enough work-groups to keep every CU streaming the cache (three
-// one-wave work-groups fit a CU's LDS at d = 64, one at d = 128), in chunks of
+// Chunking: enough work-groups to keep every CU streaming the cache (the
+// double-buffered tiles of an E4M3 cache, 2 bytes per K+V element pair, let
+// 5 one-wave work-groups share a CU's LDS at d = 64 and 2 at d = 128; a
+// binary16 cache, 3 bytes, fits fewer and is split the same way), in chunks of
 // at least kMinChunkBlocks blocks so that filling each work-group's two-tile
 // pipeline stays a small part of its work.
 constexpr int kMinChunkBlocks = 4;
@@ -246,7 +306,9 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     pl.row_tiles = (G * Nq + 31) / 32;
     const int nkb = (Nk + SAGE_BN - 1) / SAGE_BN;
     const long long units = (long long)B * Hkv * pl.row_tiles;
-    const long long target = 2LL * 256 * (d == 64 ? 3 : 1);
+    const long long lds = 2LL * SAGE_BN * d * 2;
+    const long long per_cu = 163840 / lds;
+    const long long target = 2LL * 256 * per_cu;
     long long want = (target + units - 1) / units;
     int per = (int)((nkb + want - 1) / want);
     if (per < kMinChunkBlocks) per = kMinChunkBlocks;
@@ -258,7 +320,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 
 template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
+    constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * cache_vb<PV16>();
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)attn_decode<In, D, KSPLIT, CAUSAL, PV16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -269,8 +331,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
                        st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nchunk == 1) return e;
-    hipLaunchKernelGGL((decode_merge<D>), dim3((unsigned)((long long)a.B * a.Hq * a.Nq)), dim3(D), 0,
-                       st, a);
+    hipLaunchKernelGGL((decode_merge<D>), dim3((unsigned)((long long)a.B * a.Hq * a.Nq)),
+                       dim3(kMergeThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -290,7 +352,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, bool fine_k, int causal, 
                   : launch_decode_k<In, D, 2>(a, causal, pv16, st);
 }
 
-hipError_t launch_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out,
+hipError_t launch_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out,
                          float* part_o, float* part_ml, int B, int Hq, int Hkv, int Nq, int Nk,
                          int d, int causal, float qk, float l448, hipStream_t st) {
     const DecodePlan pl = decode_plan(B, Hq, Hkv, Nq, Nk, d);
@@ -298,7 +360,7 @@ hipError_t launch_decode(const void* q, int dtype, const sage_qkv_quant* cache, 
     a.q = (const uint16_t*)q;
     a.k_i8 = cache->k_i8;
     a.k_scale = cache->k_scale;
-    a.v16 = cache->v16;
+    a.v = cache->v;
     a.v_scale = cache->v_scale;
     a.out = out;
     a.part_o = part_o;

@@ -104,6 +104,21 @@ __device__ inline void v_codes_to_tile(const float (&x)[8], const float* inv, in
     }
 }
 
+// The E4M3 code bytes of x[i] * inv[i], i = 0..7, into the transposed byte
+// tile vt[D][SAGE_BN] at key position pos (a KV cache's V).
+template <int D>
+__device__ inline void v_codes_to_tile8(const float (&x)[8], const float* inv, int col, int pos,
+                                        uint8_t* vt) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const float y0 = fminf(fmaxf(x[i] * inv[i], -448.0f), 448.0f);
+        const float y1 = fminf(fmaxf(x[i + 1] * inv[i + 1], -448.0f), 448.0f);
+        const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        vt[(col + i) * SAGE_BN + pos] = (uint8_t)(codes & 0xFF);
+        vt[(col + i + 1) * SAGE_BN + pos] = (uint8_t)((codes >> 8) & 0xFF);
+    }
+}
+
 // V's binary16 rounding (nearest even, clamped to +-65504 first so that
 // out-of-range bf16 values saturate) of x[i], i = 0..7, into the transposed
 // V tile.
@@ -116,16 +131,15 @@ __device__ inline void v_f16_to_tile(const float (&x)[8], int col, int pos, uint
     }
 }
 
-// Copies a transposed V tile from LDS to its place in v16 (streaming
-// stores: the tile is not read again by this step).
-template <int D>
-__device__ inline void store_v_tile(const uint16_t* vt, uint16_t* dst, int tid) {
-    constexpr int OUT_CH = D * SAGE_BN * 2 / 16 / kThreads;
+// Copies a transposed V tile of VB-byte values from LDS to its place in the
+// V operand (streaming stores: the tile is not read again by this step).
+template <int D, int VB>
+__device__ inline void store_v_tile(const void* vt, void* dst, int tid) {
+    constexpr int OUT_CH = D * SAGE_BN * VB / 16 / kThreads;
 #pragma unroll
     for (int c = 0; c < OUT_CH; ++c) {
         const int e = tid + c * kThreads;
-        __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(vt + e * 8),
-                                    reinterpret_cast<v4u*>(dst + e * 8));
+        __builtin_nontemporal_store(*(reinterpret_cast<const v4u*>(vt) + e), reinterpret_cast<v4u*>(dst) + e);
     }
 }
 
@@ -264,7 +278,7 @@ template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_pack(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s, int bk,
     const float* __restrict__ k_mean, const float* __restrict__ v_inv,
-    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint16_t* __restrict__ v16, int pv16) {
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, void* __restrict__ v_out, int v_store) {
     constexpr int CPR = D / 8;
     __shared__ float rmax[64], gmax[64];
     __shared__ __attribute__((aligned(16))) uint16_t vt[D * SAGE_BN];
@@ -331,13 +345,20 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = 0.0f;
         }
-        if (pv16)
+        if (v_store == kVF16)
             v_f16_to_tile<D>(x, col, v_key_position(key), vt);
+        else if (v_store == kVE4M3Byte)
+            v_codes_to_tile8<D>(x, v_inv + (long long)bg * D + col, col, v_key_position(key),
+                                reinterpret_cast<uint8_t*>(vt));
         else
             v_codes_to_tile<D>(x, v_inv + (long long)bg * D + col, col, v_key_position(key), vt);
     }
     __syncthreads();
-    store_v_tile<D>(vt, v16 + ((long long)bg * nvb + T) * (long long)(D * SAGE_BN), tid);
+    const long long tile = ((long long)bg * nvb + T) * (long long)(D * SAGE_BN);
+    if (v_store == kVE4M3Byte)
+        store_v_tile<D, 1>(vt, static_cast<uint8_t*>(v_out) + tile, tid);
+    else
+        store_v_tile<D, 2>(vt, static_cast<uint16_t*>(v_out) + tile, tid);
 }
 
 // Clears the arrival counters when the K/V half runs without prep_q (whose
@@ -348,19 +369,19 @@ __global__ __launch_bounds__(kThreads) void clear_words(int* __restrict__ w, int
 
 // ------------------------------------------------------------ launchers
 template <typename In, int D>
-static hipError_t launch_prep_kv_t(const void* k, const void* v, const Shape& s,
-                                   const sage_qkv_quant* z, hipStream_t st) {
+static hipError_t launch_prep_kv_t(const void* k, const void* v, const Shape& s, const KVViews& z,
+                                   hipStream_t st) {
     const int nchunk = s.part_chunks();
-    const int pv16 = z->pv_format == SAGE_PV_F16;
+    const int pv16 = z.v_store == kVF16;
     hipLaunchKernelGGL((prep_stats<In, D>), dim3(s.B * s.Hkv * nchunk), dim3(kThreads), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, s, z->k_part, z->v_part, z->sync,
-                       z->k_mean, z->v_scale, z->v_inv, pv16);
+                       (const uint16_t*)k, (const uint16_t*)v, s, z.k_part, z.v_part, z.sync,
+                       z.k_mean, z.v_scale, z.v_inv, pv16);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int per_head = s.Np / 64 + s.Np / SAGE_BN;
     hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, s, (int)z->k_block, z->k_mean,
-                       z->v_inv, z->k_i8, z->k_scale, z->v16, pv16);
+                       (const uint16_t*)k, (const uint16_t*)v, s, z.k_block, z.k_mean, z.v_inv,
+                       z.k_i8, z.k_scale, z.v, z.v_store);
     return hipGetLastError();
 }
 
@@ -372,7 +393,10 @@ static hipError_t launch_prep_t(const void* q, const void* k, const void* v, con
                        (int)z->q_block, z->q_i8, z->q_scale, z->sync);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_prep_kv_t<In, D>(k, v, s, z, st);
+    const KVViews kv = {z->k_i8,   z->k_scale, z->k_mean, z->v16,     z->v_scale,
+                        z->v_inv,  z->k_part,  z->v_part, z->sync,    z->k_block,
+                        z->pv_format == SAGE_PV_F16 ? kVF16 : kVE4M3Half};
+    return launch_prep_kv_t<In, D>(k, v, s, kv, st);
 }
 
 hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, const Shape& s,
@@ -384,9 +408,9 @@ hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, c
                      : launch_prep_t<Bf16Tag, 128>(q, k, v, s, z, st);
 }
 
-hipError_t launch_prep_kv(const void* k, const void* v, int dtype, const Shape& s,
-                          const sage_qkv_quant* z, hipStream_t st) {
-    hipLaunchKernelGGL(clear_words, dim3(1), dim3(kThreads), 0, st, z->sync, sync_words(s));
+hipError_t launch_prep_kv(const void* k, const void* v, int dtype, const Shape& s, const KVViews& z,
+                          hipStream_t st) {
+    hipLaunchKernelGGL(clear_words, dim3(1), dim3(kThreads), 0, st, z.sync, sync_words(s));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dtype == SAGE_F16)

@@ -8,11 +8,11 @@
 namespace sage {
 hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, const Shape& s,
                        const sage_qkv_quant* z, hipStream_t st);
-hipError_t launch_prep_kv(const void* k, const void* v, int dtype, const Shape& s,
-                          const sage_qkv_quant* z, hipStream_t st);
+hipError_t launch_prep_kv(const void* k, const void* v, int dtype, const Shape& s, const KVViews& z,
+                          hipStream_t st);
 hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal, float qk,
                        float l448, hipStream_t st);
-hipError_t launch_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out,
+hipError_t launch_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out,
                          float* part_o, float* part_ml, int B, int Hq, int Hkv, int Nq, int Nk,
                          int d, int causal, float qk, float l448, hipStream_t st);
 int prep_sync_words(const Shape& s);
@@ -37,12 +37,12 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout: each region starts on a 256-byte boundary.  A KV cache
-// (with_q false) has no Q regions.
+// (with_q false) has no Q regions, and v_bytes (1 or 2) per V element.
 struct Layout {
     size_t q_i8, q_scale, k_i8, k_scale, k_mean, v16, v_scale, v_inv, k_part, v_part, sync, total;
 };
 
-static Layout layout(const Shape& s, bool with_q = true) {
+static Layout layout(const Shape& s, bool with_q = true, size_t v_bytes = sizeof(uint16_t)) {
     Layout L;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -53,7 +53,7 @@ static Layout layout(const Shape& s, bool with_q = true) {
     const size_t Bq = (size_t)s.B * s.Hq, Bkv = (size_t)s.B * s.Hkv;
     L.q_i8 = with_q ? take((size_t)s.q_elems()) : 0;
     L.k_i8 = take((size_t)s.kv_elems());
-    L.v16 = take((size_t)s.kv_elems() * sizeof(uint16_t));
+    L.v16 = take((size_t)s.kv_elems() * v_bytes);
     // scales sized for the finer of the two granularities
     L.q_scale = with_q ? take(Bq * (s.Np / SAGE_BQ_THREAD) * sizeof(float)) : 0;
     L.k_scale = take(Bkv * (s.Np / SAGE_BK_THREAD) * sizeof(float));
@@ -74,15 +74,18 @@ static bool granularity_ok(int q_block, int k_block) {
 
 static bool pv_format_ok(int f) { return f == SAGE_PV_E4M3 || f == SAGE_PV_F16; }
 
-// The K/V half of a sage_qkv_quant (all a KV cache has).
-static int check_cache(const sage_qkv_quant* z) {
+static bool k_block_ok(int k_block) { return k_block == SAGE_BK || k_block == SAGE_BK_THREAD; }
+
+// Bytes per V element of a KV cache: E4M3 codes, or binary16.
+static size_t cache_v_bytes(int pv_format) { return pv_format == SAGE_PV_F16 ? 2 : 1; }
+
+static int check_cache(const sage_kv_cache* z) {
     if (!z) return SAGE_ERR_INVALID_ARG;
-    if ((z->k_block != SAGE_BK && z->k_block != SAGE_BK_THREAD) || !pv_format_ok(z->pv_format))
-        return SAGE_ERR_UNSUPPORTED;
-    if (!z->k_i8 || !z->k_scale || !z->k_mean || !z->v16 || !z->v_scale || !z->v_inv ||
-        !z->k_part || !z->v_part || !z->sync)
+    if (!k_block_ok(z->k_block) || !pv_format_ok(z->pv_format)) return SAGE_ERR_UNSUPPORTED;
+    if (!z->k_i8 || !z->k_scale || !z->k_mean || !z->v || !z->v_scale || !z->v_inv || !z->k_part ||
+        !z->v_part || !z->sync)
         return SAGE_ERR_INVALID_ARG;
-    if (!aligned(z->k_i8, 16) || !aligned(z->v16, 16) || !aligned(z->k_scale, 16) ||
+    if (!aligned(z->k_i8, 16) || !aligned(z->v, 16) || !aligned(z->k_scale, 16) ||
         !aligned(z->v_scale, 16) || !aligned(z->k_part, 8))
         return SAGE_ERR_INVALID_ARG;
     return SAGE_OK;
@@ -237,38 +240,37 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
                                   SAGE_BK, workspace, ws_bytes, stream);
 }
 
-size_t sage_kv_cache_bytes(int B, int Hkv, int Nk, int d) {
-    if (check_shape(B, Hkv, Hkv, Nk, d) != SAGE_OK) return 0;
-    return layout(sage::make_shape(B, Hkv, Hkv, Nk, d), false).total;
+size_t sage_kv_cache_bytes(int B, int Hkv, int Nk, int d, int pv_format) {
+    if (check_shape(B, Hkv, Hkv, Nk, d) != SAGE_OK || !pv_format_ok(pv_format)) return 0;
+    return layout(sage::make_shape(B, Hkv, Hkv, Nk, d), false, cache_v_bytes(pv_format)).total;
 }
 
-int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, sage_qkv_quant* out) {
+int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, int k_block,
+                        int pv_format, sage_kv_cache* out) {
     int rc = check_shape(B, Hkv, Hkv, Nk, d);
     if (rc != SAGE_OK) return rc;
+    if (!k_block_ok(k_block) || !pv_format_ok(pv_format)) return SAGE_ERR_UNSUPPORTED;
     if (!out) return SAGE_ERR_INVALID_ARG;
     if (!buf || !aligned(buf, 256)) return SAGE_ERR_WORKSPACE;
-    const Layout L = layout(sage::make_shape(B, Hkv, Hkv, Nk, d), false);
+    const Layout L = layout(sage::make_shape(B, Hkv, Hkv, Nk, d), false, cache_v_bytes(pv_format));
     if (bytes < L.total) return SAGE_ERR_WORKSPACE;
     char* base = (char*)buf;
-    out->q_i8 = NULL;
-    out->q_scale = NULL;
     out->k_i8 = (int8_t*)(base + L.k_i8);
     out->k_scale = (float*)(base + L.k_scale);
     out->k_mean = (float*)(base + L.k_mean);
-    out->v16 = (uint16_t*)(base + L.v16);
+    out->v = (void*)(base + L.v16);
     out->v_scale = (float*)(base + L.v_scale);
     out->v_inv = (float*)(base + L.v_inv);
     out->k_part = (double*)(base + L.k_part);
     out->v_part = (float*)(base + L.v_part);
     out->sync = (int32_t*)(base + L.sync);
-    out->q_block = SAGE_BQ_THREAD;
-    out->k_block = SAGE_BK;
-    out->pv_format = SAGE_PV_E4M3;
+    out->k_block = k_block;
+    out->pv_format = pv_format;
     return SAGE_OK;
 }
 
 int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
-                     const sage_qkv_quant* cache, void* stream) {
+                     const sage_kv_cache* cache, void* stream) {
     int rc = check_shape(B, Hkv, Hkv, Nk, d);
     if (rc != SAGE_OK) return rc;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
@@ -276,7 +278,11 @@ int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, in
     rc = check_cache(cache);
     if (rc != SAGE_OK) return rc;
     const Shape s = sage::make_shape(B, Hkv, Hkv, Nk, d);
-    hipError_t e = sage::launch_prep_kv(k, v, dtype, s, cache, (hipStream_t)stream);
+    const sage::KVViews kv = {cache->k_i8,   cache->k_scale, cache->k_mean, cache->v,
+                              cache->v_scale, cache->v_inv,  cache->k_part, cache->v_part,
+                              cache->sync,   cache->k_block,
+                              cache->pv_format == SAGE_PV_F16 ? sage::kVF16 : sage::kVE4M3Byte};
+    hipError_t e = sage::launch_prep_kv(k, v, dtype, s, kv, (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
@@ -285,7 +291,7 @@ size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d
     return decode_layout(B, Hq, Hkv, Nq, Nk, d).total;
 }
 
-int sage_attn_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out, int B,
+int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
                      int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
                      void* workspace, size_t ws_bytes, void* stream) {
     int rc = check_decode_shape(B, Hq, Hkv, Nq, Nk, d);

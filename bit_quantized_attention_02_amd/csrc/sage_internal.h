@@ -27,6 +27,25 @@ inline Shape make_shape(int B, int Hq, int Hkv, int N, int d) {
     return s;
 }
 
+// What the K/V half of the prep step writes, from either a full workspace
+// (sage_qkv_quant) or a KV cache (sage_kv_cache).  The V operand is stored
+// as the binary16 values of its E4M3 codes (the prefill workspace), as V's
+// own binary16 rounding (binary16 P.V), or as E4M3 code bytes (a KV cache).
+enum VStore { kVE4M3Half = 0, kVF16 = 1, kVE4M3Byte = 2 };
+struct KVViews {
+    int8_t* k_i8;
+    float* k_scale;
+    float* k_mean;
+    void* v;
+    float* v_scale;
+    float* v_inv;
+    double* k_part;
+    float* v_part;
+    int32_t* sync;
+    int k_block;
+    int v_store;
+};
+
 // Split of a short-query attention over a KV cache into work-groups: row
 // tiles of 32 packed (q head, query row) pairs per kv head, and chunks of
 // chunk_blocks consecutive key blocks (nchunk of them).  A pure function of

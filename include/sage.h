@@ -201,31 +201,55 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, in
 /*
  * ---- Short queries against a quantized KV cache (decode).
  *
- * A KV cache is the K/V half of sage_qkv_quant (the q_i8 and q_scale fields
- * are NULL), quantized once: K smoothed with its channel mean over the Nk
- * cached tokens and coded INT8 with one scale per k_block keys, V coded per
- * channel in the pv_format's values -- the operands the attention kernel
- * reads, at 3 bytes per K+V element pair instead of 4 for fp16/bf16 (the
- * memory claim of the Berkeley brief's checklist).  Appending tokens means
- * quantizing the cache again (the K mean and the V scales are global over
- * the cached tokens).
+ * A KV cache holds the K/V half of the prep step over Nk cached tokens,
+ * quantized once: K smoothed with its channel mean over those tokens and
+ * coded INT8 with one scale per k_block keys; V coded per channel, as one
+ * E4M3 code byte per element (SAGE_PV_E4M3) or as binary16 (SAGE_PV_F16).
+ * With E4M3 that is 2 bytes per K+V element pair instead of 4 for fp16/bf16
+ * (the memory claim of the Berkeley brief's checklist).  Appending tokens
+ * means quantizing the cache again: the K mean and the V scales are global
+ * over the cached tokens.
+ *
+ * Views of a cache (filled by sage_kv_cache_carve); N_p = Nk rounded up to
+ * SAGE_NPAD, rows Nk..N_p-1 zero padding:
+ *   k_i8    int8 [B, Hkv, N_p, d]            codes of K - k_mean
+ *   k_scale f32  [B, Hkv, N_p / k_block]
+ *   k_mean  f32  [B, Hkv, d]
+ *   v       [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: uint8 E4M3 codes (SAGE_PV_E4M3,
+ *           V * 448 / absmax_c) or binary16 values (SAGE_PV_F16), each block's
+ *           keys in the order of sage_v_key_position()
+ *   v_scale f32  [B, Hkv, d]                 absmax / 448 per channel (1 with SAGE_PV_F16)
+ *   v_inv, k_part, v_part, sync: working storage of sage_kv_quantize.
  */
+typedef struct {
+    int8_t* k_i8;
+    float* k_scale;
+    float* k_mean;
+    void* v;
+    float* v_scale;
+    float* v_inv;
+    double* k_part;
+    float* v_part;
+    int32_t* sync;
+    int32_t k_block;   /* SAGE_BK or SAGE_BK_THREAD */
+    int32_t pv_format; /* SAGE_PV_E4M3 or SAGE_PV_F16 */
+} sage_kv_cache;
 
-/* Bytes of a KV cache for [B, Hkv, Nk, d] (0 when the shape is invalid). */
-size_t sage_kv_cache_bytes(int B, int Hkv, int Nk, int d);
+/* Bytes of a KV cache for [B, Hkv, Nk, d] in this P.V format (0 when the
+ * shape or format is invalid). */
+size_t sage_kv_cache_bytes(int B, int Hkv, int Nk, int d, int pv_format);
 
-/* Split `buf` (device memory, 256-byte aligned, `bytes` long) into the K/V
- * views of `cache`; q_i8 and q_scale become NULL, k_block SAGE_BK and
- * pv_format SAGE_PV_E4M3, which the caller may switch to SAGE_BK_THREAD and
- * SAGE_PV_F16 before quantizing.  Host-only; no HIP call. */
-int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d,
-                        sage_qkv_quant* cache);
+/* Split `buf` (device memory, 256-byte aligned, `bytes` long) into the views of
+ * `cache` for this K granularity (k_block = SAGE_BK or SAGE_BK_THREAD) and P.V
+ * format.  Host-only; no HIP call. */
+int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, int k_block,
+                        int pv_format, sage_kv_cache* cache);
 
 /* The K/V half of sage_quantize: K mean, smoothing, INT8 K, V codes, from
  * fp16/bf16 K, V [B, Hkv, Nk, d] into `cache`.  Runs as three kernels on
  * `stream` (counter clearing, statistics, codes). */
 int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
-                     const sage_qkv_quant* cache, void* stream);
+                     const sage_kv_cache* cache, void* stream);
 
 /* Workspace bytes sage_attn_decode needs for this shape (at least 256; 0 when
  * the shape is invalid). */
@@ -244,7 +268,7 @@ size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d
  * second kernel in `workspace` (device memory, 256-byte aligned) when there is
  * more than one chunk.
  */
-int sage_attn_decode(const void* q, int dtype, const sage_qkv_quant* cache, float* out, int B,
+int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
                      int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
                      void* workspace, size_t ws_bytes, void* stream);
 

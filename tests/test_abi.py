@@ -191,33 +191,48 @@ def test_pv_format_is_validated(sage):
 
 
 def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
-    """The KV-cache and short-query calls: sizes, carving (no Q regions) and
-    argument checks before any HIP call."""
+    """The KV-cache and short-query calls: sizes, carving and argument checks
+    before any HIP call."""
     L = sage._lib
     fake = 1 << 40
     f = ctypes.c_float
     assert sage.sage_kv_cache_bytes(1, 2, 300, 64) > 0
     assert sage.sage_kv_cache_bytes(1, 2, 300, 80) == 0
     assert sage.sage_kv_cache_bytes(1, 2, 0, 64) == 0
-    # a cache is smaller than a full workspace of the same shape (no Q)
-    assert sage.sage_kv_cache_bytes(1, 2, 300, 64) < sage.sage_workspace_bytes(1, 2, 2, 300, 64)
+    assert L.sage_kv_cache_bytes(1, 2, 300, 64, 7) == 0
+    # E4M3 V takes one byte per element, binary16 two; both less than a full
+    # workspace of the same shape (no Q)
+    e8, e16 = sage.sage_kv_cache_bytes(1, 2, 512, 64), sage.sage_kv_cache_bytes(1, 2, 512, 64, "f16")
+    assert e16 - e8 == 2 * 512 * 64
+    assert e16 < sage.sage_workspace_bytes(1, 2, 2, 512, 64)
     need = sage.sage_kv_cache_bytes(1, 2, 300, 64)
     z = sage.sage_kv_cache_carve(fake, need, 1, 2, 300, 64)
-    assert z.q_i8 is None and z.q_scale is None
-    ptrs = [getattr(z, n) for n in ("k_i8", "k_scale", "k_mean", "v16", "v_scale", "v_inv", "k_part",
-                                    "v_part", "sync")]
-    assert all(p % 256 == 0 for p in ptrs) and max(ptrs) < fake + need
+    ptrs = [getattr(z, n) for n, t in sage.sage_kv_cache._fields_ if t is ctypes.c_void_p]
+    assert len(ptrs) == 9
+    assert all(p % 256 == 0 for p in ptrs) and len(set(ptrs)) == 9 and max(ptrs) < fake + need
     assert (z.k_block, z.pv_format) == (64, 0)
+    zt = sage.sage_kv_cache_carve(fake, need, 1, 2, 300, 64, granularity="thread")
+    assert zt.k_block == 32
     with pytest.raises(sage.SageError):
         sage.sage_kv_cache_carve(fake, need - 1, 1, 2, 300, 64)
+    with pytest.raises(sage.SageError):
+        sage.sage_kv_cache_carve(fake, need, 1, 2, 300, 64, pv="f16")  # needs the larger size
+    c = sage.sage_kv_cache()
+    assert L.sage_kv_cache_carve(fake, need, 1, 2, 300, 64, 128, 0, ctypes.byref(c)) == sage.SAGE_ERR_UNSUPPORTED
+    assert L.sage_kv_cache_carve(fake, need, 1, 2, 300, 64, 64, 3, ctypes.byref(c)) == sage.SAGE_ERR_UNSUPPORTED
+    assert L.sage_kv_cache_carve(fake + 16, need, 1, 2, 300, 64, 64, 0, ctypes.byref(c)) == sage.SAGE_ERR_WORKSPACE
     zp = ctypes.byref(z)
     # sage_kv_quantize
     assert L.sage_kv_quantize(fake, None, 0, 1, 2, 300, 64, zp, None) == sage.SAGE_ERR_INVALID_ARG
     assert L.sage_kv_quantize(fake, fake, 2, 1, 2, 300, 64, zp, None) == sage.SAGE_ERR_INVALID_ARG
     assert L.sage_kv_quantize(fake, fake, 0, 1, 2, 300, 96, zp, None) == sage.SAGE_ERR_UNSUPPORTED
-    bad = sage.sage_qkv_quant.from_buffer_copy(z)
+    assert L.sage_kv_quantize(fake, fake, 0, 1, 2, 300, 64, None, None) == sage.SAGE_ERR_INVALID_ARG
+    bad = sage.sage_kv_cache.from_buffer_copy(z)
     bad.k_block = 128
     assert L.sage_kv_quantize(fake, fake, 0, 1, 2, 300, 64, ctypes.byref(bad), None) == sage.SAGE_ERR_UNSUPPORTED
+    nov = sage.sage_kv_cache.from_buffer_copy(z)
+    nov.v = None
+    assert L.sage_kv_quantize(fake, fake, 0, 1, 2, 300, 64, ctypes.byref(nov), None) == sage.SAGE_ERR_INVALID_ARG
     # decode workspace
     assert sage.sage_decode_workspace_bytes(1, 8, 2, 1, 300, 64) >= 256
     assert sage.sage_decode_workspace_bytes(1, 8, 2, 0, 300, 64) == 0
@@ -243,6 +258,6 @@ def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
     assert dec(ws=fake + 64) == sage.SAGE_ERR_WORKSPACE
     assert dec(n=wsb - 1) == sage.SAGE_ERR_WORKSPACE
     assert dec(c=ctypes.byref(bad)) == sage.SAGE_ERR_UNSUPPORTED
-    bad2 = sage.sage_qkv_quant.from_buffer_copy(z)
+    bad2 = sage.sage_kv_cache.from_buffer_copy(z)
     bad2.pv_format = 5
     assert dec(c=ctypes.byref(bad2)) == sage.SAGE_ERR_UNSUPPORTED

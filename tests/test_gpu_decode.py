@@ -1,10 +1,10 @@
 """GPU parity of the short-query path over a quantized KV cache (through the
 C ABI) against the CPU oracle.
 
-The cache (K mean, INT8 K and its scales, V codes) must be bit-exact against
-the oracle's K/V half of the prep.  The attention output must lie within the
-oracle's interval (see test_gpu_parity.py) up to max-abs 2e-3 and rel-L1
-1e-3.  Cases cover one and several query rows, GQA packing of up to several
+The cache (K mean, INT8 K and its scales, V as E4M3 code bytes or binary16)
+must be bit-exact against the oracle's K/V half of the prep.  The attention
+output must lie within the oracle's interval (see test_gpu_parity.py) up to
+max-abs 2e-3 and rel-L1 1e-3.  Cases cover one and several query rows, GQA packing of up to several
 32-row tiles, caches that take one key chunk (the kernel writes the output)
 and many (the merge kernel does), ragged key counts, both K granularities and
 both P.V formats.
@@ -42,7 +42,7 @@ def run_decode(sage, q, k, v, causal, sm_scale, granularity="block", pv="e4m3"):
     out = cache.attend(qd, causal=causal, sm_scale=sm_scale)
     torch.cuda.synchronize()
     B, Hkv, Nk, d = k.shape
-    quant = sage.read_quantized(cache.z, cache.buf, B, 0, Hkv, Nk, d)
+    quant = sage.read_kv_cache(cache.z, cache.buf, B, Hkv, Nk, d)
     return out, quant
 
 
@@ -65,6 +65,8 @@ def check_cache(orc, quant, oz):
         np.testing.assert_array_equal(quant["v_fp8"].numpy(), oz["v_fp8"])
         np.testing.assert_array_equal(quant["v_scale"].numpy(), oz["v_scale"])
     assert not quant["k_pad"].any() and not quant["v_pad"].any()
+    vals = orc.f16_decode(oz["v_f16"]) if oz["pv"] == "f16" else orc.e4m3_decode(oz["v_fp8"])
+    np.testing.assert_array_equal(quant["v_half"].to(torch.float64).numpy(), vals)
 
 
 def check_attn(orc, got, oz, causal, sm_scale, rows=None):
@@ -138,8 +140,8 @@ def test_cache_on_a_used_buffer(sage, orc):
     b.buf.fill_(0xFF)
     sage.sage_kv_quantize(kd, vd, b.z)
     torch.cuda.synchronize()
-    qa = sage.read_quantized(a.z, a.buf, B, 0, Hkv, Nk, d)
-    qb = sage.read_quantized(b.z, b.buf, B, 0, Hkv, Nk, d)
+    qa = sage.read_kv_cache(a.z, a.buf, B, Hkv, Nk, d)
+    qb = sage.read_kv_cache(b.z, b.buf, B, Hkv, Nk, d)
     for key in ("k_i8", "v_half", "k_mean", "v_scale", "k_scale"):
         assert torch.equal(qa[key], qb[key]), key
 
