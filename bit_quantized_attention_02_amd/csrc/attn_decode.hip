@@ -38,35 +38,36 @@ struct DecodeArgs {
     float qk, l448;
 };
 
-// INT8 codes of one query row, quantized with one scale for the row.  Lane
-// (r32, h) holds elements [32 ks + 16 h, +16) of its row for each ks, i.e.
-// exactly the bytes of its Q.K^T operand; the two lanes of a row agree on the
-// row's absmax through one permlane32 swap.  The codes and the scale use the
-// float32 operations of the prep step: scale = absmax / 127, codes
+// This lane's part of one query row: elements [32 ks + 16 h, +16) for each
+// ks, i.e. exactly the bytes of its Q.K^T operand (zeros for a padding lane).
+template <int D>
+__device__ inline void load_q_row(const uint16_t* __restrict__ qrow, bool valid, int h,
+                                  uint4 (&raw)[D / 16]) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        const int ks = j >> 1, half = j & 1;
+        raw[j] = valid ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 16 * h + 8 * half)
+                       : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// INT8 codes of the row, with one scale for the row; the two lanes of a row
+// agree on its absmax through one permlane32 swap.  The codes and the scale
+// use the float32 operations of the prep step: scale = absmax / 127, codes
 // rne(x * (127 / absmax)) clamped to +-127.
 template <typename In, int D>
-__device__ inline float quantize_q_row(const uint16_t* __restrict__ qrow, bool valid, int h,
-                                       v4i (&qf)[D / 32]) {
+__device__ inline float quantize_q_row(const uint4 (&raw)[D / 16], v4i (&qf)[D / 32]) {
     constexpr int KS = D / 32;
     float x[KS][16];
     float am = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int j = 0; j < D / 16; ++j) {
+        float f[8];
+        unpack8<In>(raw[j], f);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            float f[8];
-            if (valid) {
-                const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 16 * h + 8 * half);
-                unpack8<In>(u, f);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = 0.0f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                x[ks][8 * half + e] = f[e];
-                am = fmaxf(am, fabsf(f[e]));
-            }
+        for (int e = 0; e < 8; ++e) {
+            x[j >> 1][8 * (j & 1) + e] = f[e];
+            am = fmaxf(am, fabsf(f[e]));
         }
     }
     // non-negative floats order like their bit patterns
@@ -93,16 +94,33 @@ constexpr int cache_vb() {
     return PV16 ? 2 : 1;
 }
 
+// LDS tile buffers per work-group.  A decode wave needs more than half the
+// register file, so a CU runs at most one per SIMD, four in all; at d = 128 a
+// second buffer would leave LDS for only two of them.  With one buffer the
+// next block's copy waits for the current block's products, and the other
+// waves of the CU cover that wait.
+template <int D>
+constexpr int decode_bufs() {
+    return D == 128 ? 1 : 2;
+}
+constexpr int kDecodeWavesPerCU = 4;
+
+template <int D, bool PV16>
+constexpr size_t decode_lds() {
+    return (size_t)decode_bufs<D>() * (SAGE_BN * D + D * SAGE_BN * cache_vb<PV16>());
+}
+
 template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
 __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     constexpr int CT = D / 32;
     constexpr int VB = cache_vb<PV16>();
     constexpr bool V8 = VB == 1;
+    constexpr int NBUF = decode_bufs<D>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* const lk0 = smem;
-    uint8_t* const lk1 = smem + SAGE_BN * D;
-    uint8_t* const lv0 = smem + 2 * SAGE_BN * D;
-    uint8_t* const lv1 = lv0 + D * SAGE_BN * VB;
+    uint8_t* const lk1 = smem + (NBUF - 1) * SAGE_BN * D;
+    uint8_t* const lv0 = smem + NBUF * SAGE_BN * D;
+    uint8_t* const lv1 = lv0 + (NBUF - 1) * D * SAGE_BN * VB;
 
     const int lane = threadIdx.x;
     const int h = lane >> 5, r32 = lane & 31;
@@ -126,9 +144,6 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     // the row's last allowed key (causal: bottom-right aligned)
     const int pos = CAUSAL && valid ? a.Nk - a.Nq + i : a.Nk - 1;
 
-    v4i qf[D / 32];
-    const float sq = quantize_q_row<In, D>(a.q + grow * D, valid, h, qf);
-
     const int nkb = (a.Nk + SAGE_BN - 1) / SAGE_BN;
     const int T0 = chunk * a.chunk_blocks;
     const int T1 = min(nkb, T0 + a.chunk_blocks);
@@ -147,19 +162,34 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) O[ct][v] = 0.0f;
 
+    // the query row and the first block's scales are loaded before the first
+    // block's copy goes out (waits count in issue order), so the row is
+    // quantized while the copy is in flight
+    uint4 qraw[D / 16];
+    load_q_row<D>(a.q + grow * D, valid, h, qraw);
     typedef float kvec __attribute__((ext_vector_type(KSPLIT)));
     kvec kscale = *reinterpret_cast<const kvec*>(ksc + KSPLIT * T0);
     const TileLoader<D, 1, VB> tiles(kbase, vbase, a.Np, 0, lane);
     tiles.load(T0, lk0, lv0, 0);
+    // keep the quantization between the copy's issue and its wait: nothing
+    // is scheduled across the barrier, and the empty asm statements take the
+    // codes and scale as operands, so their computation cannot sink below
+    // the wait
+    __builtin_amdgcn_sched_barrier(0);
+    v4i qf[D / 32];
+    float sq = quantize_q_row<In, D>(qraw, qf);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+    asm volatile("" : "+v"(sq));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int T = T0; T < T1; ++T) {
-        const bool odd = (T - T0) & 1;
+        const bool odd = NBUF == 2 && ((T - T0) & 1);
         const bool more = T + 1 < T1;
         // the next block's K scales before its tile copy (waits count in
         // issue order)
         const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
-        if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, 0);
+        if (NBUF == 2 && more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, 0);
         float c[KSPLIT];
 #pragma unroll
         for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * kscale[gg]) * a.qk;
@@ -170,6 +200,11 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
             attn_block<D, KSPLIT, CAUSAL, PV16, true, V8>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
                                                           a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
+        if (NBUF == 1 && more) {
+            // every LDS read of this block has been consumed by its products
+            __syncthreads();
+            tiles.load(T + 1, lk0, lv0, 0);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
@@ -213,7 +248,7 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
 // chunk weights are formed once (one thread per chunk), then every
 // (chunk, channel) partial is read by its own thread, so all loads are in
 // flight together, and the sums are reduced in LDS.
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a) {
@@ -258,10 +293,24 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a) {
     if (t == 0) s_l = red[0];
     __syncthreads();
 
-    // O: thread t sums channel t % D over chunks k = t / D (mod GROUPS)
+    // O: thread t sums channel t % D over chunks k = t / D (mod GROUPS),
+    // eight chunks' loads issued together
     const int c = t % D, grp = t / D;
     float o = 0.0f;
-    for (int k = grp; k < a.nchunk; k += GROUPS) {
+    int k = grp;
+    for (; k + 7 * GROUPS < a.nchunk; k += 8 * GROUPS) {
+        float x[8], w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = po[(long long)(k + u * GROUPS) * D + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int kk = k + u * GROUPS;
+            w[u] = kk < kMergeThreads ? wgt[kk] : __builtin_amdgcn_exp2f(ml[2 * kk] - M);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o = __builtin_fmaf(x[u], w[u], o);
+    }
+    for (; k < a.nchunk; k += GROUPS) {
         const float w = k < kMergeThreads ? wgt[k] : __builtin_amdgcn_exp2f(ml[2 * k] - M);
         o = __builtin_fmaf(po[(long long)k * D + c], w, o);
     }
@@ -292,13 +341,11 @@ SAGE_DECODE_INST_K(Bf16Tag, 128)
 template __global__ void decode_merge<64>(DecodeArgs);
 template __global__ void decode_merge<128>(DecodeArgs);
 
-// Chunking: enough work-groups to keep every CU streaming the cache (the
-// double-buffered tiles of an E4M3 cache, 2 bytes per K+V element pair, let
-// 5 one-wave work-groups share a CU's LDS at d = 64 and 2 at d = 128; a
-// binary16 cache, 3 bytes, fits fewer and is split the same way), in chunks of
+// Chunking: enough work-groups for two rounds of kDecodeWavesPerCU per CU (a
+// binary16 cache fits fewer at once and is split the same way), in chunks of
 // at least kMinChunkBlocks blocks so that filling each work-group's two-tile
 // pipeline stays a small part of its work.
-constexpr int kMinChunkBlocks = 4;
+constexpr int kMinChunkBlocks = 2;
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     DecodePlan pl;
@@ -306,9 +353,8 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     pl.row_tiles = (G * Nq + 31) / 32;
     const int nkb = (Nk + SAGE_BN - 1) / SAGE_BN;
     const long long units = (long long)B * Hkv * pl.row_tiles;
-    const long long lds = 2LL * SAGE_BN * d * 2;
-    const long long per_cu = 163840 / lds;
-    const long long target = 2LL * 256 * per_cu;
+    (void)d;
+    const long long target = 2LL * 256 * kDecodeWavesPerCU;
     long long want = (target + units - 1) / units;
     int per = (int)((nkb + want - 1) / want);
     if (per < kMinChunkBlocks) per = kMinChunkBlocks;
@@ -320,7 +366,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 
 template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * cache_vb<PV16>();
+    constexpr size_t lds = decode_lds<D, PV16>();
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)attn_decode<In, D, KSPLIT, CAUSAL, PV16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
