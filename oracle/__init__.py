@@ -67,11 +67,11 @@ def _load():
         lib.oracle_f16_encode.argtypes = [dd]
         lib.oracle_f16_encode_array.argtypes = [P, l, P]
         lib.oracle_f16_decode_array.argtypes = [P, l, P]
-        lib.oracle_quantize.argtypes = [P, P, P, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
-        lib.oracle_quantize_q.argtypes = [P, i, i, i, i, i, P, P]
-        lib.oracle_quantize_kv.argtypes = [P, P, i, i, i, i, i, i, P, P, P, P, P]
-        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, i, f, dd,
-                                      P, l, P, P, P, P]
+        lib.oracle_quantize.argtypes = [P, P, P, i, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
+        lib.oracle_quantize_q.argtypes = [P, i, i, i, i, i, i, P, P]
+        lib.oracle_quantize_kv.argtypes = [P, P, i, i, i, i, i, i, i, P, P, P, P, P]
+        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, i, i, f,
+                                      dd, P, l, P, P, P, P]
         lib.oracle_attn_f64.argtypes = [P, P, P, i, i, i, i, i, i, i, dd, P, l, P]
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -127,19 +127,25 @@ def f16_decode(c) -> np.ndarray:
 PV_FORMATS = ("e4m3", "f16")
 
 
-def quantize_q(q, bq: int = BQ) -> dict:
-    """The Q half of the prep step on [B,Hq,Nq,d]: INT8 codes and one scale
-    per bq rows (see oracle_quantize_q in oracle.c)."""
+# largest integer code of the Q, K formats: INT8, and the INT4 of the 4-bit variant
+QK_MAX = {8: 127, 4: 7}
+
+
+def quantize_q(q, bq: int = BQ, qk_bits: int = 8) -> dict:
+    """The Q half of the prep step on [B,Hq,Nq,d]: integer codes (INT8, or
+    INT4 values with qk_bits=4) and one scale per bq rows (see
+    oracle_quantize_q in oracle.c)."""
     q = to_f32(q)
     B, Hq, Nq, d = q.shape
     r = dict(q_i8=np.empty((B, Hq, Nq, d), np.int8),
              q_scale=np.empty((B, Hq, -(-Nq // bq)), np.float32))
-    _load().oracle_quantize_q(_ptr(q), B, Hq, Nq, d, bq, _ptr(r["q_i8"]), _ptr(r["q_scale"]))
-    r.update(B=B, Hq=Hq, Nq=Nq, d=d, bq=bq)
+    _load().oracle_quantize_q(_ptr(q), B, Hq, Nq, d, bq, QK_MAX[qk_bits], _ptr(r["q_i8"]),
+                              _ptr(r["q_scale"]))
+    r.update(B=B, Hq=Hq, Nq=Nq, d=d, bq=bq, qk_bits=qk_bits)
     return r
 
 
-def quantize_kv(k, v, bk: int = BK, smooth: bool = True, pv: str = "e4m3") -> dict:
+def quantize_kv(k, v, bk: int = BK, smooth: bool = True, pv: str = "e4m3", qk_bits: int = 8) -> dict:
     """The K/V half of the prep step on [B,Hkv,Nk,d] (a quantized KV cache):
     K mean, smoothed INT8 K with one scale per bk keys, and V as E4M3 codes
     with per-channel scales, or with pv="f16" also v_f16, the binary16 codes
@@ -152,21 +158,23 @@ def quantize_kv(k, v, bk: int = BK, smooth: bool = True, pv: str = "e4m3") -> di
              k_scale=np.empty((B, Hkv, -(-Nk // bk)), np.float32),
              k_mean=np.empty((B, Hkv, d), np.float32), v_fp8=np.empty((B, Hkv, Nk, d), np.uint8),
              v_scale=np.empty((B, Hkv, d), np.float32))
-    _load().oracle_quantize_kv(_ptr(k), _ptr(v), B, Hkv, Nk, d, bk, int(smooth), _ptr(r["k_i8"]),
+    _load().oracle_quantize_kv(_ptr(k), _ptr(v), B, Hkv, Nk, d, bk, QK_MAX[qk_bits], int(smooth),
+                               _ptr(r["k_i8"]),
                                _ptr(r["k_scale"]), _ptr(r["k_mean"]), _ptr(r["v_fp8"]),
                                _ptr(r["v_scale"]))
     if pv == "f16":
         r["v_f16"] = f16_encode(v)
-    r.update(B=B, Hkv=Hkv, Nk=Nk, d=d, bk=bk, pv=pv)
+    r.update(B=B, Hkv=Hkv, Nk=Nk, d=d, bk=bk, pv=pv, qk_bits=qk_bits)
     return r
 
 
-def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True, pv: str = "e4m3") -> dict:
+def quantize(q, k, v, bq: int = BQ, bk: int = BK, smooth: bool = True, pv: str = "e4m3",
+             qk_bits: int = 8) -> dict:
     """The prep step on [B,H,N,d] inputs (both halves, same N).  Returns codes
     in the plain logical layout [B,H,N,d] and the scales (see oracle_quantize
     in oracle.c)."""
-    r = quantize_q(q, bq)
-    r.update(quantize_kv(k, v, bk, smooth, pv))
+    r = quantize_q(q, bq, qk_bits)
+    r.update(quantize_kv(k, v, bk, smooth, pv, qk_bits))
     r["N"] = r["Nk"]
     return r
 
@@ -178,6 +186,7 @@ def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
     positions) for the given flattened rows (None = all), in the P.V format
     qz["pv"] was made for.  Returns (out, lo, hi, flagged), float64 [nrows, d]."""
     f16 = qz.get("pv", "e4m3") == "f16"
+    seeded = qz.get("qk_bits", 8) == 8
     v_codes = qz["v_f16"] if f16 else qz["v_fp8"]
     v_scale = None if f16 else qz["v_scale"]
     B, Hq, Hkv, Nq, Nk, d = qz["B"], qz["Hq"], qz["Hkv"], qz["Nq"], qz["Nk"], qz["d"]
@@ -193,7 +202,7 @@ def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
     hi = np.empty((nrows, d), np.float64) if interval else None
     flagged = np.empty(nrows, np.int64) if interval else None
     _load().oracle_attn_q(_ptr(qz["q_i8"]), _ptr(qz["q_scale"]), _ptr(qz["k_i8"]),
-                          _ptr(qz["k_scale"]), _ptr(v_codes), _ptr(v_scale), int(f16),
+                          _ptr(qz["k_scale"]), _ptr(v_codes), _ptr(v_scale), int(f16), int(seeded),
                           B, Hq, Hkv, Nq, Nk, d, qz["bq"], qz["bk"], bn, int(causal),
                           float(sm_scale), float(tau), _ptr(rows), nrows,
                           _ptr(out), _ptr(lo), _ptr(hi), _ptr(flagged))

@@ -22,6 +22,13 @@
  * HIP path implements too):
  *   - INT8 is symmetric, range +-127, round-to-nearest-even of x*(127/absmax)
  *     evaluated in float32; an all-zero block gets scale 0 and codes 0.
+ *   - The 4-bit Q, K of SageAttention2 (INT4; the Berkeley brief's comparison
+ *     table) are the same with 7 in place of 127: codes in [-7, 7], scale
+ *     absmax/7.  The codes are stored one per byte and multiplied like the
+ *     INT8 codes.  Their scores are evaluated without the 1.5*2^23 offset
+ *     below (seeded = 0: F = acc, u = 0): the float32 rounding of that offset
+ *     is about one integer step of c, negligible at INT8 scales but not at
+ *     INT4 scales, which are about 330 times larger.
  *   - E4M3 is OCP E4M3FN (bias 7, max 448, subnormal step 2^-9), RNE,
  *     saturating at +-448; V codes are e4m3(v * (448/absmax_c)) in float32.
  *   - The P block is one query row by `bn` keys.  Its scale is the block
@@ -150,8 +157,10 @@ void oracle_f16_decode_array(const uint16_t* c, long n, double* out) {
 
 /* ------------------------------------------------------------ quantisation */
 
-/* Symmetric INT8 of one block of `count` float32 values. */
-static void quant_block_i8(const float* x, long count, int8_t* out, float* scale) {
+/* Symmetric integer codes of one block of `count` float32 values, in
+ * [-qmax, qmax] (qmax = 127 for INT8, 7 for INT4). */
+static void quant_block_i8(const float* x, long count, int qmax, int8_t* out, float* scale) {
+    const float qm = (float)qmax;
     float a = 0.0f;
     for (long i = 0; i < count; ++i) {
         float m = fabsf(x[i]);
@@ -162,12 +171,12 @@ static void quant_block_i8(const float* x, long count, int8_t* out, float* scale
         memset(out, 0, (size_t)count);
         return;
     }
-    float inv = 127.0f / a;
-    *scale = a / 127.0f;
+    float inv = qm / a;
+    *scale = a / qm;
     for (long i = 0; i < count; ++i) {
         float t = rintf(x[i] * inv);
-        if (t > 127.0f) t = 127.0f;
-        if (t < -127.0f) t = -127.0f;
+        if (t > qm) t = qm;
+        if (t < -qm) t = -qm;
         out[i] = (int8_t)t;
     }
 }
@@ -185,8 +194,8 @@ static void quant_block_i8(const float* x, long count, int8_t* out, float* scale
  *   v_fp8 [B,Hkv,N,d] (E4M3 codes), v_scale [B,Hkv,d]
  * smooth = 0 skips the K mean (ablation only; k_mean is then all zero).
  */
-void oracle_quantize_q(const float* q, int B, int Hq, int N, int d, int bq, int8_t* q_i8,
-                       float* q_scale) {
+void oracle_quantize_q(const float* q, int B, int Hq, int N, int d, int bq, int qmax,
+                       int8_t* q_i8, float* q_scale) {
     const long nd = (long)N * d;
     const int nqb = (N + bq - 1) / bq;
     /* one scale per (b, h, block of bq rows) */
@@ -194,14 +203,14 @@ void oracle_quantize_q(const float* q, int B, int Hq, int N, int d, int bq, int8
     for (int bh = 0; bh < B * Hq; ++bh)
         for (int t = 0; t < nqb; ++t) {
             long r0 = (long)t * bq, r1 = r0 + bq < N ? r0 + bq : N;
-            quant_block_i8(q + bh * nd + r0 * d, (r1 - r0) * d, q_i8 + bh * nd + r0 * d,
+            quant_block_i8(q + bh * nd + r0 * d, (r1 - r0) * d, qmax, q_i8 + bh * nd + r0 * d,
                            q_scale + (long)bh * nqb + t);
         }
 }
 
 void oracle_quantize_kv(const float* k, const float* v, int B, int Hkv, int N, int d, int bk,
-                        int smooth, int8_t* k_i8, float* k_scale, float* k_mean, uint8_t* v_fp8,
-                        float* v_scale) {
+                        int qmax, int smooth, int8_t* k_i8, float* k_scale, float* k_mean,
+                        uint8_t* v_fp8, float* v_scale) {
     const long nd = (long)N * d;
     const int nkb = (N + bk - 1) / bk;
 
@@ -222,7 +231,7 @@ void oracle_quantize_kv(const float* k, const float* v, int B, int Hkv, int N, i
             for (int c = 0; c < d; ++c) ks[n * d + c] = kh[n * d + c] - mean[c];
         for (int t = 0; t < nkb; ++t) {
             long r0 = (long)t * bk, r1 = r0 + bk < N ? r0 + bk : N;
-            quant_block_i8(ks + r0 * d, (r1 - r0) * d, k_i8 + bg * nd + r0 * d,
+            quant_block_i8(ks + r0 * d, (r1 - r0) * d, qmax, k_i8 + bg * nd + r0 * d,
                            k_scale + (long)bg * nkb + t);
         }
         free(ks);
@@ -250,11 +259,11 @@ void oracle_quantize_kv(const float* k, const float* v, int B, int Hkv, int N, i
 }
 
 void oracle_quantize(const float* q, const float* k, const float* v,
-                     int B, int Hq, int Hkv, int N, int d, int bq, int bk, int smooth,
+                     int B, int Hq, int Hkv, int N, int d, int bq, int bk, int qmax, int smooth,
                      int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
                      float* k_mean, uint8_t* v_fp8, float* v_scale) {
-    oracle_quantize_q(q, B, Hq, N, d, bq, q_i8, q_scale);
-    oracle_quantize_kv(k, v, B, Hkv, N, d, bk, smooth, k_i8, k_scale, k_mean, v_fp8, v_scale);
+    oracle_quantize_q(q, B, Hq, N, d, bq, qmax, q_i8, q_scale);
+    oracle_quantize_kv(k, v, B, Hkv, N, d, bk, qmax, smooth, k_i8, k_scale, k_mean, v_fp8, v_scale);
 }
 
 /* ------------------------------------------------- quantised attention */
@@ -279,6 +288,9 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  *            O[c] = sum_t w_t A_t[c],  l = sum_t w_t R_t
  *   out[c] = O[c] * sv[c] / l
  *
+ * seeded = 0 (the 4-bit Q, K variant) evaluates the scores without the offset:
+ * F_j = acc_j and u_j = 0 in every formula above.
+ *
  * pv_f16 = 1 selects the binary16 P.V mode: v_codes holds binary16 codes of V
  * (uint16), v_scale may be NULL (sv = 1), f32(log2 448) above is replaced by 0
  * and P16_j = f16(y_j) replaces P8_j; the rest is unchanged.
@@ -292,7 +304,7 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  */
 void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                    const float* k_scale, const void* v_codes, const float* v_scale, int pv_f16,
-                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int bq, int bk, int bn,
+                   int seeded, int B, int Hq, int Hkv, int Nq, int Nk, int d, int bq, int bk, int bn,
                    int causal, float sm_scale, double tau, const int64_t* rows, long nrows,
                    double* out, double* out_lo, double* out_hi, int64_t* flagged) {
     const long qnd = (long)Nq * d, nd = (long)Nk * d;
@@ -302,7 +314,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
     const float qk = (float)((double)sm_scale * 1.4426950408889634); /* log2(e) */
     /* the P block scale: the block maximum maps to 448 (E4M3) or to 1 (binary16) */
     const float l448 = pv_f16 ? 0.0f : (float)log2(448.0);
-    const float seed = 12582912.0f; /* 1.5 * 2^23 */
+    const float seed = seeded ? 12582912.0f : 0.0f; /* 1.5 * 2^23 */
+    const int32_t seed_int = seeded ? 12582912 : 0;
     /* decoded value of every code of the P.V format, and its largest finite
      * positive code */
     const int ncode = pv_f16 ? 65536 : 256;
@@ -350,7 +363,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 acc[j] = s;
                 float sqk = sq * skh[j / bk];
                 cj[j] = sqk * qk;
-                Fj[j] = (float)(12582912 + s);
+                Fj[j] = (float)(seed_int + s);
                 uj[j] = seed * cj[j];
             }
             /* per-block maximum score: the P scale of the block */

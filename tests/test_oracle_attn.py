@@ -193,9 +193,11 @@ def _online_reference(orc, z, causal, sm_scale, bn):
                         accs.append(acc)
                         cs.append(c)
                     # the score enters float32 as F = 1.5 2^23 + acc (exact),
-                    # with the constant's product u = f32(1.5 2^23 c) taken off
-                    Fs = [np.float32(12582912 + a) for a in accs]
-                    us = [np.float32(np.float32(12582912.0) * c) for c in cs]
+                    # with the constant's product u = f32(1.5 2^23 c) taken
+                    # off; the 4-bit variant takes F = acc, u = 0
+                    seed = 12582912 if z.get("qk_bits", 8) == 8 else 0
+                    Fs = [np.float32(seed + a) for a in accs]
+                    us = [np.float32(np.float32(seed) * c) for c in cs]
                     mt = max(_fma_f32(F, c, -u) for F, c, u in zip(Fs, cs, us))
                     a_blk = np.zeros(d)
                     r_blk = 0.0
@@ -215,16 +217,16 @@ def _online_reference(orc, z, causal, sm_scale, bn):
     return out
 
 
-@pytest.mark.parametrize("pv", ["e4m3", "f16"])
+@pytest.mark.parametrize("pv,qk_bits", [("e4m3", 8), ("f16", 8), ("e4m3", 4)])
 @pytest.mark.parametrize("N", [1, 2, 3, 5, 16])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d,G", [(64, 1), (128, 4)])
-def test_closed_form_equals_online_recurrence_tiny(orc, N, causal, d, G, pv):
+def test_closed_form_equals_online_recurrence_tiny(orc, N, causal, d, G, pv, qk_bits):
     """The oracle's closed form over P blocks equals the online recurrence
     (running max, rescaled accumulator) with small blocks so several blocks and
     ragged tails occur (bq=4, bk=2, bn=4)."""
     q, k, v = workloads.random_inputs(1, G, 1, N, d, "bf16", seed=100 + N + d, scale=1.5)
-    z = orc.quantize(q, k, v, bq=4, bk=2, pv=pv)
+    z = orc.quantize(q, k, v, bq=4, bk=2, pv=pv, qk_bits=qk_bits)
     out, lo, hi, fl = orc.attn_q(z, causal, 1 / math.sqrt(d), bn=4)
     ref = _online_reference(orc, z, causal, 1 / math.sqrt(d), bn=4)
     ok = fl == 0
@@ -299,6 +301,50 @@ def test_f16_pv_is_closer_to_full_precision_than_e4m3(orc, recipe):
     e16 = orc.accuracy(orc.attn_q(orc.quantize(q, k, v, pv="f16"), w.causal, w.sm_scale,
                                   rows=rows)[0], ref)
     assert e16["rel_l1"] < e8["rel_l1"] and e16["cos"] > e8["cos"]
+
+
+@pytest.mark.parametrize("recipe", [1, 3, 5])
+def test_int4_qk_within_p_rounding_of_dequantized_reference(orc, recipe):
+    """The 4-bit Q, K variant changes only the codes: against float64
+    attention on its own dequantized Q, K and V, the error is P's E4M3
+    rounding, as for INT8."""
+    w0 = workloads.WORKLOADS[recipe]
+    w = w0.resized(B=1, Hq=w0.Hq // w0.Hkv * 2, Hkv=2, N=500)
+    q, k, v = workloads.generate(w, seed=recipe)
+    z = orc.quantize(q, k, v, qk_bits=4)
+    assert np.abs(z["q_i8"]).max() == 7 and np.abs(z["k_i8"]).max() == 7
+    rows = workloads.sample_rows(w, 120)
+    out, lo, hi, _ = orc.attn_q(z, w.causal, w.sm_scale, rows=rows)
+    qd, kd, vd = _deq_inputs(orc, z)
+    ref = orc.attn_f64(qd, kd, vd, w.causal, w.sm_scale, rows=rows)
+    bound = 2 * np.abs(vd).max() * (2.0 ** -4 / (1 - 2.0 ** -4) + w.N * 2.0 ** -10 / 448.0)
+    assert np.abs(out - ref).max() <= bound
+    assert np.all(lo <= out) and np.all(out <= hi)
+
+
+def test_int4_qk_needs_smoothing_and_fine_scales(orc):
+    """The Berkeley brief and the SageAttention2 summary: 4-bit Q, K lose
+    accuracy without outlier smoothing and fine-grained scales.  With K
+    channel outliers, INT4 without smoothing is worse than with it, per-row /
+    32-key scales improve on per-block ones, and INT8 stays far better than
+    INT4 (attending with exact V isolates the Q, K part)."""
+    w = workloads.WORKLOADS[3].resized(B=1, Hq=2, Hkv=2, N=600)
+    q, k, v = workloads.generate(w, seed=3)
+    rows = workloads.sample_rows(w, 150)
+    ref = orc.attn_f64(q, k, v, w.causal, w.sm_scale, rows=rows)
+
+    def err(**kw):
+        z = orc.quantize(q, k, v, **kw)
+        qd, kd, _ = _deq_inputs(orc, z)
+        kd = kd + (0.0 if kw.get("smooth", True) is False else z["k_mean"][:, :, None, :])
+        return orc.accuracy(orc.attn_f64(qd, kd, orc.to_f32(v), w.causal, w.sm_scale, rows=rows),
+                            ref)["rel_l1"]
+
+    e4_raw = err(qk_bits=4, smooth=False)
+    e4 = err(qk_bits=4)
+    e4_fine = err(qk_bits=4, bq=1, bk=32)
+    e8 = err(qk_bits=8)
+    assert e4_raw > 1.2 * e4 and e4_fine < 0.9 * e4 and e8 < 0.2 * e4_fine
 
 
 def test_smoothing_helps_when_k_has_channel_outliers(orc):

@@ -120,39 +120,46 @@ def _deq(codes, scale, blk, n):
     return codes.astype(np.float64) * s[..., None]
 
 
+@pytest.mark.parametrize("qk_bits,qmax", [(8, 127), (4, 7)])
 @pytest.mark.parametrize("N,d", [(300, 64), (256, 128), (1, 64), (129, 64)])
-def test_int8_blocks_round_half_even_within_half_step(orc, N, d):
+def test_int8_blocks_round_half_even_within_half_step(orc, N, d, qk_bits, qmax):
+    """INT8 (and the INT4 values of the 4-bit variant): scale absmax/qmax,
+    codes numpy's rint of the float32 product, the block's largest magnitude
+    at +-qmax, every code within half a step."""
     q, k, v = workloads.random_inputs(2, 3, 3, N, d, "f16", seed=N + d, scale=3.0)
-    z = orc.quantize(q, k, v)
+    z = orc.quantize(q, k, v, qk_bits=qk_bits)
     q32 = orc.to_f32(q)
     nqb = -(-N // 128)
+    qm = np.float32(qmax)
     for b in range(2):
         for h in range(3):
             for t in range(nqb):
                 blk = q32[b, h, t * 128:(t + 1) * 128]
                 a = np.abs(blk).max()
                 s = z["q_scale"][b, h, t]
-                assert s == np.float32(a) / np.float32(127.0)
+                assert s == np.float32(a) / qm
                 codes = z["q_i8"][b, h, t * 128:(t + 1) * 128]
                 # numpy's own rint (half-even) on the float32 product
-                ref = np.clip(np.rint(blk * (np.float32(127.0) / np.float32(a))), -127, 127)
+                ref = np.clip(np.rint(blk * (qm / np.float32(a))), -qmax, qmax)
                 np.testing.assert_array_equal(codes, ref.astype(np.int8))
-                # the largest magnitude maps to +-127 and every code is within
+                # the largest magnitude maps to +-qmax and every code is within
                 # half a step of the value (plus float32 rounding of scale and
-                # reciprocal, at most 127 * 3 * 2^-24 of a step)
-                assert np.abs(codes).max() == 127
+                # reciprocal, at most qmax * 3 * 2^-24 of a step)
+                assert np.abs(codes).max() == qmax
                 err = np.abs(codes.astype(np.float64) * s - blk)
                 assert np.all(err <= (0.5 + 1e-4) * s)
 
 
+@pytest.mark.parametrize("qk_bits,qmax", [(8, 127), (4, 7)])
 @pytest.mark.parametrize("bq,bk", [(1, 32), (128, 64)])
-def test_scale_groups_of_both_granularities(orc, bq, bk):
+def test_scale_groups_of_both_granularities(orc, bq, bk, qk_bits, qmax):
     """Q scales per bq rows and K scales per bk keys, each the group's absmax /
-    127 with numpy's rint on the float32 product, for the per-block and the
+    qmax with numpy's rint on the float32 product, for the per-block and the
     thread-level (per-row Q, 32-key K) granularities; ragged last groups."""
     N, d = 70, 64
     q, k, v = workloads.random_inputs(1, 2, 2, N, d, "bf16", seed=bq + bk, scale=2.0)
-    z = orc.quantize(q, k, v, bq=bq, bk=bk)
+    z = orc.quantize(q, k, v, bq=bq, bk=bk, qk_bits=qk_bits)
+    qm = np.float32(qmax)
     assert z["q_scale"].shape[-1] == -(-N // bq) and z["k_scale"].shape[-1] == -(-N // bk)
     q32 = orc.to_f32(q)
     ks = orc.to_f32(k) - z["k_mean"][:, :, None, :]
@@ -161,8 +168,8 @@ def test_scale_groups_of_both_granularities(orc, bq, bk):
             for t in range(-(-N // g)):
                 blk = x[0, h, t * g:(t + 1) * g]
                 a = np.abs(blk).max()
-                assert scales[0, h, t] == np.float32(a) / np.float32(127.0)
-                ref = np.clip(np.rint(blk * (np.float32(127.0) / np.float32(a))), -127, 127)
+                assert scales[0, h, t] == np.float32(a) / qm
+                ref = np.clip(np.rint(blk * (qm / np.float32(a))), -qmax, qmax)
                 np.testing.assert_array_equal(codes[0, h, t * g:(t + 1) * g], ref.astype(np.int8))
 
 
