@@ -41,6 +41,8 @@ def parse():
                    help="Q/K scale granularity: block (128 rows / 64 keys) or thread (per row / 32 keys)")
     p.add_argument("--pv", choices=("e4m3", "f16"), default="e4m3",
                    help="P.V format: e4m3 (FP8 P and V, the default) or f16 (binary16 P and V)")
+    p.add_argument("--qk-bits", type=int, choices=(8, 4), default=8,
+                   help="Q, K codes: INT8 (the default) or the INT4 values of the 4-bit variant")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
     p.add_argument("--contrast", action="store_true",
@@ -72,7 +74,7 @@ def kernel_digest(paths=KERNEL_SOURCES):
     return h.hexdigest()
 
 
-def measured_traffic(granularity, pv):
+def measured_traffic(granularity, pv, qk_bits):
     """(workload, HBM bytes per attention launch) from the committed
     byte-counter summary taken with this granularity and P.V format, or
     (None, None) when the kernel sources changed since the counters were
@@ -83,7 +85,7 @@ def measured_traffic(granularity, pv):
         with open(path) as f:
             d = json.load(f)
         if (d.get("kernel_source_sha256") == digest and d.get("granularity", "block") == granularity
-                and d.get("pv_format", "e4m3") == pv):
+                and d.get("pv_format", "e4m3") == pv and d.get("qk_bits", 8) == qk_bits):
             return d.get("workload"), d.get("traffic_bytes_per_launch")
     return None, None
 
@@ -138,7 +140,7 @@ def prep_flushed(sage, qd, kd, vd, z, steps, torch):
     return times[len(times) // 2]
 
 
-def cpu_baseline(w, q, k, v, rows_wanted, bq, bk, pv):
+def cpu_baseline(w, q, k, v, rows_wanted, bq, bk, pv, qk_bits):
     """The oracle as it stands: its prep over the whole input, pro-rated to the
     sampled rows, plus its attention over the sampled rows."""
     import numpy as np
@@ -148,7 +150,7 @@ def cpu_baseline(w, q, k, v, rows_wanted, bq, bk, pv):
 
     oracle.build()
     t0 = time.perf_counter()
-    oz = oracle.quantize(q, k, v, bq=bq, bk=bk, pv=pv)
+    oz = oracle.quantize(q, k, v, bq=bq, bk=bk, pv=pv, qk_bits=qk_bits)
     t_prep = time.perf_counter() - t0
     total_rows = w.B * w.Hq * w.N
     if rows_wanted <= 0:
@@ -279,8 +281,8 @@ def main():
     out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
     ws = sage.workspace_for(qd, kd)
     z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d,
-                                  granularity=args.granularity, pv=args.pv)
-    opts = sage.options(args.granularity, args.pv)
+                                  granularity=args.granularity, pv=args.pv, qk_bits=args.qk_bits)
+    opts = sage.options(args.granularity, args.pv, args.qk_bits)
     qb, kb = opts.q_block, opts.k_block
 
     def step():
@@ -297,7 +299,7 @@ def main():
     ms_prep = timed(lambda: sage.sage_quantize(qd, kd, vd, z), args.steps, torch)
     ms_attn = timed(lambda: sage.sage_attn_fwd_quantized(z, out, w.B, w.Hq, w.Hkv, w.N, w.d,
                                                          w.causal, w.sm_scale), args.steps, torch)
-    traffic_wl, traffic = measured_traffic(args.granularity, args.pv)
+    traffic_wl, traffic = measured_traffic(args.granularity, args.pv, args.qk_bits)
     if traffic_wl != w.name:
         traffic = None
     tops = w.ops / (ms_step * 1e-3) / 1e12
@@ -309,10 +311,12 @@ def main():
         "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"i8 (QK^T, i32 acc) + {args.pv} values (P.V, f32 acc)", "data": "synthetic",
+        "dtype": f"{'i8' if args.qk_bits == 8 else 'i4 values in i8'} (QK^T, i32 acc) + {args.pv} values "
+                 f"(P.V, f32 acc)", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "input_dtype": w.dtype, "sm_scale": w.sm_scale,
-                   "q_block": qb, "k_block": kb, "pv_format": args.pv, "parallelism": "single GPU"},
+                   "q_block": qb, "k_block": kb, "pv_format": args.pv, "qk_bits": args.qk_bits,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd", "ms_per_launch": round(ms_attn, 4)},
@@ -327,7 +331,7 @@ def main():
     if args.contrast:
         line["contrast"] = contrast_sdpa(w, qd, kd, vd, args.steps, torch)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, qb, kb, args.pv)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, qb, kb, args.pv, args.qk_bits)
     print(json.dumps(line), flush=True)
 
 

@@ -27,6 +27,7 @@ SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_BQ, SAGE_BK, SAGE_BN, SAGE_NPAD = 128, 64, 128, 256
 SAGE_BQ_THREAD, SAGE_BK_THREAD = 1, 32
 SAGE_PV_E4M3, SAGE_PV_F16 = 0, 1
+SAGE_QK_INT8, SAGE_QK_INT4 = 8, 4
 # (q_block, k_block) of the two quantization granularities
 GRANULARITY = {"block": (SAGE_BQ, SAGE_BK), "thread": (SAGE_BQ_THREAD, SAGE_BK_THREAD)}
 # P.V formats: FP8 E4M3 P and V, or binary16 P and V (both accumulated in FP32)
@@ -42,7 +43,7 @@ class sage_qkv_quant(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v16", "v_scale", "v_inv",
                  "k_part", "v_part", "sync")] + [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32),
-                                                 ("pv_format", ctypes.c_int32)]
+                                                 ("pv_format", ctypes.c_int32), ("qk_bits", ctypes.c_int32)]
 
 
 class sage_kv_cache(ctypes.Structure):
@@ -52,7 +53,8 @@ class sage_kv_cache(ctypes.Structure):
 
 
 class sage_options(ctypes.Structure):
-    _fields_ = [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32), ("pv_format", ctypes.c_int32)]
+    _fields_ = [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32), ("pv_format", ctypes.c_int32),
+                ("qk_bits", ctypes.c_int32)]
 
 
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -143,14 +145,15 @@ def sage_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
 
 def sage_workspace_carve(workspace: torch.Tensor | int | None, ws_bytes: int, B: int, Hq: int,
                          Hkv: int, N: int, d: int, granularity: str = "block",
-                         pv: str = "e4m3") -> sage_qkv_quant:
-    """The C call, then (q_block, k_block) and pv_format set to the chosen
-    granularity and P.V format."""
+                         pv: str = "e4m3", qk_bits: int = 8) -> sage_qkv_quant:
+    """The C call, then (q_block, k_block), pv_format and qk_bits set to the
+    chosen granularity, P.V format and Q, K code width."""
     z = sage_qkv_quant()
     ptr = workspace.data_ptr() if isinstance(workspace, torch.Tensor) else workspace
     _check(_lib.sage_workspace_carve(ptr, ws_bytes, B, Hq, Hkv, N, d, ctypes.byref(z)))
     z.q_block, z.k_block = GRANULARITY[granularity]
     z.pv_format = PV_FORMAT[pv]
+    z.qk_bits = qk_bits
     return z
 
 
@@ -229,10 +232,11 @@ def sage_attn_decode(q: torch.Tensor, cache: sage_kv_cache, out: torch.Tensor, H
 
 # ------------------------------------------------------------------ helpers
 
-def options(granularity: str = "block", pv: str = "e4m3") -> sage_options:
-    """sage_options from the names of a granularity and a P.V format."""
+def options(granularity: str = "block", pv: str = "e4m3", qk_bits: int = 8) -> sage_options:
+    """sage_options from the names of a granularity and a P.V format, and the
+    Q, K code width (8, or 4 for the INT4 variant)."""
     qb, kb = GRANULARITY[granularity]
-    return sage_options(qb, kb, PV_FORMAT[pv])
+    return sage_options(qb, kb, PV_FORMAT[pv], qk_bits)
 
 
 def workspace_for(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
@@ -246,11 +250,12 @@ def workspace_for(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
 
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
          sm_scale: float | None = None, workspace: torch.Tensor | None = None,
-         granularity: str = "block", pv: str = "e4m3") -> torch.Tensor:
+         granularity: str = "block", pv: str = "e4m3", qk_bits: int = 8) -> torch.Tensor:
     """Drop-in attention: [B,Hq,N,d] fp16/bf16 Q and [B,Hkv,N,d] K,V on the GPU
     -> FP32 [B,Hq,N,d], on the current stream.  granularity: "block" (one Q
     scale per 128 rows, one K scale per 64 keys) or "thread" (per row, per 32
-    keys); pv: "e4m3" (FP8 P and V) or "f16" (binary16 P and V)."""
+    keys); pv: "e4m3" (FP8 P and V) or "f16" (binary16 P and V); qk_bits: 8
+    (INT8 Q, K) or 4 (INT4 values)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     for t in (q, k, v):
@@ -259,7 +264,7 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = workspace_for(q, k)
-    sage_attn_fwd_ex(q, k, v, out, causal, sm_scale, options(granularity, pv), workspace)
+    sage_attn_fwd_ex(q, k, v, out, causal, sm_scale, options(granularity, pv, qk_bits), workspace)
     return out
 
 

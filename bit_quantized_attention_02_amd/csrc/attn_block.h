@@ -166,11 +166,16 @@ __device__ inline int max_across_halves(int x) {
 // block are excluded (causal diagonal, or keys >= N).  PV16: P is rounded to
 // binary16 directly (l448 is then 0) instead of through E4M3.  V8: the V tile
 // holds E4M3 code bytes (a KV cache), converted to binary16 -- exactly -- as
-// each fragment is read.
+// each fragment is read.  SEEDED (INT8 codes): the accumulator is seeded with
+// 1.5*2^23 and read as a float; without it (the INT4 codes of the 4-bit
+// variant, whose score factors are about 330 times larger, so the seed's
+// float32 rounding would no longer be negligible) each score is converted
+// from the integer accumulator, one more instruction per score.
 // KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
 // 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
 // log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false,
+          bool SEEDED = true>
 __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const void* __restrict__ lv,
                                            const v4i (&qf)[D / 32], int T, int row, int N,
@@ -181,7 +186,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
     constexpr int TPG = 4 / KSPLIT;  // tiles per scale group
     float u[KSPLIT];
 #pragma unroll
-    for (int g = 0; g < KSPLIT; ++g) u[g] = kSeed * c[g];
+    for (int g = 0; g < KSPLIT; ++g) u[g] = SEEDED ? kSeed * c[g] : 0.0f;
 
     // ---- S^T = K Q^T (INT32).  Tile t, element v: key 32t + 8(v/4) + 4h + v%4.
     v16i S[4];
@@ -192,7 +197,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
         // float32, is exactly 1.5*2^23 + acc (|acc| < 2^22)
         v16i acc;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = kSeedBits;
+        for (int v = 0; v < 16; ++v) acc[v] = SEEDED ? kSeedBits : 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const v4i kf = *reinterpret_cast<const v4i*>(lk + kr * D + (((2 * ks + h) ^ kswz<D>(kr)) << 4));
@@ -222,7 +227,8 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
 #pragma unroll
             for (int v = (tt == 0 ? 1 : 0); v < 16; ++v) M = max(M, S[g * TPG + tt][v]);
         M = max_across_halves(M);
-        float m = __builtin_fmaf(__builtin_bit_cast(float, M), c[g], -u[g]);
+        const float fm = SEEDED ? __builtin_bit_cast(float, M) : (float)M;
+        float m = __builtin_fmaf(fm, c[g], -u[g]);
         if (MASKED && M == INT32_MIN) m = -INFINITY;
         mt = fmaxf(mt, m);
     }
@@ -268,7 +274,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                 const float bt = bias[t / TPG];
                 // (bit_cast of the whole vector: this compiler mis-reads a
                 // bit_cast of a single vector element as element 0)
-                const v16f F = __builtin_bit_cast(v16f, S[t]);
+                const v16f F = SEEDED ? __builtin_bit_cast(v16f, S[t]) : __builtin_convertvector(S[t], v16f);
                 v4i quad;
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {

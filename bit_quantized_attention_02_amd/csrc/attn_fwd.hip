@@ -26,7 +26,7 @@ struct AttnArgs {
     float l448;  // f32(log2 448), or 0 for binary16 P
 };
 
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, int WAVES, int WAVES_PER_SIMD>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool SEEDED, int WAVES, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs a) {
     constexpr int KS = D / 32;
     constexpr int CT = D / 32;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         float c[KSPLIT];
 #pragma unroll
         for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-        attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N,
+        attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N,
                                                    c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -124,10 +124,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 #pragma unroll
         for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
         if (T < n_full)
-            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
+            attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
                                                        a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         else if (T <= wave_last)
-            attn_block<D, KSPLIT, CAUSAL, PV16, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
+            attn_block<D, KSPLIT, CAUSAL, PV16, true, false, SEEDED>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
                                                       a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -178,11 +178,12 @@ constexpr int attn_waves_per_simd() {
 // Explicit instantiations: with the packed-FP32 feature switched off on the
 // command line, this compiler otherwise leaves the host stubs of some of these
 // kernels undefined.
-#define SAGE_ATTN_INST(D, KSPLIT, CAUSAL, PV16)                                                  \
-    template __global__ void attn_fwd<D, KSPLIT, CAUSAL, PV16, attn_waves<D>(), attn_waves_per_simd<D>()>( \
-        AttnArgs);
-#define SAGE_ATTN_INST_PV(D, KSPLIT, CAUSAL) \
-    SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true)
+#define SAGE_ATTN_INST(D, KSPLIT, CAUSAL, PV16, SEEDED)                                           \
+    template __global__ void                                                                        \
+    attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, attn_waves<D>(), attn_waves_per_simd<D>()>(AttnArgs);
+#define SAGE_ATTN_INST_PV(D, KSPLIT, CAUSAL)                                                       \
+    SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false, true) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true, true)    \
+    SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false, false) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true, false)
 SAGE_ATTN_INST_PV(64, 2, false)
 SAGE_ATTN_INST_PV(64, 2, true)
 SAGE_ATTN_INST_PV(64, 4, false)
@@ -194,33 +195,39 @@ SAGE_ATTN_INST_PV(128, 4, true)
 #undef SAGE_ATTN_INST_PV
 #undef SAGE_ATTN_INST
 
-template <int D, int KSPLIT, bool CAUSAL, bool PV16>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool SEEDED>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WAVES = attn_waves<D>();
     constexpr int WPS = attn_waves_per_simd<D>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int total = a.B * a.Hq * a.nqt;
-    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>), dim3(total), dim3(64 * WAVES),
-                       lds, st, a);
+    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>), dim3(total),
+                       dim3(64 * WAVES), lds, st, a);
     return hipGetLastError();
 }
 
-template <int D, int KSPLIT, bool PV16>
+template <int D, int KSPLIT, bool PV16, bool SEEDED>
 static hipError_t launch_attn_p(AttnArgs a, int causal, hipStream_t st) {
-    return causal ? launch_attn_t<D, KSPLIT, true, PV16>(a, st)
-                  : launch_attn_t<D, KSPLIT, false, PV16>(a, st);
+    return causal ? launch_attn_t<D, KSPLIT, true, PV16, SEEDED>(a, st)
+                  : launch_attn_t<D, KSPLIT, false, PV16, SEEDED>(a, st);
+}
+
+template <int D, int KSPLIT, bool PV16>
+static hipError_t launch_attn_s(AttnArgs a, int causal, bool seeded, hipStream_t st) {
+    return seeded ? launch_attn_p<D, KSPLIT, PV16, true>(a, causal, st)
+                  : launch_attn_p<D, KSPLIT, PV16, false>(a, causal, st);
 }
 
 template <int D, int KSPLIT>
-static hipError_t launch_attn_d(AttnArgs a, int causal, bool pv16, hipStream_t st) {
-    return pv16 ? launch_attn_p<D, KSPLIT, true>(a, causal, st)
-                : launch_attn_p<D, KSPLIT, false>(a, causal, st);
+static hipError_t launch_attn_d(AttnArgs a, int causal, bool pv16, bool seeded, hipStream_t st) {
+    return pv16 ? launch_attn_s<D, KSPLIT, true>(a, causal, seeded, st)
+                : launch_attn_s<D, KSPLIT, false>(a, causal, seeded, st);
 }
 
 hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal,
@@ -245,9 +252,12 @@ hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int 
     a.l448 = l448;
     const bool fine_k = z->k_block == SAGE_BK_THREAD;  // 4 K scales per block, else 2
     const bool pv16 = z->pv_format == SAGE_PV_F16;
+    const bool seeded = z->qk_bits == SAGE_QK_INT8;  // INT4 codes take the unseeded scores
     if (s.d == 64)
-        return fine_k ? launch_attn_d<64, 4>(a, causal, pv16, st) : launch_attn_d<64, 2>(a, causal, pv16, st);
-    return fine_k ? launch_attn_d<128, 4>(a, causal, pv16, st) : launch_attn_d<128, 2>(a, causal, pv16, st);
+        return fine_k ? launch_attn_d<64, 4>(a, causal, pv16, seeded, st)
+                      : launch_attn_d<64, 2>(a, causal, pv16, seeded, st);
+    return fine_k ? launch_attn_d<128, 4>(a, causal, pv16, seeded, st)
+                  : launch_attn_d<128, 2>(a, causal, pv16, seeded, st);
 }
 
 }  // namespace sage

@@ -36,13 +36,14 @@ typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------ shared pieces
-// INT8 codes of 8 values with multiplier inv (RNE, clamped to +-127).
-__device__ inline uint2 int8_codes(const float (&x)[8], float inv) {
+// Integer codes of 8 values with multiplier inv (RNE, clamped to +-qmax: 127
+// for INT8, 7 for the INT4 values of the 4-bit variant), one byte each.
+__device__ inline uint2 int8_codes(const float (&x)[8], float inv, float qmax) {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float r = __builtin_rintf(x[i] * inv);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        r = fminf(fmaxf(r, -qmax), qmax);
         w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (i & 3));
     }
     return make_uint2(w[0], w[1]);
@@ -147,7 +148,7 @@ __device__ inline void store_v_tile(const void* vt, void* dst, int tid) {
 // One work-group per 128 rows of a q head; one scale per bq rows (128 or 1).
 template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ q, Shape s, int bq,
-                                                   int8_t* __restrict__ q_i8,
+                                                   float qmax, int8_t* __restrict__ q_i8,
                                                    float* __restrict__ q_scale,
                                                    int* __restrict__ sync) {
     constexpr int CPR = D / 8;  // 16-byte chunks per row
@@ -188,9 +189,9 @@ __global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ 
         const int e = tid + c * kThreads;
         const int row = t * R + e / CPR, col = (e % CPR) * 8;
         const float a = am[c];
-        if (e % CPR == 0 && row % bq == 0) q_scale[sbase + row / bq] = a / 127.0f;
-        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-        *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv);
+        if (e % CPR == 0 && row % bq == 0) q_scale[sbase + row / bq] = a / qmax;
+        const float inv = a > 0.0f ? qmax / a : 0.0f;
+        *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv, qmax);
     }
 }
 
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void prep_stats(
 
 template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_pack(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s, int bk,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s, int bk, float qmax,
     const float* __restrict__ k_mean, const float* __restrict__ v_inv,
     int8_t* __restrict__ k_i8, float* __restrict__ k_scale, void* __restrict__ v_out, int v_store) {
     constexpr int CPR = D / 8;
@@ -322,9 +323,9 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
             const int e = tid + c * kThreads;
             const int row = t * R + e / CPR, col = (e % CPR) * 8;
             const float a = am[c];
-            if (e % CPR == 0 && row % bk == 0) k_scale[sbase + row / bk] = a / 127.0f;
-            const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-            *reinterpret_cast<uint2*>(k_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv);
+            if (e % CPR == 0 && row % bk == 0) k_scale[sbase + row / bk] = a / qmax;
+            const float inv = a > 0.0f ? qmax / a : 0.0f;
+            *reinterpret_cast<uint2*>(k_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv, qmax);
         }
         return;
     }
@@ -380,7 +381,7 @@ static hipError_t launch_prep_kv_t(const void* k, const void* v, const Shape& s,
     if (e != hipSuccess) return e;
     const int per_head = s.Np / 64 + s.Np / SAGE_BN;
     hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, s, z.k_block, z.k_mean, z.v_inv,
+                       (const uint16_t*)k, (const uint16_t*)v, s, z.k_block, z.qmax, z.k_mean, z.v_inv,
                        z.k_i8, z.k_scale, z.v, z.v_store);
     return hipGetLastError();
 }
@@ -389,13 +390,14 @@ template <typename In, int D>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const Shape& s,
                                 const sage_qkv_quant* z, hipStream_t st) {
     const int nq = s.B * s.Hq * (s.Np / 128);
+    const float qmax = z->qk_bits == SAGE_QK_INT4 ? 7.0f : 127.0f;
     hipLaunchKernelGGL((prep_q<In, D>), dim3(nq + 1), dim3(kThreads), 0, st, (const uint16_t*)q, s,
-                       (int)z->q_block, z->q_i8, z->q_scale, z->sync);
+                       (int)z->q_block, qmax, z->q_i8, z->q_scale, z->sync);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const KVViews kv = {z->k_i8,   z->k_scale, z->k_mean, z->v16,     z->v_scale,
                         z->v_inv,  z->k_part,  z->v_part, z->sync,    z->k_block,
-                        z->pv_format == SAGE_PV_F16 ? kVF16 : kVE4M3Half};
+                        z->pv_format == SAGE_PV_F16 ? kVF16 : kVE4M3Half, qmax};
     return launch_prep_kv_t<In, D>(k, v, s, kv, st);
 }
 

@@ -73,6 +73,7 @@ static bool granularity_ok(int q_block, int k_block) {
 }
 
 static bool pv_format_ok(int f) { return f == SAGE_PV_E4M3 || f == SAGE_PV_F16; }
+static bool qk_bits_ok(int b) { return b == SAGE_QK_INT8 || b == SAGE_QK_INT4; }
 
 static bool k_block_ok(int k_block) { return k_block == SAGE_BK || k_block == SAGE_BK_THREAD; }
 
@@ -122,7 +123,8 @@ static DecodeLayout decode_layout(int B, int Hq, int Hkv, int Nq, int Nk, int d)
 
 static int check_quant(const sage_qkv_quant* z) {
     if (!z) return SAGE_ERR_INVALID_ARG;
-    if (!granularity_ok(z->q_block, z->k_block) || !pv_format_ok(z->pv_format))
+    if (!granularity_ok(z->q_block, z->k_block) || !pv_format_ok(z->pv_format) ||
+        !qk_bits_ok(z->qk_bits))
         return SAGE_ERR_UNSUPPORTED;
     if (!z->q_i8 || !z->q_scale || !z->k_i8 || !z->k_scale || !z->k_mean || !z->v16 ||
         !z->v_scale || !z->v_inv || !z->k_part || !z->v_part || !z->sync)
@@ -163,6 +165,7 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->q_block = SAGE_BQ;
     out->k_block = SAGE_BK;
     out->pv_format = SAGE_PV_E4M3;
+    out->qk_bits = SAGE_QK_INT8;
     return SAGE_OK;
 }
 
@@ -205,7 +208,8 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, in
     int rc = check_shape(B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
     if (!opts) return SAGE_ERR_INVALID_ARG;
-    if (!granularity_ok(opts->q_block, opts->k_block) || !pv_format_ok(opts->pv_format))
+    if (!granularity_ok(opts->q_block, opts->k_block) || !pv_format_ok(opts->pv_format) ||
+        !qk_bits_ok(opts->qk_bits))
         return SAGE_ERR_UNSUPPORTED;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
@@ -219,6 +223,7 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, in
     z.q_block = opts->q_block;
     z.k_block = opts->k_block;
     z.pv_format = opts->pv_format;
+    z.qk_bits = opts->qk_bits;
     rc = sage_quantize(q, k, v, dtype, B, Hq, Hkv, N, d, &z, stream);
     if (rc != SAGE_OK) return rc;
     return sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, causal, sm_scale, stream);
@@ -228,7 +233,7 @@ int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* o
                            int Hkv, int N, int d, int causal, float sm_scale, int dtype,
                            int q_block, int k_block, void* workspace, size_t ws_bytes,
                            void* stream) {
-    const sage_options o = {q_block, k_block, SAGE_PV_E4M3};
+    const sage_options o = {q_block, k_block, SAGE_PV_E4M3, SAGE_QK_INT8};
     return sage_attn_fwd_ex(q, k, v, out, B, Hq, Hkv, N, d, causal, sm_scale, dtype, &o, workspace,
                             ws_bytes, stream);
 }
@@ -281,7 +286,8 @@ int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, in
     const sage::KVViews kv = {cache->k_i8,   cache->k_scale, cache->k_mean, cache->v,
                               cache->v_scale, cache->v_inv,  cache->k_part, cache->v_part,
                               cache->sync,   cache->k_block,
-                              cache->pv_format == SAGE_PV_F16 ? sage::kVF16 : sage::kVE4M3Byte};
+                              cache->pv_format == SAGE_PV_F16 ? sage::kVF16 : sage::kVE4M3Byte,
+                              127.0f};
     hipError_t e = sage::launch_prep_kv(k, v, dtype, s, kv, (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
@@ -335,7 +341,8 @@ const char* sage_status_string(int status) {
         case SAGE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad flag or size)";
         case SAGE_ERR_UNSUPPORTED:
             return "unsupported shape or option (d must be 64 or 128, Hq % Hkv == 0, N <= 2^20; "
-                   "(q_block, k_block) = (128, 64) or (1, 32); P.V format E4M3 (0) or binary16 (1))";
+                   "(q_block, k_block) = (128, 64) or (1, 32); P.V format E4M3 (0) or binary16 (1); "
+                   "Q, K codes of 8 or 4 bits)";
         case SAGE_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
         case SAGE_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";

@@ -44,6 +44,7 @@ struct KVViews {
     int32_t* sync;
     int k_block;
     int v_store;
+    float qmax;  // largest K code: 127 (INT8) or 7 (INT4)
 };
 
 // Split of a short-query attention over a KV cache into work-groups: row

@@ -42,6 +42,14 @@
  *     f16(2^fmaf(acc, c, -m)), so the block's largest element is exactly 1.
  *     The article accumulates in FP16; the binary16 matrix cores here
  *     accumulate in FP32 only, so both levels stay FP32.
+ *   - Q, K code width (sage_qkv_quant.qk_bits).  SAGE_QK_INT4 is the 4-bit
+ *     Q, K of SageAttention2 (the SageAttention2 summary; the Berkeley brief's
+ *     comparison table): the INT8 scheme with 7 in place of 127 (codes in
+ *     [-7, 7], scale absmax/7), stored one code per byte and multiplied on
+ *     the INT8 matrix core (gfx950 has no INT4 one), at INT8 speed.  Its
+ *     scores are converted from the integer accumulator instead of the
+ *     1.5*2^23-seeded float read, whose float32 rounding (about one integer
+ *     step of c) would matter at INT4 scales.  Decode caches are INT8 only.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -80,6 +88,8 @@ extern "C" {
 #define SAGE_BK_THREAD 32 /* keys per K scale, thread-level granularity */
 #define SAGE_PV_E4M3 0    /* P and V as FP8 E4M3 (the default) */
 #define SAGE_PV_F16 1     /* P and V as binary16 */
+#define SAGE_QK_INT8 8    /* Q, K codes: INT8 (the default) */
+#define SAGE_QK_INT4 4    /* Q, K codes: INT4 values in [-7, 7], one per byte */
 
 typedef enum {
     SAGE_OK = 0,
@@ -136,6 +146,7 @@ typedef struct {
     int32_t k_block; /* keys per K scale: SAGE_BK (set by sage_workspace_carve) or SAGE_BK_THREAD */
     int32_t pv_format; /* SAGE_PV_E4M3 (set by sage_workspace_carve) or SAGE_PV_F16; the
                           attention call must see the value the quantize call saw */
+    int32_t qk_bits;   /* SAGE_QK_INT8 (set by sage_workspace_carve) or SAGE_QK_INT4; likewise */
 } sage_qkv_quant;
 
 /* Method options of sage_attn_fwd_ex. */
@@ -143,6 +154,7 @@ typedef struct {
     int32_t q_block;   /* SAGE_BQ or SAGE_BQ_THREAD */
     int32_t k_block;   /* SAGE_BK or SAGE_BK_THREAD (paired with q_block as above) */
     int32_t pv_format; /* SAGE_PV_E4M3 or SAGE_PV_F16 */
+    int32_t qk_bits;   /* SAGE_QK_INT8 or SAGE_QK_INT4 */
 } sage_options;
 
 /* Bytes of workspace sage_quantize/sage_attn_fwd need for this shape (0 when

@@ -190,6 +190,29 @@ def test_pv_format_is_validated(sage):
     assert z.pv_format == sage.SAGE_PV_F16
 
 
+def test_qk_bits_are_validated(sage):
+    """Q, K code widths 8 (the carve's default) and 4 are accepted; others are
+    rejected before any HIP call."""
+    L = sage._lib
+    fake = 1 << 40
+    shape = (1, 4, 2, 300, 64)
+    need = sage.sage_workspace_bytes(*shape)
+    f = ctypes.c_float
+    z = sage.sage_workspace_carve(fake, need, *shape)
+    assert z.qk_bits == 8
+    for bits, ok in ((8, True), (4, True), (2, False), (16, False), (0, False)):
+        o = sage.options("thread", "e4m3", 8)
+        o.qk_bits = bits
+        rc = L.sage_attn_fwd_ex(fake, fake, fake, None, *shape, 0, f(0.125), 0, ctypes.byref(o), fake,
+                                need, None)
+        assert rc == (sage.SAGE_ERR_INVALID_ARG if ok else sage.SAGE_ERR_UNSUPPORTED)
+        if not ok:
+            z.qk_bits = bits
+            zp = ctypes.byref(z)
+            assert L.sage_quantize(fake, fake, fake, 0, *shape, zp, None) == sage.SAGE_ERR_UNSUPPORTED
+            assert L.sage_attn_fwd_quantized(zp, fake, *shape, 0, f(0.125), None) == sage.SAGE_ERR_UNSUPPORTED
+
+
 def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
     """The KV-cache and short-query calls: sizes, carving and argument checks
     before any HIP call."""

@@ -4,7 +4,8 @@ Prep outputs (codes, scales, K mean) must be bit-exact.  The attention output
 must lie within the oracle's interval (the set of outputs reachable by the P
 codes that sit within 2^-20 of an E4M3 or binary16 rounding midpoint, where
 the hardware exp2 may round either way) up to max-abs 2e-3 and rel-L1 1e-3.
-Both P.V formats (E4M3 and binary16) and both quantization granularities are
+Both P.V formats (E4M3 and binary16), both quantization granularities and
+both Q, K code widths (INT8 and the INT4 values of the 4-bit variant) are
 covered.
 """
 import math
@@ -34,12 +35,13 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(sage, q, k, v, causal, sm_scale, granularity="block", pv="e4m3"):
+def run_gpu(sage, q, k, v, causal, sm_scale, granularity="block", pv="e4m3", qk_bits=8):
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     ws = sage.workspace_for(qd, kd)
-    z = sage.sage_workspace_carve(ws, ws.numel(), B, Hq, Hkv, N, d, granularity=granularity, pv=pv)
+    z = sage.sage_workspace_carve(ws, ws.numel(), B, Hq, Hkv, N, d, granularity=granularity, pv=pv,
+                                  qk_bits=qk_bits)
     sage.sage_quantize(qd, kd, vd, z)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     sage.sage_attn_fwd_quantized(z, out, B, Hq, Hkv, N, d, causal, sm_scale)
@@ -86,9 +88,9 @@ def _rows_of(out, rows, d):
     return out.reshape(-1, d).cpu().numpy()[rows]
 
 
-def quantize_as(orc, q, k, v, granularity, pv="e4m3"):
+def quantize_as(orc, q, k, v, granularity, pv="e4m3", qk_bits=8):
     bq, bk = {"block": (128, 64), "thread": (1, 32)}[granularity]
-    return orc.quantize(q, k, v, bq=bq, bk=bk, pv=pv)
+    return orc.quantize(q, k, v, bq=bq, bk=bk, pv=pv, qk_bits=qk_bits)
 
 
 @pytest.mark.parametrize("pv", ["e4m3", "f16"])
@@ -109,17 +111,37 @@ def test_parity_reduced_workloads(sage, orc, recipe, granularity, pv):
     check_attn(orc, out.reshape(-1, w.d).cpu().numpy(), oz, w.causal, w.sm_scale, rows)
 
 
+@pytest.mark.parametrize("granularity", ["block", "thread"])
+@pytest.mark.parametrize("recipe", [1, 2, 3, 4, 5])
+def test_parity_int4_qk(sage, orc, recipe, granularity):
+    """The 4-bit (INT4) Q, K variant on every recipe at N = 700: codes in
+    [-7, 7] bit-exact, scores without the float offset."""
+    w0 = workloads.WORKLOADS[recipe]
+    w = w0.resized(B=2, Hq=2 * (w0.Hq // w0.Hkv), Hkv=2, N=700)
+    pv = "f16" if recipe == 2 else "e4m3"
+    _say(f"case int4 recipe={recipe} shape={(w.B, w.Hq, w.Hkv, w.N, w.d)} causal={w.causal} "
+         f"granularity={granularity} pv={pv}")
+    q, k, v = workloads.generate(w, seed=2000 + recipe)
+    out, quant = run_gpu(sage, q, k, v, w.causal, w.sm_scale, granularity, pv, 4)
+    oz = quantize_as(orc, q, k, v, granularity, pv, 4)
+    assert np.abs(oz["q_i8"]).max() == 7
+    check_prep(orc, quant, oz)
+    rows = np.arange(w.B * w.Hq * w.N)
+    check_attn(orc, out.reshape(-1, w.d).cpu().numpy(), oz, w.causal, w.sm_scale, rows)
+
+
 @pytest.mark.parametrize("N", [1, 2, 17, 64, 127, 128, 129, 255, 256, 300])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_parity_edge_lengths(sage, orc, N, d, causal):
     granularity = "thread" if N in (17, 129, 300) else "block"
     pv = "f16" if N in (2, 64, 129, 256) else "e4m3"
-    _say(f"case N={N} d={d} causal={causal} granularity={granularity} pv={pv}")
+    qk_bits = 4 if N in (1, 127, 129) else 8
+    _say(f"case N={N} d={d} causal={causal} granularity={granularity} pv={pv} qk_bits={qk_bits}")
     q, k, v = workloads.random_inputs(1, 4, 2, N, d, "f16" if d == 64 else "bf16",
                                       seed=N * 7 + d + causal, scale=1.5)
-    out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d), granularity, pv)
-    oz = quantize_as(orc, q, k, v, granularity, pv)
+    out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d), granularity, pv, qk_bits)
+    oz = quantize_as(orc, q, k, v, granularity, pv, qk_bits)
     check_prep(orc, quant, oz)
     check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 1 / math.sqrt(d), None)
 
@@ -189,30 +211,31 @@ def test_sage_attn_fwd_matches_two_step_path(sage, pv):
         assert torch.equal(one, out)
 
 
-@pytest.mark.parametrize("index,granularity,pv", [
-    (1, "block", "e4m3"), (2, "block", "e4m3"), (3, "block", "e4m3"), (4, "block", "e4m3"),
-    (5, "block", "e4m3"), (3, "thread", "e4m3"), (4, "thread", "e4m3"), (5, "thread", "e4m3"),
-    (2, "block", "f16"), (3, "block", "f16"), (4, "block", "f16"), (5, "block", "f16"),
-    (5, "thread", "f16")])
-def test_parity_full_size_workloads(sage, orc, index, granularity, pv):
+@pytest.mark.parametrize("index,granularity,pv,qk_bits", [
+    (1, "block", "e4m3", 8), (2, "block", "e4m3", 8), (3, "block", "e4m3", 8), (4, "block", "e4m3", 8),
+    (5, "block", "e4m3", 8), (3, "thread", "e4m3", 8), (4, "thread", "e4m3", 8), (5, "thread", "e4m3", 8),
+    (2, "block", "f16", 8), (3, "block", "f16", 8), (4, "block", "f16", 8), (5, "block", "f16", 8),
+    (5, "thread", "f16", 8), (3, "thread", "e4m3", 4), (4, "thread", "f16", 4)])
+def test_parity_full_size_workloads(sage, orc, index, granularity, pv, qk_bits):
     """Each workload at its full size, through sage_attn_fwd as the benchmark
     times it: the prep outputs are compared in full (bit-exact), the attention
     output on sampled rows the oracle computes one by one (first and last row
     of the first and last head, 256 seeded rows, and for the peaked-row recipe
     some of the x20 rows)."""
     w = workloads.WORKLOADS[index]
-    _say(f"case full-size workload {index} {w.name} granularity={granularity} pv={pv}")
+    _say(f"case full-size workload {index} {w.name} granularity={granularity} pv={pv} qk_bits={qk_bits}")
     q, k, v = workloads.generate(w)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
     ws = sage.workspace_for(qd, kd)
-    sage.sage_attn_fwd_ex(qd, kd, vd, out, w.causal, w.sm_scale, sage.options(granularity, pv), ws)
+    sage.sage_attn_fwd_ex(qd, kd, vd, out, w.causal, w.sm_scale, sage.options(granularity, pv, qk_bits),
+                          ws)
     torch.cuda.synchronize()
     z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d, granularity=granularity,
-                                  pv=pv)
+                                  pv=pv, qk_bits=qk_bits)
     quant = sage.read_quantized(z, ws, w.B, w.Hq, w.Hkv, w.N, w.d)
     del qd, kd, vd
-    oz = quantize_as(orc, q, k, v, granularity, pv)
+    oz = quantize_as(orc, q, k, v, granularity, pv, qk_bits)
     check_prep(orc, quant, oz)
     rows = workloads.sample_rows(w, 256, seed=11)
     if w.recipe == 4:
