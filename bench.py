@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
     p.add_argument("--contrast", action="store_true",
                    help="also time torch's scaled_dot_product_attention (flash backend only) in the "
-                        "input dtype on the same inputs: the native attention this path replaces")
+                        "input dtype on the same inputs: the native attention this path replaces; "
+                        "and a naive unfused 16-bit attention of our own (hipBLASLt products)")
     p.add_argument("--prep-flush", action="store_true",
                    help="also time the prep step alone with a 512 MB write between launches, so the "
                         "last-level cache holds none of its inputs")
@@ -122,6 +123,38 @@ def contrast_sdpa(w, qd, kd, vd, steps, torch):
     return {"kind": f"torch {torch.__version__} scaled_dot_product_attention, flash backend, "
                     f"{w.dtype} in and out", "ms_per_call": round(ms, 4),
             "TOPS": round(w.ops / (ms * 1e-3) / 1e12, 2)}
+
+
+def contrast_naive(w, qd, kd, vd, steps, torch):
+    """Unfused 16-bit attention of our own, head by head: S = Q K^T on the
+    matrix core through torch.matmul (hipBLASLt; K transposed into a
+    contiguous operand first), the mask and softmax in FP32, P rounded to the
+    input dtype, O = P V through torch.matmul."""
+    G = w.Hq // w.Hkv
+    kt = kd.transpose(-1, -2).contiguous()  # [B, Hkv, d, N]
+    out = torch.empty(qd.shape, dtype=qd.dtype, device=qd.device)
+    mask = None
+    if w.causal:
+        mask = torch.ones(w.N, w.N, dtype=torch.bool, device=qd.device).triu(1)
+
+    def run():
+        for b in range(w.B):
+            for h in range(w.Hq):
+                s = torch.matmul(qd[b, h], kt[b, h // G]).float() * w.sm_scale
+                if mask is not None:
+                    s.masked_fill_(mask, float("-inf"))
+                p = torch.softmax(s, dim=-1).to(qd.dtype)
+                out[b, h] = torch.matmul(p, vd[b, h // G])
+
+    try:
+        run()
+        torch.cuda.synchronize()
+        ms = timed(run, max(1, min(steps, 3)), torch)
+    except RuntimeError as e:
+        return {"kind": "naive 16-bit attention", "error": str(e).splitlines()[0][:200]}
+    return {"kind": f"naive attention of our own: torch.matmul (hipBLASLt) for both products, "
+                    f"FP32 softmax, {w.dtype} in and out, one head at a time",
+            "ms_per_call": round(ms, 4), "TOPS": round(w.ops / (ms * 1e-3) / 1e12, 2)}
 
 
 def prep_flushed(sage, qd, kd, vd, z, steps, torch):
@@ -330,6 +363,7 @@ def main():
         line["prep"]["flushed_alg_GBps"] = round(3.0 * elems / (ms_pf * 1e-3) / 1e9, 1)
     if args.contrast:
         line["contrast"] = contrast_sdpa(w, qd, kd, vd, args.steps, torch)
+        line["contrast_naive"] = contrast_naive(w, qd, kd, vd, args.steps, torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows, qb, kb, args.pv, args.qk_bits)
     print(json.dumps(line), flush=True)
