@@ -5,13 +5,13 @@
 // article.  Memory-bound: every kernel streams 16-byte loads and does its
 // reductions in registers, wavefront shuffles and LDS.
 //
-//   prep_q      per (q head, 128-row block): Q absmax per scale group (the
-//               block, or each row at the thread-level granularity), scales
-//               and INT8 codes;
-//               one extra work-group clears the per-head arrival counters.
-//   prep_stats  per (kv head, 512-row chunk): partial statistics (float64 K
-//               channel sums, V channel absmax unless V goes to binary16).
-//               The head's last work-group
+//   clear_words clears the per-kv-head arrival counters.
+//   prep_qstats one launch for two independent jobs, so they overlap:
+//               per (kv head, 512-row chunk): partial statistics (float64 K
+//               channel sums, V channel absmax unless V goes to binary16),
+//               and per (q head, 128-row block): Q absmax per scale group
+//               (the block, or each row at the thread-level granularity),
+//               scales and integer codes.  The head's last statistics work-group
 //               to arrive (an atomic counter; nobody waits) reduces the
 //               partials in a fixed chunk order (deterministic) into the K
 //               mean and the V scales.
@@ -19,17 +19,17 @@
 //               (the block, or each 32-row half at the thread-level
 //               granularity), scales, codes;
 //               per (kv head, 128-key block) V E4M3 codes, stored as the
-//               binary16 values they denote (or V's own binary16 rounding),
-//               and transposed to the attention
-//               kernel's channel-major, permuted-key layout.  Heads are
-//               visited in the reverse order of prep_stats so the second read
-//               of K and V finds the most recent heads still in the
+//               binary16 values they denote (or as code bytes for a KV cache,
+//               or V's own binary16 rounding), transposed to the attention
+//               kernels' channel-major, permuted-key layout.  Heads are
+//               visited in the reverse order of the statistics so the second
+//               read of K and V finds the most recent heads still in the
 //               last-level cache.
 #include "sage_internal.h"
 
 namespace sage {
 
-// The arrival counters of prep_stats, one per kv head.
+// The arrival counters of the statistics, one per kv head.
 __host__ __device__ inline int sync_words(const Shape& s) { return s.B * s.Hkv; }
 
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
@@ -145,23 +145,17 @@ __device__ inline void store_v_tile(const void* vt, void* dst, int tid) {
 }
 
 // ------------------------------------------------------------ Q
-// One work-group per 128 rows of a q head; one scale per bq rows (128 or 1).
+// Work-group qb codes 128 rows of a q head; one scale per bq rows (128 or 1).
+// rmax and gmax are 128 floats of LDS each.
 template <typename In, int D>
-__global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ q, Shape s, int bq,
-                                                   float qmax, int8_t* __restrict__ q_i8,
-                                                   float* __restrict__ q_scale,
-                                                   int* __restrict__ sync) {
+__device__ inline void q_rows(const uint16_t* __restrict__ q, const Shape& s, int bq, float qmax,
+                              int8_t* __restrict__ q_i8, float* __restrict__ q_scale, int qb,
+                              float* rmax, float* gmax) {
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     constexpr int R = 128;      // rows per work-group
     constexpr int NCH = R * CPR / kThreads;  // chunks per thread
-    __shared__ float rmax[R], gmax[R];
     const int tid = threadIdx.x;
     const int nwg = s.Np / R;
-    const int qb = blockIdx.x;
-    if (qb == s.B * s.Hq * nwg) {
-        for (int i = tid; i < sync_words(s); i += kThreads) sync[i] = 0;
-        return;
-    }
     // rows [t*R, t*R+R) of head bh; rows >= N are zero padding
     const int bh = qb / nwg, t = qb % nwg;
     const long long src_head = (long long)bh * s.N * D;
@@ -196,19 +190,30 @@ __global__ __launch_bounds__(kThreads) void prep_q(const uint16_t* __restrict__ 
 }
 
 // ------------------------------------------------------------ K and V
+// Work-group wg sums one 512-row chunk of a kv head; the head's last chunk to
+// arrive forms its K mean and V scales.
+template <int D>
+struct StatsSmem {
+    static constexpr int RPI = kThreads / (D / 8);
+    double ssum[RPI][D];
+    float smax[RPI][D];
+    int last;
+};
+
 template <typename In, int D>
-__global__ __launch_bounds__(kThreads) void prep_stats(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s,
-    double* __restrict__ k_part, float* __restrict__ v_part, int* __restrict__ cnt,
-    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv, int pv16) {
+__device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                const Shape& s, double* __restrict__ k_part,
+                                float* __restrict__ v_part, int* __restrict__ cnt,
+                                float* __restrict__ k_mean, float* __restrict__ v_scale,
+                                float* __restrict__ v_inv, int pv16, int wg, StatsSmem<D>& sm) {
     constexpr int CPR = D / 8;
-    constexpr int RPI = kThreads / CPR;
-    __shared__ double ssum[RPI][D];
-    __shared__ float smax[RPI][D];
-    __shared__ int s_last;
+    constexpr int RPI = StatsSmem<D>::RPI;
+    auto& ssum = sm.ssum;
+    auto& smax = sm.smax;
+    int& s_last = sm.last;
     const int tid = threadIdx.x;
     const int nchunk = s.part_chunks();
-    const int bg = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    const int bg = wg / nchunk, chunk = wg % nchunk;
     const int cg = tid % CPR, rr = tid / CPR;
     const long long head = (long long)bg * s.N * D;
     const int r0 = chunk * kStatRows;
@@ -275,6 +280,26 @@ __global__ __launch_bounds__(kThreads) void prep_stats(
     v_inv[o] = pv16 ? 1.0f : (m > 0.0f ? 448.0f / m : 0.0f);
 }
 
+// The K/V statistics and the Q codes in one launch: they read disjoint inputs,
+// so they overlap.  Work-groups [0, nstats) take the statistics (the longer
+// ones, dispatched first), the rest the Q row blocks (nq of them, 0 for a KV
+// cache).  The arrival counters are cleared by clear_words beforehand.
+template <typename In, int D>
+__global__ __launch_bounds__(kThreads) void prep_qstats(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    Shape s, int bq, float qmax, int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
+    double* __restrict__ k_part, float* __restrict__ v_part, int* __restrict__ cnt,
+    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv, int pv16) {
+    __shared__ StatsSmem<D> stats_smem;
+    __shared__ float rmax[128], gmax[128];
+    const int nstats = s.B * s.Hkv * s.part_chunks();
+    const int wg = blockIdx.x;
+    if (wg < nstats)
+        kv_stats<In, D>(k, v, s, k_part, v_part, cnt, k_mean, v_scale, v_inv, pv16, wg, stats_smem);
+    else
+        q_rows<In, D>(q, s, bq, qmax, q_i8, q_scale, wg - nstats, rmax, gmax);
+}
+
 template <typename In, int D>
 __global__ __launch_bounds__(kThreads) void prep_pack(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s, int bk, float qmax,
@@ -286,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     const int tid = threadIdx.x;
     const int nkb = s.Np / 64, nvb = s.Np / SAGE_BN;
     const int per_head = nkb + nvb;
-    // reverse head order relative to prep_stats
+    // reverse head order relative to the statistics
     const int bg = s.B * s.Hkv - 1 - (int)(blockIdx.x / per_head);
     const int j = blockIdx.x % per_head;
     const long long src_head = (long long)bg * s.N * D;
@@ -362,22 +387,27 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
         store_v_tile<D, 2>(vt, static_cast<uint16_t*>(v_out) + tile, tid);
 }
 
-// Clears the arrival counters when the K/V half runs without prep_q (whose
-// extra work-group clears them otherwise).
+// Clears the arrival counters of prep_qstats (one per kv head), before it.
 __global__ __launch_bounds__(kThreads) void clear_words(int* __restrict__ w, int n) {
     for (int i = threadIdx.x; i < n; i += kThreads) w[i] = 0;
 }
 
 // ------------------------------------------------------------ launchers
+// Counter clearing, then the statistics with the Q codes of nq row blocks
+// (none for a KV cache), then the K and V codes.
 template <typename In, int D>
-static hipError_t launch_prep_kv_t(const void* k, const void* v, const Shape& s, const KVViews& z,
-                                   hipStream_t st) {
-    const int nchunk = s.part_chunks();
-    const int pv16 = z.v_store == kVF16;
-    hipLaunchKernelGGL((prep_stats<In, D>), dim3(s.B * s.Hkv * nchunk), dim3(kThreads), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, s, z.k_part, z.v_part, z.sync,
-                       z.k_mean, z.v_scale, z.v_inv, pv16);
+static hipError_t launch_prep_all(const void* q, const void* k, const void* v, const Shape& s,
+                                  int nq, int bq, float qmax, int8_t* q_i8, float* q_scale,
+                                  const KVViews& z, hipStream_t st) {
+    hipLaunchKernelGGL(clear_words, dim3(1), dim3(kThreads), 0, st, z.sync, sync_words(s));
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nstats = s.B * s.Hkv * s.part_chunks();
+    const int pv16 = z.v_store == kVF16;
+    hipLaunchKernelGGL((prep_qstats<In, D>), dim3(nstats + nq), dim3(kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, bq, qmax, q_i8,
+                       q_scale, z.k_part, z.v_part, z.sync, z.k_mean, z.v_scale, z.v_inv, pv16);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int per_head = s.Np / 64 + s.Np / SAGE_BN;
     hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
@@ -389,16 +419,12 @@ static hipError_t launch_prep_kv_t(const void* k, const void* v, const Shape& s,
 template <typename In, int D>
 static hipError_t launch_prep_t(const void* q, const void* k, const void* v, const Shape& s,
                                 const sage_qkv_quant* z, hipStream_t st) {
-    const int nq = s.B * s.Hq * (s.Np / 128);
     const float qmax = z->qk_bits == SAGE_QK_INT4 ? 7.0f : 127.0f;
-    hipLaunchKernelGGL((prep_q<In, D>), dim3(nq + 1), dim3(kThreads), 0, st, (const uint16_t*)q, s,
-                       (int)z->q_block, qmax, z->q_i8, z->q_scale, z->sync);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const KVViews kv = {z->k_i8,   z->k_scale, z->k_mean, z->v16,     z->v_scale,
                         z->v_inv,  z->k_part,  z->v_part, z->sync,    z->k_block,
                         z->pv_format == SAGE_PV_F16 ? kVF16 : kVE4M3Half, qmax};
-    return launch_prep_kv_t<In, D>(k, v, s, kv, st);
+    return launch_prep_all<In, D>(q, k, v, s, s.B * s.Hq * (s.Np / 128), (int)z->q_block, qmax,
+                                  z->q_i8, z->q_scale, kv, st);
 }
 
 hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, const Shape& s,
@@ -412,14 +438,14 @@ hipError_t launch_prep(const void* q, const void* k, const void* v, int dtype, c
 
 hipError_t launch_prep_kv(const void* k, const void* v, int dtype, const Shape& s, const KVViews& z,
                           hipStream_t st) {
-    hipLaunchKernelGGL(clear_words, dim3(1), dim3(kThreads), 0, st, z.sync, sync_words(s));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     if (dtype == SAGE_F16)
-        return s.d == 64 ? launch_prep_kv_t<_Float16, 64>(k, v, s, z, st)
-                         : launch_prep_kv_t<_Float16, 128>(k, v, s, z, st);
-    return s.d == 64 ? launch_prep_kv_t<Bf16Tag, 64>(k, v, s, z, st)
-                     : launch_prep_kv_t<Bf16Tag, 128>(k, v, s, z, st);
+        return s.d == 64 ? launch_prep_all<_Float16, 64>(nullptr, k, v, s, 0, 1, z.qmax, nullptr,
+                                                         nullptr, z, st)
+                         : launch_prep_all<_Float16, 128>(nullptr, k, v, s, 0, 1, z.qmax, nullptr,
+                                                          nullptr, z, st);
+    return s.d == 64 ? launch_prep_all<Bf16Tag, 64>(nullptr, k, v, s, 0, 1, z.qmax, nullptr, nullptr, z, st)
+                     : launch_prep_all<Bf16Tag, 128>(nullptr, k, v, s, 0, 1, z.qmax, nullptr, nullptr,
+                                                     z, st);
 }
 
 int prep_sync_words(const Shape& s) { return sync_words(s); }
