@@ -86,7 +86,7 @@ __device__ inline void group_absmax(float (&am)[NCH], int G, float* rmax, float*
 // The binary16 values of the E4M3 codes of x[i] * inv[i], i = 0..7, into the
 // transposed V tile vt[D][SAGE_BN] at key position pos.
 template <int D>
-__device__ inline void v_codes_to_tile(const float (&x)[8], const float* inv, int col, int pos,
+__device__ inline void v_codes_to_tile(const float (&x)[8], const float (&inv)[8], int col, int pos,
                                        uint16_t* vt) {
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
@@ -108,7 +108,7 @@ __device__ inline void v_codes_to_tile(const float (&x)[8], const float* inv, in
 // The E4M3 code bytes of x[i] * inv[i], i = 0..7, into the transposed byte
 // tile vt[D][SAGE_BN] at key position pos (a KV cache's V).
 template <int D>
-__device__ inline void v_codes_to_tile8(const float (&x)[8], const float* inv, int col, int pos,
+__device__ inline void v_codes_to_tile8(const float (&x)[8], const float (&inv)[8], int col, int pos,
                                         uint8_t* vt) {
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
@@ -160,15 +160,22 @@ __device__ inline void q_rows(const uint16_t* __restrict__ q, const Shape& s, in
     const int bh = qb / nwg, t = qb % nwg;
     const long long src_head = (long long)bh * s.N * D;
     const long long dst_head = (long long)bh * s.Np * D;
+    // all of this thread's loads first (rows past N read row N-1 and are
+    // zeroed), so they are in flight together
+    uint4 u[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = tid + c * kThreads;
+        const int row = min(t * R + e / CPR, s.N - 1), col = (e % CPR) * 8;
+        u[c] = *reinterpret_cast<const uint4*>(q + src_head + (long long)row * D + col);
+    }
     float x[NCH][8], am[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
-        const int row = t * R + e / CPR, col = (e % CPR) * 8;
-        if (row < s.N) {
-            const uint4 u = *reinterpret_cast<const uint4*>(q + src_head + (long long)row * D + col);
-            unpack8<In>(u, x[c]);
-        } else {
+        const int row = t * R + e / CPR;
+        unpack8<In>(u[c], x[c]);
+        if (row >= s.N) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[c][i] = 0.0f;
         }
@@ -225,13 +232,39 @@ __device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* 
         sum[i] = 0.0;
         mx[i] = 0.0f;
     }
-    for (int r = r0 + rr; r < r1; r += RPI) {
+    // four rows per step, their loads issued together (the float64 sums of
+    // 16-bit inputs are exact, so the order does not matter)
+    constexpr int U = 4;
+    int r = r0 + rr;
+    for (; r + (U - 1) * RPI < r1; r += U * RPI) {
+        uint4 uk[U], uv[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const long long off = head + (long long)(r + j * RPI) * D + cg * 8;
+            uk[j] = *reinterpret_cast<const uint4*>(k + off);
+            if (!pv16) uv[j] = *reinterpret_cast<const uint4*>(v + off);
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float fk[8];
+            unpack8<In>(uk[j], fk);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sum[i] += (double)fk[i];
+            if (!pv16) {  // binary16 V needs no channel scale
+                float fv[8];
+                unpack8<In>(uv[j], fv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(fv[i]));
+            }
+        }
+    }
+    for (; r < r1; r += RPI) {
         const long long off = head + (long long)r * D + cg * 8;
         float fk[8];
         unpack8<In>(*reinterpret_cast<const uint4*>(k + off), fk);
 #pragma unroll
         for (int i = 0; i < 8; ++i) sum[i] += (double)fk[i];
-        if (!pv16) {  // binary16 V needs no channel scale
+        if (!pv16) {
             float fv[8];
             unpack8<In>(*reinterpret_cast<const uint4*>(v + off), fv);
 #pragma unroll
@@ -322,15 +355,28 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
         constexpr int R = 64;
         constexpr int NCH = R * CPR / kThreads;
         const long long dst_head = (long long)bg * s.Np * D;
+        uint4 u[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int e = tid + c * kThreads;
+            const int row = min(t * R + e / CPR, s.N - 1), col = (e % CPR) * 8;
+            u[c] = *reinterpret_cast<const uint4*>(k + src_head + (long long)row * D + col);
+        }
+        // a thread's column is the same in every chunk (kThreads % CPR == 0)
+        float mean[8];
+        {
+            const float4* mp = reinterpret_cast<const float4*>(k_mean + (long long)bg * D + (tid % CPR) * 8);
+            const float4 m0 = mp[0], m1 = mp[1];
+            mean[0] = m0.x, mean[1] = m0.y, mean[2] = m0.z, mean[3] = m0.w;
+            mean[4] = m1.x, mean[5] = m1.y, mean[6] = m1.z, mean[7] = m1.w;
+        }
         float x[NCH][8], am[NCH];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int e = tid + c * kThreads;
-            const int row = t * R + e / CPR, col = (e % CPR) * 8;
+            const int row = t * R + e / CPR;
             if (row < s.N) {
-                const uint4 u = *reinterpret_cast<const uint4*>(k + src_head + (long long)row * D + col);
-                unpack8<In>(u, x[c]);
-                const float* mean = k_mean + (long long)bg * D + col;
+                unpack8<In>(u[c], x[c]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) x[c][i] = x[c][i] - mean[i];
             } else {
@@ -358,26 +404,39 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     // V block T: 128 keys x D channels, transposed through LDS.
     const int T = j - nkb;
     constexpr int NCH = SAGE_BN * CPR / kThreads;
+    static_assert(kThreads % CPR == 0, "a thread keeps its column in every chunk");
+    float inv[8];
+    if (v_store != kVF16) {
+        const float4* ip = reinterpret_cast<const float4*>(v_inv + (long long)bg * D + (tid % CPR) * 8);
+        const float4 i0 = ip[0], i1 = ip[1];
+        inv[0] = i0.x, inv[1] = i0.y, inv[2] = i0.z, inv[3] = i0.w;
+        inv[4] = i1.x, inv[5] = i1.y, inv[6] = i1.z, inv[7] = i1.w;
+    }
+    uint4 u[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = tid + c * kThreads;
+        const int row = min(T * SAGE_BN + e / CPR, s.N - 1), col = (e % CPR) * 8;
+        u[c] = *reinterpret_cast<const uint4*>(v + src_head + (long long)row * D + col);
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
         const int key = e / CPR, col = (e % CPR) * 8;
         const int row = T * SAGE_BN + key;
         float x[8];
-        if (row < s.N) {
-            const uint4 u = *reinterpret_cast<const uint4*>(v + src_head + (long long)row * D + col);
-            unpack8<In>(u, x);
-        } else {
+        unpack8<In>(u[c], x);
+        if (row >= s.N) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = 0.0f;
         }
         if (v_store == kVF16)
             v_f16_to_tile<D>(x, col, v_key_position(key), vt);
         else if (v_store == kVE4M3Byte)
-            v_codes_to_tile8<D>(x, v_inv + (long long)bg * D + col, col, v_key_position(key),
+            v_codes_to_tile8<D>(x, inv, col, v_key_position(key),
                                 reinterpret_cast<uint8_t*>(vt));
         else
-            v_codes_to_tile<D>(x, v_inv + (long long)bg * D + col, col, v_key_position(key), vt);
+            v_codes_to_tile<D>(x, inv, col, v_key_position(key), vt);
     }
     __syncthreads();
     const long long tile = ((long long)bg * nvb + T) * (long long)(D * SAGE_BN);
