@@ -341,10 +341,13 @@ SAGE_DECODE_INST_K(Bf16Tag, 128)
 template __global__ void decode_merge<64>(DecodeArgs);
 template __global__ void decode_merge<128>(DecodeArgs);
 
-// Chunking: enough work-groups for two rounds of kDecodeWavesPerCU per CU (a
+// Chunking: about one round of work-groups, kDecodeWavesPerCU per CU (a
 // binary16 cache fits fewer at once and is split the same way), in chunks of
-// at least kMinChunkBlocks blocks so that filling each work-group's two-tile
-// pipeline stays a small part of its work.
+// at least kMinChunkBlocks blocks so that filling each work-group's tile
+// pipeline stays a small part of its work.  One round beat two on both the
+// 32768-key single-sequence cache and the batch of eight 8192-key caches
+// (fewer partials to merge, no second-round tail).  The chunk count rounds
+// down so that the grid does not spill a short second round.
 constexpr int kMinChunkBlocks = 2;
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
@@ -354,8 +357,9 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     const int nkb = (Nk + SAGE_BN - 1) / SAGE_BN;
     const long long units = (long long)B * Hkv * pl.row_tiles;
     (void)d;
-    const long long target = 2LL * 256 * kDecodeWavesPerCU;
-    long long want = (target + units - 1) / units;
+    const long long target = 256LL * kDecodeWavesPerCU;
+    long long want = target / units;
+    if (want < 1) want = 1;
     int per = (int)((nkb + want - 1) / want);
     if (per < kMinChunkBlocks) per = kMinChunkBlocks;
     if (per > nkb) per = nkb;
