@@ -243,83 +243,80 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     if (h == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(mref, lsum);
 }
 
-// One work-group of 256 threads per query row: out = O * s_V / l over the
-// row's chunks, each weighted by 2^(its reference max - the largest).  The
-// chunk weights are formed once (one thread per chunk), then every
-// (chunk, channel) partial is read by its own thread, so all loads are in
-// flight together, and the sums are reduced in LDS.
+// One work-group per query row: out = O * s_V / l over the row's chunks, each
+// weighted by 2^(its reference max - the largest).  Every thread issues its
+// loads first (the max and row sum of chunk t, and the partial O of channel
+// t % D for chunks t / D, t / D + GROUPS, ...), so the merge waits on one
+// round trip to memory; the largest max, the weighted row sum and the sum
+// over chunk groups then take wave shuffles and one LDS exchange each.  The
+// key split never makes more than kMergeThreads chunks.
 constexpr int kMergeThreads = 1024;
+constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMergeLoads = 16;  // partial-O loads per thread issued together
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a) {
     constexpr int GROUPS = kMergeThreads / D;  // chunk groups summed in parallel
-    __shared__ float red[kMergeThreads];
     __shared__ float wgt[kMergeThreads];
-    __shared__ float s_M, s_l;
-    const long long row = blockIdx.x;  // (b * Hq + hq) * Nq + i
-    const int t = threadIdx.x;
-    const int hq = (int)((row / a.Nq) % a.Hq), b = (int)(row / ((long long)a.Nq * a.Hq));
+    __shared__ float osum[kMergeThreads];
+    __shared__ float wmax[kMergeWaves], wl[kMergeWaves];
+    const int row32 = blockIdx.x;  // (b * Hq + hq) * Nq + i
+    const long long row = row32;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int nchunk = a.nchunk;
+    const int bh = row32 / a.Nq;
+    const int hq = bh % a.Hq, b = bh / a.Hq;
     const int bg = b * a.Hkv + hq / a.G;
-    const float* ml = a.part_ml + row * a.nchunk * 2;
-    const float* po = a.part_o + row * a.nchunk * D;
-
-    // the largest reference max (an empty chunk has -inf)
-    float m = -INFINITY;
-    for (int k = t; k < a.nchunk; k += kMergeThreads) m = fmaxf(m, ml[2 * k]);
-    red[t] = m;
-    __syncthreads();
-    for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
-        if (t < o) red[t] = fmaxf(red[t], red[t + o]);
-        __syncthreads();
-    }
-    if (t == 0) s_M = red[0];
-    __syncthreads();
-    const float M = s_M;
-
-    // row sum; the chunk weights of the first kMergeThreads chunks stay in LDS
-    float l = 0.0f;
-    for (int k = t; k < a.nchunk; k += kMergeThreads) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * k] - M);
-        if (k < kMergeThreads) wgt[k] = w;
-        l = __builtin_fmaf(ml[2 * k + 1], w, l);
-    }
-    __syncthreads();
-    red[t] = l;
-    __syncthreads();
-    for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
-        if (t < o) red[t] += red[t + o];
-        __syncthreads();
-    }
-    if (t == 0) s_l = red[0];
-    __syncthreads();
-
-    // O: thread t sums channel t % D over chunks k = t / D (mod GROUPS),
-    // eight chunks' loads issued together
+    const float* ml = a.part_ml + row * nchunk * 2;
+    const float* po = a.part_o + row * nchunk * D;
     const int c = t % D, grp = t / D;
-    float o = 0.0f;
-    int k = grp;
-    for (; k + 7 * GROUPS < a.nchunk; k += 8 * GROUPS) {
-        float x[8], w[8];
+
+    // an empty chunk, and a thread past the last chunk, have max -inf, sum 0
+    const float2 mlt = t < nchunk ? *reinterpret_cast<const float2*>(ml + 2 * t)
+                                  : make_float2(-INFINITY, 0.0f);
+    float x[kMergeLoads];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = po[(long long)(k + u * GROUPS) * D + c];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int kk = k + u * GROUPS;
-            w[u] = kk < kMergeThreads ? wgt[kk] : __builtin_amdgcn_exp2f(ml[2 * kk] - M);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o = __builtin_fmaf(x[u], w[u], o);
+    for (int u = 0; u < kMergeLoads; ++u) {
+        const int k = grp + u * GROUPS;
+        x[u] = k < nchunk ? po[(long long)k * D + c] : 0.0f;
     }
-    for (; k < a.nchunk; k += GROUPS) {
-        const float w = k < kMergeThreads ? wgt[k] : __builtin_amdgcn_exp2f(ml[2 * k] - M);
-        o = __builtin_fmaf(po[(long long)k * D + c], w, o);
-    }
+
+    const float mw = wave_max(mlt.x);
+    if (lane == 0) wmax[wave] = mw;
     __syncthreads();
-    red[t] = o;
+    float M = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kMergeWaves; ++i) M = fmaxf(M, wmax[i]);
+
+    const float w = t < nchunk ? __builtin_amdgcn_exp2f(mlt.x - M) : 0.0f;
+    wgt[t] = w;
+    const float lw = wave_sum(mlt.y * w);
+    if (lane == 0) wl[wave] = lw;
+    __syncthreads();
+    float l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMergeWaves; ++i) l += wl[i];
+
+    float o = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kMergeLoads; ++u) {
+        const int k = grp + u * GROUPS;
+        if (k < nchunk) o = __builtin_fmaf(x[u], wgt[k], o);
+    }
+    for (int k = grp + kMergeLoads * GROUPS; k < nchunk; k += GROUPS)
+        o = __builtin_fmaf(po[(long long)k * D + c], wgt[k], o);
+    osum[t] = o;
     __syncthreads();
     if (grp == 0) {
-        for (int g2 = 1; g2 < GROUPS; ++g2) o += red[g2 * D + c];
-        a.out[row * D + c] = o * a.v_scale[(long long)bg * D + c] * (1.0f / s_l);
+#pragma unroll
+        for (int g2 = 1; g2 < GROUPS; ++g2) o += osum[g2 * D + c];
+        a.out[row * D + c] = o * a.v_scale[(long long)bg * D + c] * (1.0f / l);
     }
 }
 
@@ -349,6 +346,7 @@ template __global__ void decode_merge<128>(DecodeArgs);
 // (fewer partials to merge, no second-round tail).  The chunk count rounds
 // down so that the grid does not spill a short second round.
 constexpr int kMinChunkBlocks = 2;
+static_assert(256 * kDecodeWavesPerCU <= kMergeThreads, "a row's chunks must fit one merge work-group");
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     DecodePlan pl;
@@ -371,6 +369,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     constexpr size_t lds = decode_lds<D, PV16>();
+    if (a.nchunk > kMergeThreads) return hipErrorInvalidValue;  // not reached: see decode_plan
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)attn_decode<In, D, KSPLIT, CAUSAL, PV16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
