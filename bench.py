@@ -63,6 +63,8 @@ def parse():
 
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_attention_02_amd", "csrc", f)
                   for f in ("attn_fwd.hip", "attn_block.h", "sage_internal.h")]
+DECODE_SOURCES = [os.path.join(ROOT, "bit_quantized_attention_02_amd", "csrc", f)
+                  for f in ("attn_decode.hip", "attn_block.h", "sage_internal.h")]
 
 
 def kernel_digest(paths=KERNEL_SOURCES):
@@ -75,18 +77,20 @@ def kernel_digest(paths=KERNEL_SOURCES):
     return h.hexdigest()
 
 
-def measured_traffic(granularity, pv, qk_bits):
-    """(workload, HBM bytes per attention launch) from the committed
-    byte-counter summary taken with this granularity and P.V format, or
-    (None, None) when the kernel sources changed since the counters were
-    taken."""
+def measured_traffic(granularity, pv, qk_bits, prefix="attn_fwd", sources=KERNEL_SOURCES,
+                     workload=None):
+    """(workload, HBM bytes per launch) from a committed byte-counter summary
+    (profiles/<prefix>_*_counters.json) taken with this granularity, P.V
+    format and Q/K width (and on `workload`, when given), or (None, None)
+    when the kernel sources changed since the counters were taken."""
     import glob
-    digest = kernel_digest()
-    for path in glob.glob(os.path.join(ROOT, "profiles", "attn_fwd_*_counters.json")):
+    digest = kernel_digest(sources)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"{prefix}_*_counters.json"))):
         with open(path) as f:
             d = json.load(f)
         if (d.get("kernel_source_sha256") == digest and d.get("granularity", "block") == granularity
-                and d.get("pv_format", "e4m3") == pv and d.get("qk_bits", 8) == qk_bits):
+                and d.get("pv_format", "e4m3") == pv and d.get("qk_bits", 8) == qk_bits
+                and (workload is None or d.get("workload") == workload)):
             return d.get("workload"), d.get("traffic_bytes_per_launch")
     return None, None
 
@@ -262,6 +266,7 @@ def bench_decode(args, sage, workloads, torch):
     nb = decode_bytes(w, kb, args.pv)
     gbs = nb / (ms * 1e-3) / 1e9
     fp16_kv = 2 * 2 * w.B * w.Hkv * w.N * w.d
+    _, traffic = measured_traffic(args.granularity, args.pv, 8, "attn_decode", DECODE_SOURCES, w.name)
     line = {
         "metric": "short-query attention over a quantized KV cache, GB/s of cache read (1 GPU)",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -272,7 +277,7 @@ def bench_decode(args, sage, workloads, torch):
                    "d": w.d, "causal": w.causal, "input_dtype": w.dtype, "k_block": kb,
                    "pv_format": args.pv, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attn_decode (+ decode_merge)", "bytes_per_launch": nb},
         "cache": {"bytes": int(cache.buf.numel()), "fp16_kv_bytes": fp16_kv,
                   "ratio": round(cache.buf.numel() / fp16_kv, 4),
