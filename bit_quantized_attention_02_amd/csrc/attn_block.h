@@ -127,17 +127,26 @@ struct TileLoader {
         }
     }
 
-    __device__ inline void load(int T, uint8_t* lk, void* lv, int wave) const {
+    // KR instructions
+    __device__ inline void load_k(int T, uint8_t* lk, int wave) const {
 #pragma unroll
         for (int r = 0; r < KR; ++r)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 krs, (__attribute__((address_space(3))) void*)(lk + (r * NT + wave * 64) * 16), 16,
                 koff[r % KP], T * SAGE_BN * D + (r / KP) * KP * NT * 16, 0, 0);
+    }
+    // VR instructions
+    __device__ inline void load_v(int T, void* lv, int wave) const {
 #pragma unroll
         for (int r = 0; r < VR; ++r)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 vrs, (__attribute__((address_space(3))) void*)((uint8_t*)lv + (r * NT + wave * 64) * 16),
                 16, voff[r % VP], T * SAGE_BN * D * VB + (r / VP) * VP * NT * 16, 0, 0);
+    }
+    // K then V
+    __device__ inline void load(int T, uint8_t* lk, void* lv, int wave) const {
+        load_k(T, lk, wave);
+        load_v(T, lv, wave);
     }
 };
 
@@ -156,45 +165,36 @@ __device__ inline v8h row_sum_selector(int lane) {
     return r;
 }
 
+// An 8-byte LDS read as one vector load.  (Read as a uint2 structure it is
+// split into two scalar loads that carry no type-based alias information, and
+// the compiler then makes them wait for every copy into LDS still in flight,
+// such as the next block's K tile.)
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2u lds_read8(const uint8_t* p) {
+    return *reinterpret_cast<const v2u*>(p);
+}
+
 // Maximum over the two lanes (l, l^32) that hold one query row.
 __device__ inline int max_across_halves(int x) {
     auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
     return max((int)a[0], (int)a[1]);
 }
 
-// One key block for one wave (32 query rows).  MASKED: some keys of the
-// block are excluded (causal diagonal, or keys >= N).  PV16: P is rounded to
-// binary16 directly (l448 is then 0) instead of through E4M3.  V8: the V tile
-// holds E4M3 code bytes (a KV cache), converted to binary16 -- exactly -- as
-// each fragment is read.  SEEDED (INT8 codes): the accumulator is seeded with
-// 1.5*2^23 and read as a float; without it (the INT4 codes of the 4-bit
-// variant, whose score factors are about 330 times larger, so the seed's
-// float32 rounding would no longer be negligible) each score is converted
-// from the integer accumulator, one more instruction per score.
-// KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
-// 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
-// log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false,
-          bool SEEDED = true>
-__device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
-                                           const void* __restrict__ lv,
-                                           const v4i (&qf)[D / 32], int T, int row, int N,
-                                           const float (&c)[KSPLIT], float l448, int h, int r32,
-                                           const v8h& rsel, float& mref, float& lsum,
-                                           v16f (&O)[D / 32]) {
-    constexpr int KS = D / 32, CT = D / 32;
-    constexpr int TPG = 4 / KSPLIT;  // tiles per scale group
-    float u[KSPLIT];
-#pragma unroll
-    for (int g = 0; g < KSPLIT; ++g) u[g] = SEEDED ? kSeed * c[g] : 0.0f;
-
-    // ---- S^T = K Q^T (INT32).  Tile t, element v: key 32t + 8(v/4) + 4h + v%4.
-    v16i S[4];
+// S^T = K Q^T of one key block for one wave (32 query rows), INT32, on
+// v_mfma_i32_32x32x32_i8.  Tile t, element v: key 32t + 8(v/4) + 4h + v%4.
+// SEEDED (INT8 codes): the accumulator is seeded with the bit pattern of
+// 1.5*2^23, so the result read as a float32 is exactly 1.5*2^23 + acc
+// (|acc| < 2^22).  Without it (the INT4 codes of the 4-bit variant, whose
+// score factors are about 330 times larger, so the seed's float32 rounding
+// would no longer be negligible) the plain sums are returned and each score
+// is converted from the integer accumulator, one more instruction per score.
+template <int D, bool SEEDED>
+__device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, const v4i (&qf)[D / 32],
+                                             int h, int r32, v16i (&S)[4]) {
+    constexpr int KS = D / 32;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int kr = 32 * t + r32;
-        // seeded with the bit pattern of 1.5*2^23: the INT32 result, read as a
-        // float32, is exactly 1.5*2^23 + acc (|acc| < 2^22)
         v16i acc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] = SEEDED ? kSeedBits : 0;
@@ -205,6 +205,28 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
         }
         S[t] = acc;
     }
+}
+
+// The rest of one key block for one wave, from its scores S: masking, online
+// softmax, P and both levels of P.V.  MASKED: some keys of the block are
+// excluded (causal diagonal, or keys >= N).  PV16: P is rounded to binary16
+// directly (l448 is then 0) instead of through E4M3.  V8: the V tile holds
+// E4M3 code bytes (a KV cache), converted to binary16 -- exactly -- as each
+// fragment is read.  SEEDED: as for block_scores.
+// KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
+// 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
+// log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false,
+          bool SEEDED = true>
+__device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __restrict__ lv, int T,
+                                                 int row, int N, const float (&c)[KSPLIT], float l448,
+                                                 int h, int r32, const v8h& rsel, float& mref,
+                                                 float& lsum, v16f (&O)[D / 32]) {
+    constexpr int CT = D / 32;
+    constexpr int TPG = 4 / KSPLIT;  // tiles per scale group
+    float u[KSPLIT];
+#pragma unroll
+    for (int g = 0; g < KSPLIT; ++g) u[g] = SEEDED ? kSeed * c[g] : 0.0f;
 
     // ---- block maxima, one per K-scale group
     if (MASKED) {
@@ -313,7 +335,7 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                 v8h vf;
                 if (V8) {
                     // keys 16s + 8h .. +8 of the channel: 8 code bytes
-                    const uint2 raw = *reinterpret_cast<const uint2*>(
+                    const v2u raw = lds_read8(
                         (const uint8_t*)lv + ch * SAGE_BN + ((s ^ vswz8(ch)) << 4) + 8 * h);
                     const v4i w = {
                         __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.x, 1.0f, false)),
@@ -336,6 +358,21 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                 O[pass * CG + j][v] = __builtin_fmaf(acc[j][v], w, O[pass * CG + j][v]);
     }
     lsum = __builtin_fmaf(rs[0], w, lsum);
+}
+
+// One whole key block for one wave: block_scores, then block_softmax_pv.
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false,
+          bool SEEDED = true>
+__device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
+                                           const void* __restrict__ lv,
+                                           const v4i (&qf)[D / 32], int T, int row, int N,
+                                           const float (&c)[KSPLIT], float l448, int h, int r32,
+                                           const v8h& rsel, float& mref, float& lsum,
+                                           v16f (&O)[D / 32]) {
+    v16i S[4];
+    block_scores<D, SEEDED>(lk, qf, h, r32, S);
+    block_softmax_pv<D, KSPLIT, CAUSAL, PV16, MASKED, V8, SEEDED>(S, lv, T, row, N, c, l448, h, r32,
+                                                                 rsel, mref, lsum, O);
 }
 
 }  // namespace sage

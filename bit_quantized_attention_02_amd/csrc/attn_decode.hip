@@ -96,9 +96,9 @@ constexpr int cache_vb() {
 
 // LDS tile buffers per work-group.  A decode wave needs more than half the
 // register file, so a CU runs at most one per SIMD, four in all; at d = 128 a
-// second buffer would leave LDS for only two of them.  With one buffer the
-// next block's copy waits for the current block's products, and the other
-// waves of the CU cover that wait.
+// second buffer would leave LDS for only two of them.  With one buffer per
+// tile, the next block's K tile is copied once this block's K fragments are
+// read and its V tile once this block's products have read theirs.
 template <int D>
 constexpr int decode_bufs() {
     return D == 128 ? 1 : 2;
@@ -169,7 +169,8 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     load_q_row<D>(a.q + grow * D, valid, h, qraw);
     typedef float kvec __attribute__((ext_vector_type(KSPLIT)));
     kvec kscale = *reinterpret_cast<const kvec*>(ksc + KSPLIT * T0);
-    const TileLoader<D, 1, VB> tiles(kbase, vbase, a.Np, 0, lane);
+    typedef TileLoader<D, 1, VB> Loader;
+    const Loader tiles(kbase, vbase, a.Np, 0, lane);
     tiles.load(T0, lk0, lv0, 0);
     // keep the quantization between the copy's issue and its wait: nothing
     // is scheduled across the barrier, and the empty asm statements take the
@@ -181,9 +182,58 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) asm volatile("" : "+v"(qf[ks]));
     asm volatile("" : "+v"(sq));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (NBUF == 1) {
+        // the first block's scores need its K tile only (the V tile was
+        // issued after it, and waits count in issue order)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Loader::VR) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    for (int T = T0; T < T1; ++T) {
+    if constexpr (NBUF == 1) {
+        // One buffer per tile: the next block's K tile is copied as soon as
+        // this block's K fragments have been read, and its V tile once this
+        // block's products have read theirs, so both copies run under this
+        // block's work; each tile is waited for only where it is first read.
+        for (int T = T0; T < T1; ++T) {
+            const bool more = T + 1 < T1;
+            const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
+            float c[KSPLIT];
+#pragma unroll
+            for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * kscale[gg]) * a.qk;
+            v16i S[4];
+            block_scores<D, true>(lk0, qf, h, r32, S);
+            if (more) {
+                // the K fragments are in registers: the tile can be replaced.
+                // (The destination goes through an empty asm statement: with
+                // its address in view, the compiler makes the V fragment reads
+                // below wait for this copy; the explicit waits order them.)
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                uint8_t* kdst = lk0;
+                asm volatile("" : "+s"(kdst));
+                tiles.load_k(T + 1, kdst, 0);
+            }
+            // V(T) was issued before knext and the next K tile
+            if (more)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Loader::KR + 1) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+            if (T < first_masked)
+                block_softmax_pv<D, KSPLIT, CAUSAL, PV16, false, V8, true>(
+                    S, lv0, T, pos, a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
+            else
+                block_softmax_pv<D, KSPLIT, CAUSAL, PV16, true, V8, true>(
+                    S, lv0, T, pos, a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
+            kscale = knext;
+            if (more) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                tiles.load_v(T + 1, lv0, 0);
+                // the next block's scores need its K tile only
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Loader::VR) : "memory");
+            }
+        }
+    }
+    for (int T = T0; NBUF == 2 && T < T1; ++T) {
         const bool odd = NBUF == 2 && ((T - T0) & 1);
         const bool more = T + 1 < T1;
         // the next block's K scales before its tile copy (waits count in
@@ -200,11 +250,6 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
             attn_block<D, KSPLIT, CAUSAL, PV16, true, V8>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
                                                           a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
-        if (NBUF == 1 && more) {
-            // every LDS read of this block has been consumed by its products
-            __syncthreads();
-            tiles.load(T + 1, lk0, lv0, 0);
-        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }

@@ -123,7 +123,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         float c[KSPLIT];
 #pragma unroll
         for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-        if (T < n_full)
+        // (without causality only the ragged last block is left here: one
+        // body, whose registers then need no spilling at d = 128)
+        if (CAUSAL && T < n_full)
             attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
                                                        a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         else if (T <= wave_last)
