@@ -98,9 +98,11 @@ static int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     int rc = check_shape(B, Hq, Hkv, Nk, d);
     if (rc != SAGE_OK) return rc;
     if (Nq > SAGE_MAX_N) return SAGE_ERR_UNSUPPORTED;
+    // query rows (and so the G * Nq packed rows of a kv head) fit an int
+    // before the plan is formed from them
+    if ((long long)B * Hq * Nq >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
     const sage::DecodePlan pl = sage::decode_plan(B, Hq, Hkv, Nq, Nk, d);
     if ((long long)B * Hkv * pl.nchunk * pl.row_tiles >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
-    if ((long long)B * Hq * Nq >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
     return SAGE_OK;
 }
 

@@ -260,6 +260,9 @@ def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
     assert sage.sage_decode_workspace_bytes(1, 8, 2, 1, 300, 64) >= 256
     assert sage.sage_decode_workspace_bytes(1, 8, 2, 0, 300, 64) == 0
     assert sage.sage_decode_workspace_bytes(1, 7, 2, 1, 300, 64) == 0
+    # 4096 q heads on one kv head with 2^20 query rows: the packed rows of a
+    # kv head (G * Nq = 2^32) do not fit an int, refused before any plan
+    assert sage.sage_decode_workspace_bytes(1, 4096, 1, 1 << 20, 1 << 20, 64) == 0
     wsb = sage.sage_decode_workspace_bytes(1, 8, 2, 1, 300, 64)
 
     def dec(q=fake, dt=0, c=zp, out=fake, B=1, Hq=8, Hkv=2, Nq=1, Nk=300, d=64, causal=1, sm=0.125,
@@ -277,6 +280,7 @@ def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
     assert dec(sm=0.0) == sage.SAGE_ERR_INVALID_ARG
     assert dec(Hq=7) == sage.SAGE_ERR_UNSUPPORTED
     assert dec(d=96) == sage.SAGE_ERR_UNSUPPORTED
+    assert dec(Hq=4096, Hkv=1, Nq=1 << 20, Nk=1 << 20) == sage.SAGE_ERR_UNSUPPORTED
     assert dec(ws=None) == sage.SAGE_ERR_WORKSPACE
     assert dec(ws=fake + 64) == sage.SAGE_ERR_WORKSPACE
     assert dec(n=wsb - 1) == sage.SAGE_ERR_WORKSPACE
