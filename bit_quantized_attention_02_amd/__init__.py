@@ -25,6 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_HIP = 0, -1, -2, -3, -4
 SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_BQ, SAGE_BK, SAGE_BN, SAGE_NPAD = 128, 64, 128, 256
+SAGE_MAX_N = 1 << 20  # longest sequence (N, Nk, Nq) the library accepts
 SAGE_BQ_THREAD, SAGE_BK_THREAD = 1, 32
 SAGE_PV_E4M3, SAGE_PV_F16 = 0, 1
 SAGE_QK_INT8, SAGE_QK_INT4 = 8, 4

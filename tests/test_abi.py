@@ -39,6 +39,22 @@ def test_config_and_layout(sage):
     assert sage.sage_v_key_position(-1) == -1 and sage.sage_v_key_position(128) == -1
 
 
+def test_binding_constants_match_the_header(sage):
+    """Every SAGE_ constant the binding mirrors has the header's value."""
+    text = open(HEADER).read()
+    defines = {m.group(1): m.group(2) for m in
+               re.finditer(r"#define\s+(SAGE_[A-Z0-9_]+)\s+(\(?[0-9]+(?:\s*<<\s*[0-9]+)?\)?)", text)}
+    assert len(defines) >= 8
+    checked = 0
+    for name, expr in defines.items():
+        if hasattr(sage, name):
+            assert getattr(sage, name) == eval(expr, {}), name
+            checked += 1
+    assert checked >= 8
+    for name in ("SAGE_BQ", "SAGE_BK", "SAGE_BN", "SAGE_NPAD", "SAGE_MAX_N", "SAGE_PV_F16", "SAGE_QK_INT4"):
+        assert name in defines and hasattr(sage, name), name
+
+
 def test_status_strings(sage):
     for st in (0, -1, -2, -3, -4):
         assert sage.sage_status_string(st)

@@ -1,0 +1,124 @@
+"""GPU parity at the largest sizes the C ABI accepts, through the C ABI,
+against the CPU oracle on the heads and rows it can afford.
+
+- Prefill at N = 2^20 (the largest sequence accepted) with 16 heads of
+  d = 128, causal: each operand tensor holds 2^31 elements, so the last
+  head starts 2^31 - 2^27 elements (about 4 GB of bf16 input) into its
+  tensor, past any 32-bit byte offset.  The first and last heads' quantized
+  operands are compared bit for bit, and rows across them (first, last,
+  tile and block edges, a seeded sample) against the oracle.
+- Decode over a 2^20-key cache with one kv head: the key split then makes
+  1024 chunks, the most the merge work-group takes.
+
+Inputs are seeded normal values drawn on the device (drawing 2^31 values on
+the host would take minutes); each head the oracle sees is copied from them.
+The oracle only needs the heads it checks: K's mean and V's scales are per
+head, so a head quantizes the same alone as inside the whole tensor.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L1 = 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_attention_02_amd as s
+    return s
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _normal(shape, seed, scale):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    return x.mul_(scale).to(torch.bfloat16)
+
+
+def _check_attn(orc, got, oz, causal, sm_scale, rows):
+    nom, lo, hi, flagged = orc.attn_q(oz, causal, sm_scale, rows=rows)
+    g = got.astype(np.float64)
+    assert np.isfinite(g).all()
+    dist = orc.interval_distance(g, lo, hi)
+    max_abs = float(dist.max())
+    rel = float(dist.sum() / np.abs(nom).sum())
+    _say(f"   parity: max|dist|={max_abs:.3e} relL1={rel:.3e} "
+         f"nominal max={float(np.abs(g - nom).max()):.3e} flagged={int(flagged.sum())}")
+    assert max_abs <= MAX_ABS and rel <= REL_L1
+
+
+def _head_view(sage, z, h, Np, d):
+    """The carved operands of head h alone (no GQA: the q and kv head
+    indices agree), as a one-head carving."""
+    zh = sage.sage_qkv_quant.from_buffer_copy(z)
+    zh.q_i8 = z.q_i8 + h * Np * d
+    zh.k_i8 = z.k_i8 + h * Np * d
+    zh.v16 = z.v16 + h * Np * d * 2
+    zh.q_scale = z.q_scale + h * (Np // z.q_block) * 4
+    zh.k_scale = z.k_scale + h * (Np // z.k_block) * 4
+    zh.k_mean = z.k_mean + h * d * 4
+    zh.v_scale = z.v_scale + h * d * 4
+    return zh
+
+
+def test_prefill_at_the_maximum_length(sage, orc):
+    N, H, d = sage.SAGE_MAX_N, 16, 128
+    sm = 1 / math.sqrt(d)
+    _say(f"case maximum-length prefill B=1 H={H} N={N} d={d} causal=True")
+    q = _normal((1, H, N, d), 501, 1.5)
+    k = _normal((1, H, N, d), 502, 1.5)
+    v = _normal((1, H, N, d), 503, 1.0)
+    out = torch.empty((1, H, N, d), dtype=torch.float32, device="cuda")
+    ws = sage.workspace_for(q, k)
+    sage.sage_attn_fwd_ex(q, k, v, out, True, sm, sage.options("block", "e4m3", 8), ws)
+    torch.cuda.synchronize()
+    z = sage.sage_workspace_carve(ws, ws.numel(), 1, H, H, N, d)
+    Np = N  # 2^20 is a multiple of the padding
+    rng = np.random.Generator(np.random.PCG64(5))
+    for h in (0, H - 1):
+        _say(f"   head {h}")
+        qh, kh, vh = (t[:, h:h + 1].cpu() for t in (q, k, v))
+        oz = orc.quantize(qh, kh, vh, bq=128, bk=64, pv="e4m3")
+        quant = sage.read_quantized(_head_view(sage, z, h, Np, d), ws, 1, 1, 1, N, d)
+        np.testing.assert_array_equal(quant["q_i8"].numpy(), oz["q_i8"])
+        np.testing.assert_array_equal(quant["k_i8"].numpy(), oz["k_i8"])
+        np.testing.assert_array_equal(quant["v_fp8"].numpy(), oz["v_fp8"])
+        np.testing.assert_array_equal(quant["k_mean"].numpy(), oz["k_mean"])
+        np.testing.assert_array_equal(quant["v_scale"].numpy(), oz["v_scale"])
+        np.testing.assert_array_equal(quant["q_scale"].numpy(), oz["q_scale"])
+        np.testing.assert_array_equal(quant["k_scale"].numpy(), oz["k_scale"])
+        edges = [0, 1, 127, 128, 129, N // 2, N - 129, N - 128, N - 2, N - 1]
+        rows = np.unique(np.concatenate([edges, rng.choice(N, size=14, replace=False)])).astype(np.int64)
+        got = out[0, h][torch.from_numpy(rows).cuda()].cpu().numpy()
+        _check_attn(orc, got, oz, True, sm, rows)
+
+
+def test_decode_over_the_longest_cache(sage, orc):
+    B, Hq, Hkv, Nq, Nk, d = 1, 8, 1, 1, 1 << 20, 128
+    sm = 1 / math.sqrt(d)
+    _say(f"case longest-cache decode B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal=True")
+    q = _normal((B, Hq, Nq, d), 601, 1.5)
+    k = _normal((B, Hkv, Nk, d), 602, 1.5)
+    v = _normal((B, Hkv, Nk, d), 603, 1.0)
+    cache = sage.KVCache(k, v)
+    out = cache.attend(q, causal=True, sm_scale=sm)
+    torch.cuda.synchronize()
+    quant = sage.read_kv_cache(cache.z, cache.buf, B, Hkv, Nk, d)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    oz = orc.quantize_q(qc, bq=1)
+    oz.update(orc.quantize_kv(kc, vc, bk=64, pv="e4m3"))
+    np.testing.assert_array_equal(quant["k_i8"].numpy(), oz["k_i8"])
+    np.testing.assert_array_equal(quant["v_fp8"].numpy(), oz["v_fp8"])
+    np.testing.assert_array_equal(quant["v_scale"].numpy(), oz["v_scale"])
+    _check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, True, sm, None)
