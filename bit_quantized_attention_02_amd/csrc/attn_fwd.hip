@@ -5,6 +5,8 @@
 // key blocks with the per-block computation of attn_block.h (double-buffered
 // LDS tiles, INT8 Q.K^T, FP32 online softmax, E4M3 or binary16 P, two-level
 // P.V).
+#include <type_traits>
+
 #include "attn_block.h"
 
 namespace sage {
@@ -37,7 +39,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     uint16_t* const lv0 = reinterpret_cast<uint16_t*>(smem + 2 * SAGE_BN * D);
     uint16_t* const lv1 = lv0 + D * SAGE_BN;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // The wave index is uniform; held in a scalar register at d = 64, the
+    // tile copies' LDS addresses are formed without vector instructions.  (At
+    // d = 128 the scalar form makes the compiler spill registers in the
+    // causal loops.)
+    const int wave = D == 64 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
     const int h = lane >> 5, r32 = lane & 31;
     const v8h rsel = row_sum_selector(lane);
 
@@ -100,20 +107,48 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     // Blocks [0, nA) need no mask for any wave of the work-group: a loop of
     // its own keeps that body free of per-wave branches.
     const int nA = CAUSAL ? min(q0 / SAGE_BN, a.N / SAGE_BN) : a.N / SAGE_BN;
-    int T = 0;
-    for (; T < nA; ++T) {
-        const bool odd = T & 1;
+    // At d = 64 that loop goes two blocks at a time, so that each copy of
+    // the body reads and fills fixed buffers (their LDS offsets become
+    // immediates; at d = 128 the second copy would push registers into
+    // spills).
+    auto full_block = [&](int T, auto odd_c) {
+        constexpr bool ODD = decltype(odd_c)::value;
         const bool more = T + 1 < nblk;
         const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
-        if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
+        if (more) tiles.load(T + 1, ODD ? lk0 : lk1, ODD ? lv0 : lv1, wave);
         float c[KSPLIT];
 #pragma unroll
         for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-        attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N,
-                                                   c, a.l448, h, r32, rsel, mref, lsum, O);
+        attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(ODD ? lk1 : lk0, ODD ? lv1 : lv0, qf, T, row,
+                                                                 a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+    typedef std::integral_constant<bool, false> even_t;
+    typedef std::integral_constant<bool, true> odd_t;
+    int T = 0;
+    if constexpr (D == 64) {
+        for (; T + 1 < nA; T += 2) {
+            full_block(T, even_t());
+            full_block(T + 1, odd_t());
+        }
+        if (T < nA) full_block(T++, even_t());  // T is even here
+    } else {
+        for (; T < nA; ++T) {
+            const bool odd = T & 1;
+            const bool more = T + 1 < nblk;
+            const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
+            if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
+            float c[KSPLIT];
+#pragma unroll
+            for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
+            attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(
+                odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
+            kscale = knext;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
     }
     for (; T < nblk; ++T) {
         const bool odd = T & 1;
