@@ -98,16 +98,29 @@ constexpr int cache_vb() {
 // register file, so a CU runs at most one per SIMD, four in all; at d = 128 a
 // second buffer would leave LDS for only two of them.  With one buffer per
 // tile, the next block's K tile is copied once this block's K fragments are
-// read and its V tile once this block's products have read theirs.
+// read and its V tile once this block's products have read theirs.  (A second
+// V buffer at d = 128, with three work-groups per CU, measured slower.)
 template <int D>
-constexpr int decode_bufs() {
+constexpr int decode_kbufs() {
+    return D == 128 ? 1 : 2;
+}
+template <int D, bool PV16>
+constexpr int decode_vbufs() {
     return D == 128 ? 1 : 2;
 }
 constexpr int kDecodeWavesPerCU = 4;
 
 template <int D, bool PV16>
 constexpr size_t decode_lds() {
-    return (size_t)decode_bufs<D>() * (SAGE_BN * D + D * SAGE_BN * cache_vb<PV16>());
+    return (size_t)decode_kbufs<D>() * SAGE_BN * D +
+           (size_t)decode_vbufs<D, PV16>() * D * SAGE_BN * cache_vb<PV16>();
+}
+
+// Work-groups resident per CU: four (one per SIMD) where LDS allows; three
+// with binary16 V tiles (48 KB).  The key split sizes its grid to this.
+template <int D, bool PV16>
+constexpr int decode_wgs_per_cu() {
+    return 160 * 1024 / decode_lds<D, PV16>() < 4 ? (int)(160 * 1024 / decode_lds<D, PV16>()) : 4;
 }
 
 template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
@@ -115,12 +128,13 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     constexpr int CT = D / 32;
     constexpr int VB = cache_vb<PV16>();
     constexpr bool V8 = VB == 1;
-    constexpr int NBUF = decode_bufs<D>();
+    constexpr int NBUF = decode_kbufs<D>();
+    constexpr int NVB = decode_vbufs<D, PV16>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* const lk0 = smem;
     uint8_t* const lk1 = smem + (NBUF - 1) * SAGE_BN * D;
     uint8_t* const lv0 = smem + NBUF * SAGE_BN * D;
-    uint8_t* const lv1 = lv0 + (NBUF - 1) * D * SAGE_BN * VB;
+    uint8_t* const lv1 = lv0 + (NVB - 1) * D * SAGE_BN * VB;
 
     const int lane = threadIdx.x;
     const int h = lane >> 5, r32 = lane & 31;
@@ -383,8 +397,7 @@ SAGE_DECODE_INST_K(Bf16Tag, 128)
 template __global__ void decode_merge<64>(DecodeArgs);
 template __global__ void decode_merge<128>(DecodeArgs);
 
-// Chunking: about one round of work-groups, kDecodeWavesPerCU per CU (a
-// binary16 cache fits fewer at once and is split the same way), in chunks of
+// Chunking: about one round of work-groups, wgs_per_cu per CU, in chunks of
 // at least kMinChunkBlocks blocks so that filling each work-group's tile
 // pipeline stays a small part of its work.  One round beat two on both the
 // 32768-key single-sequence cache and the batch of eight 8192-key caches
@@ -393,14 +406,14 @@ template __global__ void decode_merge<128>(DecodeArgs);
 constexpr int kMinChunkBlocks = 2;
 static_assert(256 * kDecodeWavesPerCU <= kMergeThreads, "a row's chunks must fit one merge work-group");
 
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int wgs_per_cu) {
     DecodePlan pl;
     const int G = Hq / Hkv;
     pl.row_tiles = (G * Nq + 31) / 32;
     const int nkb = (Nk + SAGE_BN - 1) / SAGE_BN;
     const long long units = (long long)B * Hkv * pl.row_tiles;
     (void)d;
-    const long long target = 256LL * kDecodeWavesPerCU;
+    const long long target = 256LL * wgs_per_cu;
     long long want = target / units;
     if (want < 1) want = 1;
     int per = (int)((nkb + want - 1) / want);
@@ -449,7 +462,10 @@ static hipError_t launch_decode_d(const DecodeArgs& a, bool fine_k, int causal, 
 hipError_t launch_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out,
                          float* part_o, float* part_ml, int B, int Hq, int Hkv, int Nq, int Nk,
                          int d, int causal, float qk, float l448, hipStream_t st) {
-    const DecodePlan pl = decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    const bool pv16 = cache->pv_format == SAGE_PV_F16;
+    const int wpc = d == 64 ? (pv16 ? decode_wgs_per_cu<64, true>() : decode_wgs_per_cu<64, false>())
+                            : (pv16 ? decode_wgs_per_cu<128, true>() : decode_wgs_per_cu<128, false>());
+    const DecodePlan pl = decode_plan(B, Hq, Hkv, Nq, Nk, d, wpc);
     DecodeArgs a;
     a.q = (const uint16_t*)q;
     a.k_i8 = cache->k_i8;
@@ -473,7 +489,6 @@ hipError_t launch_decode(const void* q, int dtype, const sage_kv_cache* cache, f
     a.qk = qk;
     a.l448 = l448;
     const bool fine_k = cache->k_block == SAGE_BK_THREAD;
-    const bool pv16 = cache->pv_format == SAGE_PV_F16;
     if (dtype == SAGE_F16)
         return d == 64 ? launch_decode_d<_Float16, 64>(a, fine_k, causal, pv16, st)
                        : launch_decode_d<_Float16, 128>(a, fine_k, causal, pv16, st);

@@ -54,7 +54,9 @@ struct KVViews {
 struct DecodePlan {
     int row_tiles, nchunk, chunk_blocks;
 };
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+// wgs_per_cu: decode work-groups resident per CU (4 by default: the most any
+// configuration runs, which sizes the workspace for every format)
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int wgs_per_cu = 4);
 
 // Position of key j inside a block's V row.  The attention kernel's 32x32
 // Q.K^T tiles leave, in lane half h (lanes 32h..32h+31), the scores of keys
