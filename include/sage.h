@@ -284,7 +284,7 @@ int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float
                      int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
                      void* workspace, size_t ws_bytes, void* stream);
 
-/* Block sizes and format constants of this build. */
+/* Block sizes and format constants the library was compiled with. */
 int sage_get_config(sage_config* c);
 
 /* Position of key j (0 <= j < SAGE_BN) inside a block's row of v16; -1 if j
