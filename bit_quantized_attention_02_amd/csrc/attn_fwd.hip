@@ -14,6 +14,8 @@ namespace sage {
 static_assert(SAGE_BQ == 128 && SAGE_BQ_THREAD == 1 && SAGE_BK == 64 && SAGE_BK_THREAD == 32,
               "the launch maps the two granularities to q_shift 7/0 and 2/4 K scales per block");
 
+constexpr int kMaxTailSplit = 4;  // key shares of a split tail tile, at most
+
 struct AttnArgs {
     const int8_t* q_i8;
     const float* q_scale;
@@ -23,6 +25,14 @@ struct AttnArgs {
     const float* v_scale;
     float* out;
     int B, Hq, Hkv, N, Np, G, nqt;
+    // The last partial round's tiles, when split along the keys: tiles
+    // [tiles_main, B*Hq*nqt) each take tail_split work-groups, whose partial
+    // results (unnormalised O [.., D] in part_o, reference max and row sum in
+    // part_ml) attn_tail_merge combines.  tiles_main = B*Hq*nqt: no split.
+    int tiles_main, tail_split;
+    float* part_o;
+    float* part_ml;
+    long long tail_rows;  // rows part_o / part_ml hold (0: no split)
     int q_shift;  // log2 of the query rows per Q scale (7 or 0)
     float qk;    // f32(sm_scale * log2 e)
     float l448;  // f32(log2 448), or 0 for binary16 P
@@ -51,12 +61,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     // Work-group -> tile.  Work-groups are dispatched round-robin over the 8
     // XCDs; give each XCD a contiguous range of tiles (same heads, so K and V
     // stay in that XCD's L2).
-    const int total = a.B * a.Hq * a.nqt;
-    const int per_xcd = (total + 7) / 8;
-    const int tall = total % 8 == 0 ? 8 : total % 8;
-    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-    const int logical = xcd < tall ? xcd * per_xcd + local
-                                   : tall * per_xcd + (xcd - tall) * (per_xcd - 1) + local;
+    // A split tail tile's work-groups come after all the others.
+    const int main_tiles = a.tiles_main;
+    int logical, chunk = -1;
+    if ((int)blockIdx.x < main_tiles) {
+        const int per_xcd = (main_tiles + 7) / 8;
+        const int tall = main_tiles % 8 == 0 ? 8 : main_tiles % 8;
+        const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+        logical = xcd < tall ? xcd * per_xcd + local : tall * per_xcd + (xcd - tall) * (per_xcd - 1) + local;
+    } else {
+        const int j = blockIdx.x - main_tiles;
+        logical = main_tiles + j / a.tail_split;
+        chunk = j % a.tail_split;
+    }
     const int qt_l = logical % a.nqt;
     const int bh = logical / a.nqt;
     const int hq = bh % a.Hq, b = bh / a.Hq;
@@ -72,6 +89,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     // stops after wave_last
     const int n_full = CAUSAL ? min(rbase / SAGE_BN, a.N / SAGE_BN) : a.N / SAGE_BN;
     const int wave_last = CAUSAL ? min(nkb - 1, (rbase + 31) / SAGE_BN) : nkb - 1;
+
+    // key blocks [T0, T1): all of them, or a split tile's share (non-causal)
+    int T0 = 0, T1 = nblk;
+    if (chunk >= 0) {
+        T0 = (int)((long long)chunk * nblk / a.tail_split);
+        T1 = (int)((long long)(chunk + 1) * nblk / a.tail_split);
+    }
 
     const uint8_t* kbase = (const uint8_t*)a.k_i8 + (long long)bg * a.Np * D;
     const uint16_t* vbase = a.v16 + (long long)bg * a.Np * D;
@@ -98,9 +122,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     // tile copy is issued: vector-memory waits count in issue order, so a
     // scale load issued after the copy would make its wait cover the copy too.
     typedef float kvec __attribute__((ext_vector_type(KSPLIT)));
-    kvec kscale = *reinterpret_cast<const kvec*>(ksc);
+    kvec kscale = *reinterpret_cast<const kvec*>(ksc + KSPLIT * T0);
     const TileLoader<D, WAVES> tiles(kbase, vbase, a.Np, wave, lane);
-    tiles.load(0, lk0, lv0, wave);
+    tiles.load(T0, lk0, lv0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -111,9 +135,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     // the body reads and fills fixed buffers (their LDS offsets become
     // immediates; at d = 128 the second copy would push registers into
     // spills).
+    // (Buffers alternate with the block's place after T0.)
     auto full_block = [&](int T, auto odd_c) {
         constexpr bool ODD = decltype(odd_c)::value;
-        const bool more = T + 1 < nblk;
+        const bool more = T + 1 < T1;
         const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
         if (more) tiles.load(T + 1, ODD ? lk0 : lk1, ODD ? lv0 : lv1, wave);
         float c[KSPLIT];
@@ -127,17 +152,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     };
     typedef std::integral_constant<bool, false> even_t;
     typedef std::integral_constant<bool, true> odd_t;
-    int T = 0;
+    const int nA1 = min(nA, T1);
+    int T = T0;
     if constexpr (D == 64) {
-        for (; T + 1 < nA; T += 2) {
+        for (; T + 1 < nA1; T += 2) {
             full_block(T, even_t());
             full_block(T + 1, odd_t());
         }
-        if (T < nA) full_block(T++, even_t());  // T is even here
+        if (T < nA1) full_block(T++, even_t());  // T - T0 is even here
     } else {
-        for (; T < nA; ++T) {
-            const bool odd = T & 1;
-            const bool more = T + 1 < nblk;
+        for (; T < nA1; ++T) {
+            const bool odd = (T - T0) & 1;
+            const bool more = T + 1 < T1;
             const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
             if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
             float c[KSPLIT];
@@ -150,9 +176,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
             __syncthreads();
         }
     }
-    for (; T < nblk; ++T) {
-        const bool odd = T & 1;
-        const bool more = T + 1 < nblk;
+    for (; T < T1; ++T) {
+        const bool odd = (T - T0) & 1;
+        const bool more = T + 1 < T1;
         const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
         if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
         float c[KSPLIT];
@@ -173,6 +199,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 
     // ---- epilogue: out = O * s_V / l.  O[ct][v] is channel 32ct + 8(v/4) + 4h + v%4.
     if (row >= a.N) return;
+    if (chunk >= 0) {
+        // a split tile's share: unnormalised O, reference max, row sum
+        const long long p = ((long long)(logical - main_tiles) * ROWS + (row - q0)) * a.tail_split + chunk;
+        float* po = a.part_o + p * D;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch = 32 * ct + 8 * i + 4 * h;
+                const float4 o = {O[ct][4 * i + 0], O[ct][4 * i + 1], O[ct][4 * i + 2], O[ct][4 * i + 3]};
+                *reinterpret_cast<float4*>(po + ch) = o;
+            }
+        if (h == 0) *reinterpret_cast<float2*>(a.part_ml + p * 2) = make_float2(mref, lsum);
+        return;
+    }
     const float* sv = a.v_scale + (long long)bg * D;
     const float inv_l = 1.0f / lsum;
     float* op = a.out + ((long long)bh * a.N + row) * D;
@@ -212,6 +253,38 @@ constexpr int attn_waves_per_simd() {
 #endif
 }
 
+// Combines the key-split shares of the last partial round's tiles: per query
+// row, out = sum_c 2^(m_c - M) O_c * s_V / sum_c 2^(m_c - M) l_c with M the
+// largest reference max of the row's shares.  One thread per (row, channel).
+template <int D>
+__global__ __launch_bounds__(256) void attn_tail_merge(AttnArgs a, int rows_per_tile) {
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const int ch = (int)(gid % D);
+    const long long rr = gid / D;  // row among the split tiles' rows
+    const long long tail_rows = (long long)(a.B * a.Hq * a.nqt - a.tiles_main) * rows_per_tile;
+    if (rr >= tail_rows) return;
+    const int logical = a.tiles_main + (int)(rr / rows_per_tile);
+    const int row = (logical % a.nqt) * rows_per_tile + (int)(rr % rows_per_tile);
+    if (row >= a.N) return;
+    const int bh = logical / a.nqt;
+    const int hq = bh % a.Hq, b = bh / a.Hq;
+    const int bg = b * a.Hkv + hq / a.G;
+    const int S = a.tail_split;
+    const float* ml = a.part_ml + rr * S * 2;
+    const float* po = a.part_o + rr * S * D + ch;
+    float M = ml[0];
+    for (int c = 1; c < S; ++c) M = fmaxf(M, ml[2 * c]);
+    float l = 0.0f, o = 0.0f;
+    for (int c = 0; c < S; ++c) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+        l = __builtin_fmaf(ml[2 * c + 1], w, l);
+        o = __builtin_fmaf(po[(long long)c * D], w, o);
+    }
+    a.out[((long long)bh * a.N + row) * D + ch] = o * a.v_scale[(long long)bg * D + ch] * (1.0f / l);
+}
+template __global__ void attn_tail_merge<64>(AttnArgs, int);
+template __global__ void attn_tail_merge<128>(AttnArgs, int);
+
 // Explicit instantiations: with the packed-FP32 feature switched off on the
 // command line, this compiler otherwise leaves the host stubs of some of these
 // kernels undefined.
@@ -244,8 +317,43 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     const int total = a.B * a.Hq * a.nqt;
-    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>), dim3(total),
+    constexpr int ROWS = 32 * WAVES;
+    // The last partial round: when the tiles do not fill whole rounds of the
+    // work-groups the chip runs at once, the leftover tiles (non-causal, all
+    // equally long) are split along the keys over the otherwise idle slots.
+    a.tiles_main = total;
+    a.tail_split = 1;
+    if (!CAUSAL && a.part_o != nullptr) {
+        int dev = 0, cus = 0, per_cu = 0;
+        const bool known =
+            hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, (const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>, 64 * WAVES,
+                lds) == hipSuccess;
+        if (!known) (void)hipGetLastError();  // a failed query only means no split
+        if (known) {
+            const int slots = cus * per_cu;
+            const int nkb = (a.N + SAGE_BN - 1) / SAGE_BN;
+            const int tail = slots > 0 && total > slots ? total % slots : 0;
+            if (tail > 0) {
+                int split = min(kMaxTailSplit, min(slots / tail, nkb));
+                while (split > 1 && (long long)tail * split * ROWS > a.tail_rows) --split;
+                if (split > 1) {
+                    a.tiles_main = total - tail;
+                    a.tail_split = split;
+                }
+            }
+        }
+    }
+    const int grid = a.tiles_main + (total - a.tiles_main) * a.tail_split;
+    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>), dim3(grid),
                        dim3(64 * WAVES), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.tail_split == 1) return e;
+    const long long threads = (long long)(total - a.tiles_main) * ROWS * D;
+    hipLaunchKernelGGL((attn_tail_merge<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a,
+                       ROWS);
     return hipGetLastError();
 }
 
@@ -284,6 +392,11 @@ hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int 
     a.Np = s.Np;
     a.G = s.Hq / s.Hkv;
     a.nqt = 0;
+    a.tiles_main = 0;
+    a.tail_split = 1;
+    a.tail_rows = z->tail_part ? z->tail_rows : 0;
+    a.part_o = a.tail_rows > 0 ? z->tail_part : nullptr;
+    a.part_ml = a.tail_rows > 0 ? z->tail_part + a.tail_rows * s.d : nullptr;
     a.q_shift = z->q_block == SAGE_BQ ? 7 : 0;  // SAGE_BQ = 128, SAGE_BQ_THREAD = 1
     a.qk = qk;
     a.l448 = l448;

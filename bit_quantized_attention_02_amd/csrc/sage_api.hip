@@ -39,8 +39,18 @@ static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 // Workspace layout: each region starts on a 256-byte boundary.  A KV cache
 // (with_q false) has no Q regions, and v_bytes (1 or 2) per V element.
 struct Layout {
-    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v16, v_scale, v_inv, k_part, v_part, sync, total;
+    size_t q_i8, q_scale, k_i8, k_scale, k_mean, v16, v_scale, v_inv, k_part, v_part, sync, tail, total;
+    long long tail_rows;
 };
+
+// Rows of split-tile partial results the workspace holds: at d = 64, the
+// 128-row tiles of up to 1024 leftover tiles (any tail of a GPU with up to
+// 1024 resident work-groups), none when the shape has fewer tiles.
+static long long tail_capacity(const Shape& s) {
+    if (s.d != 64) return 0;
+    const long long tiles = (long long)s.B * s.Hq * (s.Np / 128);
+    return (tiles < 1024 ? tiles : 1024) * 128;
+}
 
 static Layout layout(const Shape& s, bool with_q = true, size_t v_bytes = sizeof(uint16_t)) {
     Layout L;
@@ -63,6 +73,8 @@ static Layout layout(const Shape& s, bool with_q = true, size_t v_bytes = sizeof
     L.k_part = take(Bkv * s.part_chunks() * s.d * sizeof(double));
     L.v_part = take(Bkv * s.part_chunks() * s.d * sizeof(float));
     L.sync = take((size_t)sage::prep_sync_words(s) * sizeof(int32_t));
+    L.tail_rows = with_q ? tail_capacity(s) : 0;
+    L.tail = L.tail_rows ? take((size_t)L.tail_rows * (s.d + 2) * sizeof(float)) : 0;
     L.total = off;
     return L;
 }
@@ -134,6 +146,7 @@ static int check_quant(const sage_qkv_quant* z) {
     if (!aligned(z->q_i8, 16) || !aligned(z->k_i8, 16) || !aligned(z->v16, 16) ||
         !aligned(z->v_scale, 16) || !aligned(z->k_part, 8))
         return SAGE_ERR_INVALID_ARG;
+    if (z->tail_rows < 0 || (z->tail_part && !aligned(z->tail_part, 16))) return SAGE_ERR_INVALID_ARG;
     return SAGE_OK;
 }
 
@@ -164,6 +177,8 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->k_part = (double*)(base + L.k_part);
     out->v_part = (float*)(base + L.v_part);
     out->sync = (int32_t*)(base + L.sync);
+    out->tail_part = L.tail_rows ? (float*)(base + L.tail) : nullptr;
+    out->tail_rows = L.tail_rows;
     out->q_block = SAGE_BQ;
     out->k_block = SAGE_BK;
     out->pv_format = SAGE_PV_E4M3;

@@ -129,6 +129,12 @@ typedef struct {
  *   k_part, v_part: per-chunk partial statistics used by sage_quantize.
  *   sync    int32 [B * Hkv]: per-kv-head arrival counters of the statistics
  *           kernel of sage_quantize, which clears them itself on every call.
+ *   tail_part f32 [tail_rows, d + 2]: partial results of the attention call's
+ *           last partial round.  When the non-causal tiles do not fill whole
+ *           rounds of the work-groups the GPU runs at once, the leftover
+ *           tiles are split along the keys and their shares merged; NULL (or
+ *           too few tail_rows for a split) runs them whole.  Same results up
+ *           to FP32 rounding.  Set by sage_workspace_carve (d = 64 only).
  */
 typedef struct {
     int8_t* q_i8;
@@ -147,6 +153,8 @@ typedef struct {
     int32_t pv_format; /* SAGE_PV_E4M3 (set by sage_workspace_carve) or SAGE_PV_F16; the
                           attention call must see the value the quantize call saw */
     int32_t qk_bits;   /* SAGE_QK_INT8 (set by sage_workspace_carve) or SAGE_QK_INT4; likewise */
+    float* tail_part;   /* may be NULL */
+    int64_t tail_rows;  /* rows of tail_part (0 with NULL) */
 } sage_qkv_quant;
 
 /* Method options of sage_attn_fwd_ex. */

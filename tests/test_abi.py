@@ -86,10 +86,16 @@ def test_carve_checks_alignment_and_size(sage):
     rc, z = _carve(sage, fake, need, shape)
     assert rc == 0
     ptrs = [getattr(z, f) for f, t in sage.sage_qkv_quant._fields_ if t is ctypes.c_void_p]
-    assert len(ptrs) == 11
+    assert len(ptrs) == 12
     assert all(p % 256 == 0 for p in ptrs) and len(set(ptrs)) == len(ptrs)
     assert (z.q_block, z.k_block, z.pv_format) == (128, 64, sage.SAGE_PV_E4M3)
     assert max(ptrs) < fake + need
+    # room for the split tail tiles' partials: 8 tiles of 128 rows, d + 2 floats a row
+    assert z.tail_rows == 8 * 128
+    assert z.tail_part + z.tail_rows * (64 + 2) * 4 <= fake + need
+    # none at d = 128
+    rc, z128 = _carve(sage, fake, sage.sage_workspace_bytes(1, 2, 2, 300, 128), (1, 2, 2, 300, 128))
+    assert rc == 0 and z128.tail_part is None and z128.tail_rows == 0
     assert _carve(sage, fake, need - 1, shape)[0] == sage.SAGE_ERR_WORKSPACE
     assert _carve(sage, fake + 16, need, shape)[0] == sage.SAGE_ERR_WORKSPACE
     assert _carve(sage, None, need, shape)[0] == sage.SAGE_ERR_WORKSPACE

@@ -211,6 +211,24 @@ def test_sage_attn_fwd_matches_two_step_path(sage, pv):
         assert torch.equal(one, out)
 
 
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
+def test_parity_split_tail(sage, orc, pv):
+    """520 tiles of 128 rows: on a GPU that runs 512 work-groups at once (256
+    CUs, two each) the 8 left over after the first round are split along the
+    keys into 4 shares each, then merged.  Every row of the last head's last
+    12 tiles is compared with the oracle, with a sample of the others."""
+    w = workloads.WORKLOADS[3].resized(B=1, Hq=4, Hkv=4, N=16500)
+    _say(f"case split tail shape={(w.B, w.Hq, w.Hkv, w.N, w.d)} pv={pv}")
+    q, k, v = workloads.generate(w, seed=77)
+    out, quant = run_gpu(sage, q, k, v, False, w.sm_scale, "block", pv)
+    oz = quantize_as(orc, q, k, v, "block", pv)
+    check_prep(orc, quant, oz)
+    last = 3 * w.N
+    tail = np.arange(last + (130 - 12) * 128, last + w.N, dtype=np.int64)
+    rows = np.unique(np.concatenate([workloads.sample_rows(w, 128, seed=3), tail]))
+    check_attn(orc, _rows_of(out, rows, w.d), oz, False, w.sm_scale, rows)
+
+
 @pytest.mark.parametrize("index,granularity,pv,qk_bits", [
     (1, "block", "e4m3", 8), (2, "block", "e4m3", 8), (3, "block", "e4m3", 8), (4, "block", "e4m3", 8),
     (5, "block", "e4m3", 8), (3, "thread", "e4m3", 8), (4, "thread", "e4m3", 8), (5, "thread", "e4m3", 8),
@@ -238,6 +256,13 @@ def test_parity_full_size_workloads(sage, orc, index, granularity, pv, qk_bits):
     oz = quantize_as(orc, q, k, v, granularity, pv, qk_bits)
     check_prep(orc, quant, oz)
     rows = workloads.sample_rows(w, 256, seed=11)
+    if not w.causal:
+        # rows of the last head's last 100 tiles: where the tiles left over
+        # after the last whole round of work-groups are split along the keys
+        last = (w.B * w.Hq - 1) * w.N
+        lo = max(0, w.N - 100 * 128)
+        pick = np.random.Generator(np.random.PCG64(12)).choice(w.N - lo, size=min(32, w.N - lo), replace=False)
+        rows = np.unique(np.concatenate([rows, last + lo + pick, [last + w.N - 1]])).astype(np.int64)
     if w.recipe == 4:
         # rows scaled x20 in the first head: the largest |Q| rows
         qn = q[0, 0].float().abs().amax(dim=-1)
