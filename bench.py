@@ -357,7 +357,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd", "ms_per_launch": round(ms_attn, 4)},
+                     "kernel": "attn_fwd (+ attn_tail_merge)", "ms_per_launch": round(ms_attn, 4)},
         "prep": {"ms_per_launch": round(ms_prep, 4), "alg_GBps": round(prep_gbs, 1),
                  "frac_hbm": round(prep_gbs / HBM_PEAK_GBS, 4)},
         "timed_wall_s": round(wall, 3),

@@ -14,7 +14,7 @@ namespace sage {
 static_assert(SAGE_BQ == 128 && SAGE_BQ_THREAD == 1 && SAGE_BK == 64 && SAGE_BK_THREAD == 32,
               "the launch maps the two granularities to q_shift 7/0 and 2/4 K scales per block");
 
-constexpr int kMaxTailSplit = 4;  // key shares of a split tail tile, at most
+constexpr int kMaxTailSplit = 8;  // key shares of a split tail tile, at most
 
 struct AttnArgs {
     const int8_t* q_i8;

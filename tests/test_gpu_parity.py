@@ -215,7 +215,7 @@ def test_sage_attn_fwd_matches_two_step_path(sage, pv):
 def test_parity_split_tail(sage, orc, pv):
     """520 tiles of 128 rows: on a GPU that runs 512 work-groups at once (256
     CUs, two each) the 8 left over after the first round are split along the
-    keys into 4 shares each, then merged.  Every row of the last head's last
+    keys into 8 shares each, then merged.  Every row of the last head's last
     12 tiles is compared with the oracle, with a sample of the others."""
     w = workloads.WORKLOADS[3].resized(B=1, Hq=4, Hkv=4, N=16500)
     _say(f"case split tail shape={(w.B, w.Hq, w.Hkv, w.N, w.d)} pv={pv}")
