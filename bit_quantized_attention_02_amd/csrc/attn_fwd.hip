@@ -68,7 +68,16 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         const int per_xcd = (main_tiles + 7) / 8;
         const int tall = main_tiles % 8 == 0 ? 8 : main_tiles % 8;
         const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-        logical = xcd < tall ? xcd * per_xcd + local : tall * per_xcd + (xcd - tall) * (per_xcd - 1) + local;
+        const int start = xcd < tall ? xcd * per_xcd : tall * per_xcd + (xcd - tall) * (per_xcd - 1);
+        const int count = xcd < tall ? per_xcd : per_xcd - 1;
+        logical = start + local;
+        // causal: when an XCD's range holds whole heads, go through it by
+        // tile length (each head's longest tile, then the next longest, ...)
+        // so that no long tile starts late
+        if (CAUSAL && start % a.nqt == 0 && count % a.nqt == 0) {
+            const int heads = count / a.nqt;
+            logical = start + (local % heads) * a.nqt + local / heads;
+        }
     } else {
         const int j = blockIdx.x - main_tiles;
         logical = main_tiles + j / a.tail_split;
