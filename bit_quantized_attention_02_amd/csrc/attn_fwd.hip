@@ -241,10 +241,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         }
 }
 
-// d = 64: 4-wave work-groups, two per CU (48 KB of LDS each), whose waves
-// interleave on each SIMD.  d = 128: one 8-wave work-group per CU (96 KB of
-// LDS), two waves per SIMD.  Either way a wave has half the register file,
-// all of it architectural registers.
+// d = 64: 4-wave work-groups (48 KB of LDS each) whose waves interleave on
+// each SIMD: three per CU (168 registers a wave) for the non-causal
+// per-block granularity, whose loop fits those registers without spilling;
+// two per CU (half the register file) otherwise.  d = 128: one 8-wave
+// work-group per CU (96 KB of LDS), two waves per SIMD.
 template <int D>
 constexpr int attn_waves() {
 #ifdef SAGE_ATTN_WAVES
@@ -253,12 +254,12 @@ constexpr int attn_waves() {
     return D == 64 ? 4 : 8;
 #endif
 }
-template <int D>
+template <int D, int KSPLIT, bool CAUSAL>
 constexpr int attn_waves_per_simd() {
 #ifdef SAGE_ATTN_WPS
     return SAGE_ATTN_WPS;
 #else
-    return 2;
+    return D == 64 && KSPLIT == 2 && !CAUSAL ? 3 : 2;
 #endif
 }
 
@@ -299,7 +300,7 @@ template __global__ void attn_tail_merge<128>(AttnArgs, int);
 // kernels undefined.
 #define SAGE_ATTN_INST(D, KSPLIT, CAUSAL, PV16, SEEDED)                                           \
     template __global__ void                                                                        \
-    attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, attn_waves<D>(), attn_waves_per_simd<D>()>(AttnArgs);
+    attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, attn_waves<D>(), attn_waves_per_simd<D, KSPLIT, CAUSAL>()>(AttnArgs);
 #define SAGE_ATTN_INST_PV(D, KSPLIT, CAUSAL)                                                       \
     SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false, true) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true, true)    \
     SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false, false) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true, false)
@@ -317,7 +318,7 @@ SAGE_ATTN_INST_PV(128, 4, true)
 template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool SEEDED>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WAVES = attn_waves<D>();
-    constexpr int WPS = attn_waves_per_simd<D>();
+    constexpr int WPS = attn_waves_per_simd<D, KSPLIT, CAUSAL>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
     if (lds > 65536) {
