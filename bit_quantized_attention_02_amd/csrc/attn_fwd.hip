@@ -347,11 +347,24 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
             const int nkb = (a.N + SAGE_BN - 1) / SAGE_BN;
             const int tail = slots > 0 && total > slots ? total % slots : 0;
             if (tail > 0) {
-                int split = min(kMaxTailSplit, min(slots / tail, nkb));
-                while (split > 1 && (long long)tail * split * ROWS > a.tail_rows) --split;
-                if (split > 1) {
+                // The leftover tiles as `split` shares each run in
+                // ceil(tail * split / slots) waves of 1/split of a tile's
+                // time: take the split with the shortest, if it beats the
+                // whole tiles' one wave, within the partials' room.
+                int best = 1;
+                long long best_num = 1, best_den = 1;  // time as a fraction of a tile's
+                for (int split = 2; split <= kMaxTailSplit && split <= nkb; ++split) {
+                    if ((long long)tail * split * ROWS > a.tail_rows) break;
+                    const long long waves = ((long long)tail * split + slots - 1) / slots;
+                    if (waves * best_den < best_num * split) {
+                        best = split;
+                        best_num = waves;
+                        best_den = split;
+                    }
+                }
+                if (best > 1) {
                     a.tiles_main = total - tail;
-                    a.tail_split = split;
+                    a.tail_split = best;
                 }
             }
         }

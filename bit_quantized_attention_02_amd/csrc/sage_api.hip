@@ -44,12 +44,12 @@ struct Layout {
 };
 
 // Rows of split-tile partial results the workspace holds: at d = 64, the
-// 128-row tiles of up to 1024 leftover tiles (any tail of a GPU with up to
-// 1024 resident work-groups), none when the shape has fewer tiles.
+// shares of up to 4096 tiles of 128 rows (a tail of several hundred tiles
+// split several ways), never more than the shape's own tiles hold.
 static long long tail_capacity(const Shape& s) {
     if (s.d != 64) return 0;
     const long long tiles = (long long)s.B * s.Hq * (s.Np / 128);
-    return (tiles < 1024 ? tiles : 1024) * 128;
+    return (tiles < 4096 ? tiles : 4096) * 128;
 }
 
 static Layout layout(const Shape& s, bool with_q = true, size_t v_bytes = sizeof(uint16_t)) {

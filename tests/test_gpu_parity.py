@@ -213,17 +213,18 @@ def test_sage_attn_fwd_matches_two_step_path(sage, pv):
 
 @pytest.mark.parametrize("pv", ["e4m3", "f16"])
 def test_parity_split_tail(sage, orc, pv):
-    """520 tiles of 128 rows: on a GPU that runs 512 work-groups at once (256
-    CUs, two each) the 8 left over after the first round are split along the
-    keys into 8 shares each, then merged.  Every row of the last head's last
-    12 tiles is compared with the oracle, with a sample of the others."""
-    w = workloads.WORKLOADS[3].resized(B=1, Hq=4, Hkv=4, N=16500)
+    """780 tiles of 128 rows: on a GPU that runs 768 work-groups of this
+    kernel at once (256 CUs, three each) the 12 left over after the first
+    round are split along the keys into 8 shares each, then merged.  Every
+    row of the last head's last 12 tiles is compared with the oracle, with a
+    sample of the others."""
+    w = workloads.WORKLOADS[3].resized(B=1, Hq=6, Hkv=6, N=16500)
     _say(f"case split tail shape={(w.B, w.Hq, w.Hkv, w.N, w.d)} pv={pv}")
     q, k, v = workloads.generate(w, seed=77)
     out, quant = run_gpu(sage, q, k, v, False, w.sm_scale, "block", pv)
     oz = quantize_as(orc, q, k, v, "block", pv)
     check_prep(orc, quant, oz)
-    last = 3 * w.N
+    last = (w.Hq - 1) * w.N
     tail = np.arange(last + (130 - 12) * 128, last + w.N, dtype=np.int64)
     rows = np.unique(np.concatenate([workloads.sample_rows(w, 128, seed=3), tail]))
     check_attn(orc, _rows_of(out, rows, w.d), oz, False, w.sm_scale, rows)
