@@ -265,12 +265,14 @@ constexpr int attn_waves_per_simd() {
 
 // Combines the key-split shares of the last partial round's tiles: per query
 // row, out = sum_c 2^(m_c - M) O_c * s_V / sum_c 2^(m_c - M) l_c with M the
-// largest reference max of the row's shares.  One thread per (row, channel).
+// largest reference max of the row's shares.  One thread per (row, four
+// channels): 16-byte loads of each share's partial output.
 template <int D>
 __global__ __launch_bounds__(256) void attn_tail_merge(AttnArgs a, int rows_per_tile) {
+    constexpr int C4 = D / 4;
     const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const int ch = (int)(gid % D);
-    const long long rr = gid / D;  // row among the split tiles' rows
+    const int ch = 4 * (int)(gid % C4);
+    const long long rr = gid / C4;  // row among the split tiles' rows
     const long long tail_rows = (long long)(a.B * a.Hq * a.nqt - a.tiles_main) * rows_per_tile;
     if (rr >= tail_rows) return;
     const int logical = a.tiles_main + (int)(rr / rows_per_tile);
@@ -284,13 +286,25 @@ __global__ __launch_bounds__(256) void attn_tail_merge(AttnArgs a, int rows_per_
     const float* po = a.part_o + rr * S * D + ch;
     float M = ml[0];
     for (int c = 1; c < S; ++c) M = fmaxf(M, ml[2 * c]);
-    float l = 0.0f, o = 0.0f;
+    float l = 0.0f;
+    float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int c = 0; c < S; ++c) {
         const float w = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+        const float4 x = *reinterpret_cast<const float4*>(po + (long long)c * D);
         l = __builtin_fmaf(ml[2 * c + 1], w, l);
-        o = __builtin_fmaf(po[(long long)c * D], w, o);
+        o.x = __builtin_fmaf(x.x, w, o.x);
+        o.y = __builtin_fmaf(x.y, w, o.y);
+        o.z = __builtin_fmaf(x.z, w, o.z);
+        o.w = __builtin_fmaf(x.w, w, o.w);
     }
-    a.out[((long long)bh * a.N + row) * D + ch] = o * a.v_scale[(long long)bg * D + ch] * (1.0f / l);
+    const float4 sv = *reinterpret_cast<const float4*>(a.v_scale + (long long)bg * D + ch);
+    const float inv_l = 1.0f / l;
+    float4 r;
+    r.x = o.x * sv.x * inv_l;
+    r.y = o.y * sv.y * inv_l;
+    r.z = o.z * sv.z * inv_l;
+    r.w = o.w * sv.w * inv_l;
+    *reinterpret_cast<float4*>(a.out + ((long long)bh * a.N + row) * D + ch) = r;
 }
 template __global__ void attn_tail_merge<64>(AttnArgs, int);
 template __global__ void attn_tail_merge<128>(AttnArgs, int);
@@ -374,7 +388,7 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
                        dim3(64 * WAVES), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.tail_split == 1) return e;
-    const long long threads = (long long)(total - a.tiles_main) * ROWS * D;
+    const long long threads = (long long)(total - a.tiles_main) * ROWS * (D / 4);
     hipLaunchKernelGGL((attn_tail_merge<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a,
                        ROWS);
     return hipGetLastError();
