@@ -182,9 +182,10 @@ int sage_workspace_carve(void* workspace, size_t ws_bytes, int B, int Hq, int Hk
 /*
  * The prep step (K mean, smoothing, per-block INT8 of Q and K, per-channel
  * FP8 of V, or V's binary16 rounding with SAGE_PV_F16) from fp16/bf16 Q, K, V
- * into the views of `dst`.  Memory-bound; runs
- * as three kernels on `stream`: Q codes; K/V statistics, whose last
- * work-group per kv head forms the K mean and V scales; K/V codes.
+ * into the views of `dst`.  Memory-bound; runs as three kernels on
+ * `stream`: clearing of the arrival counters; the K/V statistics (whose last
+ * work-group per kv head forms the K mean and V scales) together with the Q
+ * codes; the K/V codes.
  */
 int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
                   int N, int d, const sage_qkv_quant* dst, void* stream);
