@@ -302,16 +302,19 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
     if (h == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(mref, lsum);
 }
 
-// One work-group per query row: out = O * s_V / l over the row's chunks, each
-// weighted by 2^(its reference max - the largest).  Every thread issues its
-// loads first (the max and row sum of chunk t, and the partial O of channel
-// t % D for chunks t / D, t / D + GROUPS, ...), so the merge waits on one
-// round trip to memory; the largest max, the weighted row sum and the sum
-// over chunk groups then take wave shuffles and one LDS exchange each.  The
-// key split never makes more than kMergeThreads chunks.
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeWaves = kMergeThreads / 64;
-constexpr int kMergeLoads = 16;  // partial-O loads per thread issued together
+// One work-group per (query row, 32 channels): out = O * s_V / l over the
+// row's chunks, each weighted by 2^(its reference max - the largest).  Every
+// thread issues its loads first (the max and row sum of chunks t, t + 256,
+// ..., the partial O of its channel for chunks in its group, and the channel's
+// V scale), so the merge waits on one round trip to memory; the largest max,
+// the weighted row sum and the sum over chunk groups then take wave shuffles
+// and one LDS exchange each.  Slicing the channels gives D / 32 work-groups
+// per row, each with that fraction of the loads.  The key split never makes
+// more than kMaxChunks chunks.
+constexpr int kMaxChunks = 1024;     // the most chunks a row may have
+constexpr int kMergeSlice = 32;      // channels per merge work-group
+constexpr int kMergeT = 256;         // threads per merge work-group
+constexpr int kMergeLoads = 16;      // partial-O loads per thread issued together
 
 __device__ inline float wave_sum(float x) {
 #pragma unroll
@@ -320,12 +323,14 @@ __device__ inline float wave_sum(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a) {
-    constexpr int GROUPS = kMergeThreads / D;  // chunk groups summed in parallel
-    __shared__ float wgt[kMergeThreads];
-    __shared__ float osum[kMergeThreads];
-    __shared__ float wmax[kMergeWaves], wl[kMergeWaves];
-    const int row32 = blockIdx.x;  // (b * Hq + hq) * Nq + i
+__global__ __launch_bounds__(kMergeT) void decode_merge(DecodeArgs a) {
+    constexpr int GROUPS = kMergeT / kMergeSlice;
+    constexpr int NS = D / kMergeSlice;
+    constexpr int MLU = kMaxChunks / kMergeT;
+    __shared__ float wgt[kMaxChunks];
+    __shared__ float osum[kMergeT];
+    __shared__ float wmax[kMergeT / 64], wl[kMergeT / 64];
+    const int row32 = blockIdx.x / NS, slice = blockIdx.x % NS;
     const long long row = row32;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int nchunk = a.nchunk;
@@ -334,33 +339,44 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a) {
     const int bg = b * a.Hkv + hq / a.G;
     const float* ml = a.part_ml + row * nchunk * 2;
     const float* po = a.part_o + row * nchunk * D;
-    const int c = t % D, grp = t / D;
+    const int c = slice * kMergeSlice + (t % kMergeSlice), grp = t / kMergeSlice;
+    const float vs = grp == 0 ? a.v_scale[(long long)bg * D + c] : 0.0f;
 
-    // an empty chunk, and a thread past the last chunk, have max -inf, sum 0
-    const float2 mlt = t < nchunk ? *reinterpret_cast<const float2*>(ml + 2 * t)
-                                  : make_float2(-INFINITY, 0.0f);
+    float2 mlt[MLU];
+#pragma unroll
+    for (int u = 0; u < MLU; ++u) {
+        const int k = t + u * kMergeT;
+        mlt[u] = k < nchunk ? *reinterpret_cast<const float2*>(ml + 2 * k) : make_float2(-INFINITY, 0.0f);
+    }
     float x[kMergeLoads];
 #pragma unroll
     for (int u = 0; u < kMergeLoads; ++u) {
         const int k = grp + u * GROUPS;
         x[u] = k < nchunk ? po[(long long)k * D + c] : 0.0f;
     }
-
-    const float mw = wave_max(mlt.x);
+    float m = mlt[0].x;
+#pragma unroll
+    for (int u = 1; u < MLU; ++u) m = fmaxf(m, mlt[u].x);
+    const float mw = wave_max(m);
     if (lane == 0) wmax[wave] = mw;
     __syncthreads();
     float M = wmax[0];
 #pragma unroll
-    for (int i = 1; i < kMergeWaves; ++i) M = fmaxf(M, wmax[i]);
-
-    const float w = t < nchunk ? __builtin_amdgcn_exp2f(mlt.x - M) : 0.0f;
-    wgt[t] = w;
-    const float lw = wave_sum(mlt.y * w);
+    for (int i = 1; i < kMergeT / 64; ++i) M = fmaxf(M, wmax[i]);
+    float lt = 0.0f;
+#pragma unroll
+    for (int u = 0; u < MLU; ++u) {
+        const int k = t + u * kMergeT;
+        const float w = k < nchunk ? __builtin_amdgcn_exp2f(mlt[u].x - M) : 0.0f;
+        wgt[k] = w;
+        lt = __builtin_fmaf(mlt[u].y, w, lt);
+    }
+    const float lw = wave_sum(lt);
     if (lane == 0) wl[wave] = lw;
     __syncthreads();
     float l = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMergeWaves; ++i) l += wl[i];
+    for (int i = 0; i < kMergeT / 64; ++i) l += wl[i];
 
     float o = 0.0f;
 #pragma unroll
@@ -374,8 +390,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a) {
     __syncthreads();
     if (grp == 0) {
 #pragma unroll
-        for (int g2 = 1; g2 < GROUPS; ++g2) o += osum[g2 * D + c];
-        a.out[row * D + c] = o * a.v_scale[(long long)bg * D + c] * (1.0f / l);
+        for (int g2 = 1; g2 < GROUPS; ++g2) o += osum[g2 * kMergeSlice + (t % kMergeSlice)];
+        a.out[row * D + c] = o * vs * (1.0f / l);
     }
 }
 
@@ -404,7 +420,7 @@ template __global__ void decode_merge<128>(DecodeArgs);
 // (fewer partials to merge, no second-round tail).  The chunk count rounds
 // down so that the grid does not spill a short second round.
 constexpr int kMinChunkBlocks = 2;
-static_assert(256 * kDecodeWavesPerCU <= kMergeThreads, "a row's chunks must fit one merge work-group");
+static_assert(256 * kDecodeWavesPerCU <= kMaxChunks, "a row's chunks must fit the merge's weight table");
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int wgs_per_cu) {
     DecodePlan pl;
@@ -427,7 +443,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int wgs_pe
 template <typename In, int D, int KSPLIT, bool CAUSAL, bool PV16>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     constexpr size_t lds = decode_lds<D, PV16>();
-    if (a.nchunk > kMergeThreads) return hipErrorInvalidValue;  // not reached: see decode_plan
+    if (a.nchunk > kMaxChunks) return hipErrorInvalidValue;  // not reached: see decode_plan
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)attn_decode<In, D, KSPLIT, CAUSAL, PV16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -438,8 +454,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
                        st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nchunk == 1) return e;
-    hipLaunchKernelGGL((decode_merge<D>), dim3((unsigned)((long long)a.B * a.Hq * a.Nq)),
-                       dim3(kMergeThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_merge<D>), dim3((unsigned)((long long)a.B * a.Hq * a.Nq * (D / kMergeSlice))),
+                       dim3(kMergeT), 0, st, a);
     return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@ against the CPU oracle on the heads and rows it can afford.
   operands are compared bit for bit, and rows across them (first, last,
   tile and block edges, a seeded sample) against the oracle.
 - Decode over a 2^20-key cache with one kv head: the key split then makes
-  1024 chunks, the most the merge work-group takes.
+  1024 chunks, the most the merge takes.
 
 Inputs are seeded normal values drawn on the device (drawing 2^31 values on
 the host would take minutes); each head the oracle sees is copied from them.
