@@ -125,6 +125,39 @@ def _shape(q: torch.Tensor, k: torch.Tensor):
     return B, Hq, k.shape[1], N, d
 
 
+# The C calls take every size from the integers they are passed and read or
+# write each buffer by those sizes; the checks below keep a tensor of another
+# shape, element type or device from being read or written out of bounds.
+
+def _check_device(ref: torch.Tensor, *ts) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != ref.device or not t.is_contiguous():
+            raise ValueError(f"tensors must be contiguous and on {ref.device}")
+
+
+def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out=None) -> None:
+    """Q [B, Hq, N, d], K and V [B, Hkv, N, d] of one dtype, out FP32 of Q's
+    shape, all contiguous on one GPU."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("Q, K, V must be 4-D [B, H, N, d]")
+    if k.shape != v.shape or (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]):
+        raise ValueError(f"K and V must be [B, Hkv, N, d] for Q of shape {tuple(q.shape)}; "
+                         f"got {tuple(k.shape)} and {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"Q, K, V must share one dtype; got {q.dtype}, {k.dtype}, {v.dtype}")
+    if out is not None and (out.shape != q.shape or out.dtype != torch.float32):
+        raise ValueError(f"out must be float32 of shape {tuple(q.shape)}")
+    _check_device(q, k, v, out)
+
+
+def _check_out(ref: torch.Tensor, out: torch.Tensor, shape) -> None:
+    if tuple(out.shape) != tuple(shape) or out.dtype != torch.float32:
+        raise ValueError(f"out must be float32 of shape {tuple(shape)}")
+    _check_device(ref, out)
+
+
 # ------------------------------------------------------------------ C names
 
 def sage_status_string(status: int) -> str:
@@ -161,6 +194,7 @@ def sage_workspace_carve(workspace: torch.Tensor | int | None, ws_bytes: int, B:
 
 def sage_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dst: sage_qkv_quant,
                   stream=None) -> None:
+    _check_qkv(q, k, v)
     B, Hq, Hkv, N, d = _shape(q, k)
     _check(_lib.sage_quantize(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, N, d,
                               ctypes.byref(dst), _stream(stream)))
@@ -168,12 +202,15 @@ def sage_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dst: sage_q
 
 def sage_attn_fwd_quantized(src: sage_qkv_quant, out: torch.Tensor, B: int, Hq: int, Hkv: int,
                             N: int, d: int, causal: bool, sm_scale: float, stream=None) -> None:
+    _check_out(out, out, (B, Hq, N, d))
     _check(_lib.sage_attn_fwd_quantized(ctypes.byref(src), _ptr(out), B, Hq, Hkv, N, d,
                                         int(causal), float(sm_scale), _stream(stream)))
 
 
 def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                   causal: bool, sm_scale: float, workspace: torch.Tensor, stream=None) -> None:
+    _check_qkv(q, k, v, out)
+    _check_device(q, workspace)
     B, Hq, Hkv, N, d = _shape(q, k)
     _check(_lib.sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, int(causal),
                               float(sm_scale), _dtype_code(q), _ptr(workspace),
@@ -183,6 +220,8 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
 def sage_attn_fwd_granular(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                            causal: bool, sm_scale: float, q_block: int, k_block: int,
                            workspace: torch.Tensor, stream=None) -> None:
+    _check_qkv(q, k, v, out)
+    _check_device(q, workspace)
     B, Hq, Hkv, N, d = _shape(q, k)
     _check(_lib.sage_attn_fwd_granular(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d,
                                        int(causal), float(sm_scale), _dtype_code(q), int(q_block),
@@ -193,6 +232,8 @@ def sage_attn_fwd_granular(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ou
 def sage_attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                      causal: bool, sm_scale: float, opts: sage_options, workspace: torch.Tensor,
                      stream=None) -> None:
+    _check_qkv(q, k, v, out)
+    _check_device(q, workspace)
     B, Hq, Hkv, N, d = _shape(q, k)
     _check(_lib.sage_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, int(causal),
                                  float(sm_scale), _dtype_code(q), ctypes.byref(opts), _ptr(workspace),
@@ -215,6 +256,9 @@ def sage_kv_cache_carve(buf: torch.Tensor | int | None, nbytes: int, B: int, Hkv
 
 
 def sage_kv_quantize(k: torch.Tensor, v: torch.Tensor, cache: sage_kv_cache, stream=None) -> None:
+    if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("K and V must be [B, Hkv, Nk, d] of one shape and dtype")
+    _check_device(k, k, v)
     B, Hkv, Nk, d = k.shape
     _check(_lib.sage_kv_quantize(_ptr(k), _ptr(v), _dtype_code(k), B, Hkv, Nk, d, ctypes.byref(cache),
                                  _stream(stream)))
@@ -226,6 +270,10 @@ def sage_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: 
 
 def sage_attn_decode(q: torch.Tensor, cache: sage_kv_cache, out: torch.Tensor, Hkv: int, Nk: int,
                      causal: bool, sm_scale: float, workspace: torch.Tensor, stream=None) -> None:
+    if q.dim() != 4:
+        raise ValueError("Q must be 4-D [B, Hq, Nq, d]")
+    _check_out(q, out, q.shape)
+    _check_device(q, q, workspace)
     B, Hq, Nq, d = q.shape
     _check(_lib.sage_attn_decode(_ptr(q), _dtype_code(q), ctypes.byref(cache), _ptr(out), B, Hq, Hkv,
                                  Nq, Nk, d, int(causal), float(sm_scale), _ptr(workspace),
@@ -260,9 +308,7 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     (INT8 Q, K) or 4 (INT4 values)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("Q, K, V must be contiguous device tensors")
+    _check_qkv(q, k, v)
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = workspace_for(q, k)
@@ -276,9 +322,9 @@ class KVCache:
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, granularity: str = "block",
                  pv: str = "e4m3", stream=None):
-        for t in (k, v):
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("K, V must be contiguous device tensors")
+        if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
+            raise ValueError("K and V must be [B, Hkv, Nk, d] of one shape and dtype")
+        _check_device(k, k, v)
         self.B, self.Hkv, self.Nk, self.d = k.shape
         nbytes = sage_kv_cache_bytes(self.B, self.Hkv, self.Nk, self.d, pv)
         if nbytes == 0:
@@ -294,8 +340,9 @@ class KVCache:
         Nk positions -> FP32 [B, Hq, Nq, d]."""
         if sm_scale is None:
             sm_scale = 1.0 / math.sqrt(q.shape[-1])
-        if not q.is_cuda or not q.is_contiguous():
-            raise ValueError("Q must be a contiguous device tensor")
+        if q.dim() != 4 or q.shape[0] != self.B or q.shape[3] != self.d:
+            raise ValueError(f"Q must be [{self.B}, Hq, Nq, {self.d}] for this cache")
+        _check_device(self.buf, q)
         B, Hq, Nq, d = q.shape
         if workspace is None:
             nbytes = sage_decode_workspace_bytes(B, Hq, self.Hkv, Nq, self.Nk, d)

@@ -310,3 +310,52 @@ def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
     bad2 = sage.sage_kv_cache.from_buffer_copy(z)
     bad2.pv_format = 5
     assert dec(c=ctypes.byref(bad2)) == sage.SAGE_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_tensors_the_sizes_do_not_describe(sage):
+    """The C calls take B, Hq, Hkv, N, d from Q and K alone; the binding
+    refuses a V, output, cache query or workspace that those sizes do not
+    describe (the checks run before any device call, so CPU tensors do)."""
+    import torch
+    f16 = torch.float16
+    q = torch.zeros(1, 4, 256, 64, dtype=f16)
+    k = torch.zeros(1, 2, 256, 64, dtype=f16)
+    opts = sage.options()
+    bad_v = [torch.zeros(1, 2, 128, 64, dtype=f16),   # shorter than K
+             torch.zeros(1, 1, 256, 64, dtype=f16),   # fewer heads than K
+             torch.zeros(2, 2, 256, 64, dtype=f16)]   # larger batch
+    for v in bad_v:
+        with pytest.raises(ValueError):
+            sage.attn(q, k, v)
+        with pytest.raises(ValueError):
+            sage.sage_quantize(q, k, v, sage.sage_qkv_quant())
+    with pytest.raises(ValueError):  # K of another length than Q
+        sage.attn(q, torch.zeros(1, 2, 255, 64, dtype=f16), torch.zeros(1, 2, 255, 64, dtype=f16))
+    with pytest.raises(ValueError):  # K of another head dimension
+        sage.attn(q, torch.zeros(1, 2, 256, 128, dtype=f16), torch.zeros(1, 2, 256, 128, dtype=f16))
+    with pytest.raises(ValueError):  # 3-D input
+        sage.attn(q[0], k[0], k[0])
+    with pytest.raises(TypeError):   # mixed dtypes
+        sage.attn(q, k, k.to(torch.bfloat16))
+    v = torch.zeros_like(k)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    for out in (torch.zeros(1, 4, 256, 64, dtype=f16),          # not FP32
+                torch.zeros(1, 4, 128, 64, dtype=torch.float32)):  # too short
+        with pytest.raises(ValueError):
+            sage.sage_attn_fwd(q, k, v, out, False, 0.125, ws)
+        with pytest.raises(ValueError):
+            sage.sage_attn_fwd_ex(q, k, v, out, False, 0.125, opts, ws)
+        with pytest.raises(ValueError):
+            sage.sage_attn_fwd_quantized(sage.sage_qkv_quant(), out, 1, 4, 2, 256, 64, False, 0.125)
+    # shapes that agree still need device tensors
+    with pytest.raises(ValueError):
+        sage.attn(q, k, v)
+    with pytest.raises(ValueError):
+        sage.sage_attn_fwd(q, k, v, torch.zeros(1, 4, 256, 64), False, 0.125, ws)
+    with pytest.raises(ValueError):  # K and V of different lengths for a cache
+        sage.KVCache(k, torch.zeros(1, 2, 128, 64, dtype=f16))
+    with pytest.raises(ValueError):
+        sage.sage_kv_quantize(k, torch.zeros(1, 2, 256, 64, dtype=torch.bfloat16), sage.sage_kv_cache())
+    with pytest.raises(ValueError):  # decode output of another shape than Q
+        sage.sage_attn_decode(torch.zeros(1, 4, 1, 64, dtype=f16), sage.sage_kv_cache(),
+                              torch.zeros(1, 4, 2, 64), 2, 256, True, 0.125, ws)
