@@ -4,8 +4,8 @@
 // scales; V as E4M3 code bytes, or binary16 for the binary16 P.V), quantized
 // once.  E4M3 V tiles stay one byte per value in LDS and are converted to
 // binary16 (exactly) as each P.V fragment is read, so a block moves 2 bytes
-// per K+V element pair from HBM and LDS holds two work-groups per CU even at
-// d = 128.  A short
+// per K+V element pair from HBM and LDS holds a work-group for each of the
+// CU's four SIMDs (three with binary16 V).  A short
 // query -- Nq rows per q head, sitting at the last Nq of the Nk positions --
 // attends to it with the same per-block computation as the prefill kernel
 // (attn_block.h).  The query rows are quantized here, one INT8 scale per row.
