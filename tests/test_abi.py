@@ -359,3 +359,9 @@ def test_binding_rejects_tensors_the_sizes_do_not_describe(sage):
     with pytest.raises(ValueError):  # decode output of another shape than Q
         sage.sage_attn_decode(torch.zeros(1, 4, 1, 64, dtype=f16), sage.sage_kv_cache(),
                               torch.zeros(1, 4, 2, 64), 2, 256, True, 0.125, ws)
+    # a query whose batch or head dimension is not the cache's
+    cache = sage.KVCache.__new__(sage.KVCache)
+    cache.B, cache.Hkv, cache.Nk, cache.d, cache.buf = 1, 2, 256, 64, torch.zeros(16, dtype=torch.uint8)
+    for qq in (torch.zeros(2, 4, 1, 64, dtype=f16), torch.zeros(1, 4, 1, 128, dtype=f16)):
+        with pytest.raises(ValueError):
+            cache.attend(qq)
