@@ -182,7 +182,7 @@ int sage_workspace_carve(void* workspace, size_t ws_bytes, int B, int Hq, int Hk
 /*
  * The prep step (K mean, smoothing, per-block INT8 of Q and K, per-channel
  * FP8 of V, or V's binary16 rounding with SAGE_PV_F16) from fp16/bf16 Q, K, V
- * into the views of `dst`.  Memory-bound; runs as three kernels on
+ * into the views of `dst` (carved for these sizes).  Memory-bound; runs as three kernels on
  * `stream`: clearing of the arrival counters; the K/V statistics (whose last
  * work-group per kv head forms the K mean and V scales) together with the Q
  * codes; the K/V codes.
@@ -194,6 +194,9 @@ int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B,
  * Attention on already-quantized operands: out = softmax(Q K^T sm_scale) V as
  * the method computes it, FP32 output [B, Hq, N, d].  causal = 1 applies the
  * square, top-left aligned mask j <= i.  sm_scale must be finite and > 0.
+ * `src` must have been carved for these B, Hq, Hkv, N, d and filled by
+ * sage_quantize: its buffers are read by these sizes, which the struct does
+ * not record.
  */
 int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq, int Hkv, int N,
                             int d, int causal, float sm_scale, void* stream);
@@ -267,8 +270,9 @@ int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, 
                         int pv_format, sage_kv_cache* cache);
 
 /* The K/V half of sage_quantize: K mean, smoothing, INT8 K, V codes, from
- * fp16/bf16 K, V [B, Hkv, Nk, d] into `cache`.  Runs as three kernels on
- * `stream` (counter clearing, statistics, codes). */
+ * fp16/bf16 K, V [B, Hkv, Nk, d] into `cache`, which must have been carved
+ * for these sizes.  Runs as three kernels on `stream` (counter clearing,
+ * statistics, codes). */
 int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
                      const sage_kv_cache* cache, void* stream);
 
@@ -287,7 +291,8 @@ size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d
  * key range is split into chunks whose partial results (reference max, row
  * sum, unnormalised output; a third FP32 accumulation level) are merged by a
  * second kernel in `workspace` (device memory, 256-byte aligned) when there is
- * more than one chunk.
+ * more than one chunk.  `cache` must have been carved and quantized for these
+ * B, Hkv, Nk, d: it is read by these sizes, which the struct does not record.
  */
 int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
                      int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
