@@ -6,7 +6,10 @@
 
 Each .hip source is compiled to an object with hipcc, then linked into one
 shared library next to this file.  Packed FP32 instructions are disabled
-(-packed-fp32-ops): the kernels are written for scalar FP32 VALU.
+(-packed-fp32-ops): the kernels are written for scalar FP32 VALU.  The decode
+source also has its kernels' scalar arguments preloaded into SGPRs, so the
+short decode_merge computes its addresses without first waiting on a load of
+its arguments.
 """
 from __future__ import annotations
 
@@ -24,11 +27,13 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
+# per-source extra flags
+EXTRA = {"attn_decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -310,7 +310,8 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
 // the weighted row sum and the sum over chunk groups then take wave shuffles
 // and one LDS exchange each.  Slicing the channels gives D / 32 work-groups
 // per row, each with that fraction of the loads.  The key split never makes
-// more than kMaxChunks chunks.
+// more than kMaxChunks chunks.  The arguments are plain scalars (not the
+// DecodeArgs struct) so that the compiler can preload them into SGPRs.
 constexpr int kMaxChunks = 1024;     // the most chunks a row may have
 constexpr int kMergeSlice = 32;      // channels per merge work-group
 constexpr int kMergeT = 256;         // threads per merge work-group
@@ -323,7 +324,11 @@ __device__ inline float wave_sum(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kMergeT) void decode_merge(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeT) void decode_merge(const float* __restrict__ part_ml,
+                                                         const float* __restrict__ part_o,
+                                                         const float* __restrict__ v_scale,
+                                                         float* __restrict__ out, int nchunk_,
+                                                         int Nq, int Hq, int G, int Hkv) {
     constexpr int GROUPS = kMergeT / kMergeSlice;
     constexpr int NS = D / kMergeSlice;
     constexpr int MLU = kMaxChunks / kMergeT;
@@ -333,14 +338,14 @@ __global__ __launch_bounds__(kMergeT) void decode_merge(DecodeArgs a) {
     const int row32 = blockIdx.x / NS, slice = blockIdx.x % NS;
     const long long row = row32;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int nchunk = a.nchunk;
-    const int bh = row32 / a.Nq;
-    const int hq = bh % a.Hq, b = bh / a.Hq;
-    const int bg = b * a.Hkv + hq / a.G;
-    const float* ml = a.part_ml + row * nchunk * 2;
-    const float* po = a.part_o + row * nchunk * D;
+    const int nchunk = nchunk_;
+    const int bh = row32 / Nq;
+    const int hq = bh % Hq, b = bh / Hq;
+    const int bg = b * Hkv + hq / G;
+    const float* ml = part_ml + row * nchunk * 2;
+    const float* po = part_o + row * nchunk * D;
     const int c = slice * kMergeSlice + (t % kMergeSlice), grp = t / kMergeSlice;
-    const float vs = grp == 0 ? a.v_scale[(long long)bg * D + c] : 0.0f;
+    const float vs = grp == 0 ? v_scale[(long long)bg * D + c] : 0.0f;
 
     float2 mlt[MLU];
 #pragma unroll
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kMergeT) void decode_merge(DecodeArgs a) {
     if (grp == 0) {
 #pragma unroll
         for (int g2 = 1; g2 < GROUPS; ++g2) o += osum[g2 * kMergeSlice + (t % kMergeSlice)];
-        a.out[row * D + c] = o * vs * (1.0f / l);
+        out[row * D + c] = o * vs * (1.0f / l);
     }
 }
 
@@ -410,8 +415,8 @@ SAGE_DECODE_INST_K(Bf16Tag, 128)
 #undef SAGE_DECODE_INST_C
 #undef SAGE_DECODE_INST_PV
 #undef SAGE_DECODE_INST
-template __global__ void decode_merge<64>(DecodeArgs);
-template __global__ void decode_merge<128>(DecodeArgs);
+template __global__ void decode_merge<64>(const float*, const float*, const float*, float*, int, int, int, int, int);
+template __global__ void decode_merge<128>(const float*, const float*, const float*, float*, int, int, int, int, int);
 
 // Chunking: about one round of work-groups, wgs_per_cu per CU, in chunks of
 // at least kMinChunkBlocks blocks so that filling each work-group's tile
@@ -455,7 +460,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nchunk == 1) return e;
     hipLaunchKernelGGL((decode_merge<D>), dim3((unsigned)((long long)a.B * a.Hq * a.Nq * (D / kMergeSlice))),
-                       dim3(kMergeT), 0, st, a);
+                       dim3(kMergeT), 0, st, a.part_ml, a.part_o, a.v_scale, a.out, a.nchunk, a.Nq, a.Hq,
+                       a.G, a.Hkv);
     return hipGetLastError();
 }
 
