@@ -210,6 +210,40 @@ def cpu_baseline(w, q, k, v, rows_wanted, bq, bk, pv, qk_bits):
                       f"(prep {t_prep:.2f} s, attention {t_attn:.2f} s)"}
 
 
+def accuracy_vs_f64(w, q, k, v, out, torch, count=256):
+    """Cosine similarity and relative L1 of the GPU output against full-precision
+    attention, softmax(Q K^T sm_scale) V in float64 on the CPU (plain torch, not
+    the oracle), on a seeded sample of query rows (for the peaked-row recipe,
+    plus some of its x20 rows)."""
+    import numpy as np
+
+    import workloads
+
+    rows = workloads.sample_rows(w, count, seed=5)
+    if w.recipe == 4:
+        qn = q[0, 0].float().abs().amax(dim=-1)
+        hot = torch.nonzero(qn > 4 * qn.median()).flatten()[:32].numpy().astype(np.int64)
+        rows = np.unique(np.concatenate([rows, hot]))
+    n, G = w.q_rows, w.Hq // w.Hkv
+    got = out.reshape(-1, w.d)[torch.from_numpy(rows).to(out.device)].double().cpu()
+    ref = torch.empty_like(got)
+    bh, i = rows // n, rows % n
+    for key in np.unique(bh // w.Hq * w.Hkv + (bh % w.Hq) // G):
+        sel = np.nonzero(bh // w.Hq * w.Hkv + (bh % w.Hq) // G == key)[0]
+        b, g = divmod(int(key), w.Hkv)
+        qr = q.reshape(w.B * w.Hq, n, w.d)[torch.from_numpy(bh[sel]), torch.from_numpy(i[sel])].double()
+        s = (qr @ k[b, g].double().T) * w.sm_scale
+        if w.causal:
+            pos = torch.from_numpy(i[sel] + (w.N - n))[:, None]
+            s.masked_fill_(torch.arange(w.N)[None, :] > pos, float("-inf"))
+        ref[torch.from_numpy(sel)] = torch.softmax(s, dim=-1) @ v[b, g].double()
+    a, r = got.flatten(), ref.flatten()
+    return {"cos": round(float(a @ r / (a.norm() * r.norm())), 6),
+            "rel_l1": round(float((a - r).abs().sum() / r.abs().sum()), 5), "rows": int(len(rows)),
+            "reference": "float64 softmax(QK^T sm_scale)V on the CPU (torch), same inputs",
+            "lines": {"cos_min": 0.999, "rel_l1_max": 0.03}}
+
+
 def decode_bytes(w, k_block, pv):
     """Bytes one short-query launch must move with this cache format: INT8 K
     (1 B), V as E4M3 codes (1 B) or binary16 (2 B), the K scales and V scales
@@ -285,6 +319,7 @@ def bench_decode(args, sage, workloads, torch):
         "tops": round(w.ops / (ms * 1e-3) / 1e12, 2),
         "timed_wall_s": round(wall, 3),
     }
+    line["accuracy"] = accuracy_vs_f64(w, q, k, v, out, torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_decode(w, q, k, v, kb, args.pv)
     print(json.dumps(line), flush=True)
@@ -356,12 +391,13 @@ def main():
                    "q_block": qb, "k_block": kb, "pv_format": args.pv, "qk_bits": args.qk_bits,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
+                     "unit": "TOPS", "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd (+ attn_tail_merge)", "ms_per_launch": round(ms_attn, 4)},
         "prep": {"ms_per_launch": round(ms_prep, 4), "alg_GBps": round(prep_gbs, 1),
                  "frac_hbm": round(prep_gbs / HBM_PEAK_GBS, 4)},
         "timed_wall_s": round(wall, 3),
     }
+    line["accuracy"] = accuracy_vs_f64(w, q, k, v, out, torch)
     if args.prep_flush:
         ms_pf = prep_flushed(sage, qd, kd, vd, z, max(args.steps, 20), torch)
         line["prep"]["flushed_median_ms"] = round(ms_pf, 4)

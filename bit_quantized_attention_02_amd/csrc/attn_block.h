@@ -12,11 +12,16 @@
 //      With keys on the M side every lane holds 64 scores of ONE query row,
 //      and the other 64 sit in the lane 32 apart: a row maximum is in-lane
 //      work plus one permlane32 swap;
-//   3. online softmax in FP32: the INT32 accumulator is seeded with the bit
-//      pattern of 1.5*2^23, so each score reads as the float32 1.5*2^23 + acc
-//      with no conversion; block maximum m (on the integer patterns, scaled per
-//      K-scale half), P8 = e4m3(2^(acc*c + log2(448) - m)), so the block's
-//      largest element codes to exactly 448 (the E4M3 P with a per-block scale);
+//   3. online softmax in FP32.  Each score enters float32 exactly: the INT32
+//      accumulator is seeded with the bit pattern of 1.5*2^23, so a tile read
+//      as float32 holds 1.5*2^23 + acc, and one v_mfma_f32_16x16x1_4b_f32 per
+//      tile (A = 1, B = -1.5*2^23) subtracts the constant from all 16 values
+//      of a lane at once -- exactly, both operands lying in [2^23, 2^24) --
+//      on the otherwise idle matrix pipe instead of 64 vector conversions.
+//      Block maximum m = f32(max acc * c) per K-scale group (on the integer
+//      patterns, which order like the scores), and
+//      P8 = e4m3(2^fmaf(acc, c, f32(log2(448) - m))), so the block's largest
+//      element codes to exactly 448 (the E4M3 P with a per-block scale);
 //   4. level 1: the block's P8.V8 product on v_mfma_f32_32x32x16_f16 -- the
 //      E4M3 values are exact in binary16 and that matrix core sums the exact
 //      products in FP32 (gfx950's FP8 matrix core truncates its internal sum to
@@ -51,8 +56,11 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyRescale = 8.0f;
-constexpr float kSeed = 12582912.0f;   // 1.5 * 2^23
-constexpr int kSeedBits = 0x4B400000;  // its float32 bit pattern
+// The seed of the Q.K^T accumulator: 1.5 * 2^23 and its float32 bit pattern.
+// With |acc| < 2^22 (127^2 * 128 < 2^21), the pattern kSeedBits + acc is the
+// float32 kSeed + acc.
+constexpr float kSeed = 12582912.0f;
+constexpr int kSeedBits = 0x4B400000;
 
 // XOR swizzle of the 16-byte chunks of one K-tile row (d bytes long): the 16
 // lanes of one LDS read phase (16 consecutive rows, same chunk) land on 16
@@ -182,13 +190,10 @@ __device__ inline int max_across_halves(int x) {
 
 // S^T = K Q^T of one key block for one wave (32 query rows), INT32, on
 // v_mfma_i32_32x32x32_i8.  Tile t, element v: key 32t + 8(v/4) + 4h + v%4.
-// SEEDED (INT8 codes): the accumulator is seeded with the bit pattern of
-// 1.5*2^23, so the result read as a float32 is exactly 1.5*2^23 + acc
-// (|acc| < 2^22).  Without it (the INT4 codes of the 4-bit variant, whose
-// score factors are about 330 times larger, so the seed's float32 rounding
-// would no longer be negligible) the plain sums are returned and each score
-// is converted from the integer accumulator, one more instruction per score.
-template <int D, bool SEEDED>
+// The accumulator is seeded with the bit pattern of 1.5*2^23, so each result
+// read as a float32 is exactly 1.5*2^23 + acc (|acc| < 2^22); the patterns
+// order like the integer scores.
+template <int D>
 __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, const v4i (&qf)[D / 32],
                                              int h, int r32, v16i (&S)[4]) {
     constexpr int KS = D / 32;
@@ -197,7 +202,7 @@ __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, con
         const int kr = 32 * t + r32;
         v16i acc;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = SEEDED ? kSeedBits : 0;
+        for (int v = 0; v < 16; ++v) acc[v] = kSeedBits;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const v4i kf = *reinterpret_cast<const v4i*>(lk + kr * D + (((2 * ks + h) ^ kswz<D>(kr)) << 4));
@@ -207,26 +212,32 @@ __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, con
     }
 }
 
+// The exact float32 values of a tile of seeded scores: every output element
+// of v_mfma_f32_16x16x1_4b_f32 is C + A*B with A = 1 and B = -1.5*2^23 in
+// every lane, so each of the lane's 16 values becomes (1.5*2^23 + acc) -
+// 1.5*2^23 = acc, exact (the two terms share their exponent).  A masked score
+// (pattern INT32_MIN, read as -0.0) becomes -1.5*2^23, which no real score
+// reaches.
+__device__ __forceinline__ v16f scores_to_f32(const v16i& s) {
+    return __builtin_amdgcn_mfma_f32_16x16x1f32(1.0f, -kSeed, __builtin_bit_cast(v16f, s), 0, 0, 0);
+}
+
 // The rest of one key block for one wave, from its scores S: masking, online
 // softmax, P and both levels of P.V.  MASKED: some keys of the block are
 // excluded (causal diagonal, or keys >= N).  PV16: P is rounded to binary16
 // directly (l448 is then 0) instead of through E4M3.  V8: the V tile holds
 // E4M3 code bytes (a KV cache), converted to binary16 -- exactly -- as each
-// fragment is read.  SEEDED: as for block_scores.
+// fragment is read.
 // KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
 // 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
 // log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false,
-          bool SEEDED = true>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false>
 __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __restrict__ lv, int T,
                                                  int row, int N, const float (&c)[KSPLIT], float l448,
                                                  int h, int r32, const v8h& rsel, float& mref,
                                                  float& lsum, v16f (&O)[D / 32]) {
     constexpr int CT = D / 32;
     constexpr int TPG = 4 / KSPLIT;  // tiles per scale group
-    float u[KSPLIT];
-#pragma unroll
-    for (int g = 0; g < KSPLIT; ++g) u[g] = SEEDED ? kSeed * c[g] : 0.0f;
 
     // ---- block maxima, one per K-scale group
     if (MASKED) {
@@ -249,11 +260,17 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
 #pragma unroll
             for (int v = (tt == 0 ? 1 : 0); v < 16; ++v) M = max(M, S[g * TPG + tt][v]);
         M = max_across_halves(M);
-        const float fm = SEEDED ? __builtin_bit_cast(float, M) : (float)M;
-        float m = __builtin_fmaf(fm, c[g], -u[g]);
+        // f32(acc_max * c): the pattern read as float32, less the seed
+        // (exact), times c, one rounding -- the largest f32(acc * c) of the
+        // group, since c >= 0
+        float m = (__builtin_bit_cast(float, M) - kSeed) * c[g];
         if (MASKED && M == INT32_MIN) m = -INFINITY;
         mt = fmaxf(mt, m);
     }
+    // the scores as float32, on the matrix pipe (see scores_to_f32)
+    v16f F[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) F[t] = scores_to_f32(S[t]);
 
     // ---- lazy update of the reference maximum
     {
@@ -275,10 +292,7 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
     // At d = 128 the channel tiles go in two passes of two, so that one pass's
     // accumulators, the P pieces and O fit in the architectural registers.
     constexpr int CG = CT < 2 ? CT : 2;
-    const float e = l448 - mt;
-    float bias[KSPLIT];
-#pragma unroll
-    for (int g = 0; g < KSPLIT; ++g) bias[g] = e - u[g];
+    const float bias = l448 - mt;
     v8h P[8];
     v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -293,10 +307,6 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
             if (pass == 0) {
                 const int t = s >> 1, base = 8 * (s & 1);
                 const float ct = c[t / TPG];
-                const float bt = bias[t / TPG];
-                // (bit_cast of the whole vector: this compiler mis-reads a
-                // bit_cast of a single vector element as element 0)
-                const v16f F = SEEDED ? __builtin_bit_cast(v16f, S[t]) : __builtin_convertvector(S[t], v16f);
                 v4i quad;
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
@@ -304,8 +314,8 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int v = base + 4 * g + i;
-                        y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[v], ct, bt));
-                        if (MASKED && S[t][v] == INT32_MIN) y[i] = 0.0f;
+                        y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[t][v], ct, bias));
+                        if (MASKED && F[t][v] == -kSeed) y[i] = 0.0f;
                     }
                     if (PV16) {
                         // round to nearest even, two values per conversion
@@ -361,8 +371,7 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
 }
 
 // One whole key block for one wave: block_scores, then block_softmax_pv.
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false,
-          bool SEEDED = true>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false>
 __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const void* __restrict__ lv,
                                            const v4i (&qf)[D / 32], int T, int row, int N,
@@ -370,9 +379,9 @@ __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const v8h& rsel, float& mref, float& lsum,
                                            v16f (&O)[D / 32]) {
     v16i S[4];
-    block_scores<D, SEEDED>(lk, qf, h, r32, S);
-    block_softmax_pv<D, KSPLIT, CAUSAL, PV16, MASKED, V8, SEEDED>(S, lv, T, row, N, c, l448, h, r32,
-                                                                 rsel, mref, lsum, O);
+    block_scores<D>(lk, qf, h, r32, S);
+    block_softmax_pv<D, KSPLIT, CAUSAL, PV16, MASKED, V8>(S, lv, T, row, N, c, l448, h, r32, rsel,
+                                                          mref, lsum, O);
 }
 
 }  // namespace sage

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
 #pragma unroll
             for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * kscale[gg]) * a.qk;
             v16i S[4];
-            block_scores<D, true>(lk0, qf, h, r32, S);
+            block_scores<D>(lk0, qf, h, r32, S);
             if (more) {
                 // the K fragments are in registers: the tile can be replaced.
                 // (The destination goes through an empty asm statement: with
@@ -233,10 +233,10 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
             else
                 asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
             if (T < first_masked)
-                block_softmax_pv<D, KSPLIT, CAUSAL, PV16, false, V8, true>(
+                block_softmax_pv<D, KSPLIT, CAUSAL, PV16, false, V8>(
                     S, lv0, T, pos, a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
             else
-                block_softmax_pv<D, KSPLIT, CAUSAL, PV16, true, V8, true>(
+                block_softmax_pv<D, KSPLIT, CAUSAL, PV16, true, V8>(
                     S, lv0, T, pos, a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);
             kscale = knext;
             if (more) {

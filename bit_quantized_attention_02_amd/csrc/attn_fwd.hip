@@ -38,7 +38,7 @@ struct AttnArgs {
     float l448;  // f32(log2 448), or 0 for binary16 P
 };
 
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool SEEDED, int WAVES, int WAVES_PER_SIMD>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16, int WAVES, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs a) {
     constexpr int KS = D / 32;
     constexpr int CT = D / 32;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         float c[KSPLIT];
 #pragma unroll
         for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-        attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(ODD ? lk1 : lk0, ODD ? lv1 : lv0, qf, T, row,
+        attn_block<D, KSPLIT, CAUSAL, PV16, false>(ODD ? lk1 : lk0, ODD ? lv1 : lv0, qf, T, row,
                                                                  a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
             float c[KSPLIT];
 #pragma unroll
             for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-            attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(
+            attn_block<D, KSPLIT, CAUSAL, PV16, false>(
                 odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
             kscale = knext;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -196,10 +196,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         // (without causality only the ragged last block is left here: one
         // body, whose registers then need no spilling at d = 128)
         if (CAUSAL && T < n_full)
-            attn_block<D, KSPLIT, CAUSAL, PV16, false, false, SEEDED>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
+            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
                                                        a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         else if (T <= wave_last)
-            attn_block<D, KSPLIT, CAUSAL, PV16, true, false, SEEDED>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
+            attn_block<D, KSPLIT, CAUSAL, PV16, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
                                                       a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -248,19 +248,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 // work-group per CU (96 KB of LDS), two waves per SIMD.
 template <int D>
 constexpr int attn_waves() {
-#ifdef SAGE_ATTN_WAVES
-    return SAGE_ATTN_WAVES;
-#else
     return D == 64 ? 4 : 8;
-#endif
 }
 template <int D, int KSPLIT, bool CAUSAL>
 constexpr int attn_waves_per_simd() {
-#ifdef SAGE_ATTN_WPS
-    return SAGE_ATTN_WPS;
-#else
     return D == 64 && KSPLIT == 2 && !CAUSAL ? 3 : 2;
-#endif
 }
 
 // Combines the key-split shares of the last partial round's tiles: per query
@@ -312,12 +304,11 @@ template __global__ void attn_tail_merge<128>(AttnArgs, int);
 // Explicit instantiations: with the packed-FP32 feature switched off on the
 // command line, this compiler otherwise leaves the host stubs of some of these
 // kernels undefined.
-#define SAGE_ATTN_INST(D, KSPLIT, CAUSAL, PV16, SEEDED)                                           \
+#define SAGE_ATTN_INST(D, KSPLIT, CAUSAL, PV16)                                                   \
     template __global__ void                                                                        \
-    attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, attn_waves<D>(), attn_waves_per_simd<D, KSPLIT, CAUSAL>()>(AttnArgs);
-#define SAGE_ATTN_INST_PV(D, KSPLIT, CAUSAL)                                                       \
-    SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false, true) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true, true)    \
-    SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false, false) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true, false)
+    attn_fwd<D, KSPLIT, CAUSAL, PV16, attn_waves<D>(), attn_waves_per_simd<D, KSPLIT, CAUSAL>()>(AttnArgs);
+#define SAGE_ATTN_INST_PV(D, KSPLIT, CAUSAL) \
+    SAGE_ATTN_INST(D, KSPLIT, CAUSAL, false) SAGE_ATTN_INST(D, KSPLIT, CAUSAL, true)
 SAGE_ATTN_INST_PV(64, 2, false)
 SAGE_ATTN_INST_PV(64, 2, true)
 SAGE_ATTN_INST_PV(64, 4, false)
@@ -329,14 +320,14 @@ SAGE_ATTN_INST_PV(128, 4, true)
 #undef SAGE_ATTN_INST_PV
 #undef SAGE_ATTN_INST
 
-template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool SEEDED>
+template <int D, int KSPLIT, bool CAUSAL, bool PV16>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WAVES = attn_waves<D>();
     constexpr int WPS = attn_waves_per_simd<D, KSPLIT, CAUSAL>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
@@ -353,7 +344,7 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
             hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
             hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, (const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>, 64 * WAVES,
+                &per_cu, (const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>, 64 * WAVES,
                 lds) == hipSuccess;
         if (!known) (void)hipGetLastError();  // a failed query only means no split
         if (known) {
@@ -384,7 +375,7 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
         }
     }
     const int grid = a.tiles_main + (total - a.tiles_main) * a.tail_split;
-    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, SEEDED, WAVES, WPS>), dim3(grid),
+    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>), dim3(grid),
                        dim3(64 * WAVES), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.tail_split == 1) return e;
@@ -394,22 +385,14 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int D, int KSPLIT, bool PV16, bool SEEDED>
-static hipError_t launch_attn_p(AttnArgs a, int causal, hipStream_t st) {
-    return causal ? launch_attn_t<D, KSPLIT, true, PV16, SEEDED>(a, st)
-                  : launch_attn_t<D, KSPLIT, false, PV16, SEEDED>(a, st);
-}
-
 template <int D, int KSPLIT, bool PV16>
-static hipError_t launch_attn_s(AttnArgs a, int causal, bool seeded, hipStream_t st) {
-    return seeded ? launch_attn_p<D, KSPLIT, PV16, true>(a, causal, st)
-                  : launch_attn_p<D, KSPLIT, PV16, false>(a, causal, st);
+static hipError_t launch_attn_p(AttnArgs a, int causal, hipStream_t st) {
+    return causal ? launch_attn_t<D, KSPLIT, true, PV16>(a, st) : launch_attn_t<D, KSPLIT, false, PV16>(a, st);
 }
 
 template <int D, int KSPLIT>
-static hipError_t launch_attn_d(AttnArgs a, int causal, bool pv16, bool seeded, hipStream_t st) {
-    return pv16 ? launch_attn_s<D, KSPLIT, true>(a, causal, seeded, st)
-                : launch_attn_s<D, KSPLIT, false>(a, causal, seeded, st);
+static hipError_t launch_attn_d(AttnArgs a, int causal, bool pv16, hipStream_t st) {
+    return pv16 ? launch_attn_p<D, KSPLIT, true>(a, causal, st) : launch_attn_p<D, KSPLIT, false>(a, causal, st);
 }
 
 hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int causal,
@@ -439,12 +422,10 @@ hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int 
     a.l448 = l448;
     const bool fine_k = z->k_block == SAGE_BK_THREAD;  // 4 K scales per block, else 2
     const bool pv16 = z->pv_format == SAGE_PV_F16;
-    const bool seeded = z->qk_bits == SAGE_QK_INT8;  // INT4 codes take the unseeded scores
+    // (INT4 codes go through the same kernels: their scores are as exact)
     if (s.d == 64)
-        return fine_k ? launch_attn_d<64, 4>(a, causal, pv16, seeded, st)
-                      : launch_attn_d<64, 2>(a, causal, pv16, seeded, st);
-    return fine_k ? launch_attn_d<128, 4>(a, causal, pv16, seeded, st)
-                  : launch_attn_d<128, 2>(a, causal, pv16, seeded, st);
+        return fine_k ? launch_attn_d<64, 4>(a, causal, pv16, st) : launch_attn_d<64, 2>(a, causal, pv16, st);
+    return fine_k ? launch_attn_d<128, 4>(a, causal, pv16, st) : launch_attn_d<128, 2>(a, causal, pv16, st);
 }
 
 }  // namespace sage

@@ -28,13 +28,16 @@
  *     .k_block select it.
  *   - FP8: OCP E4M3FN (max 448), round to nearest even.  V: one scale per
  *     channel, code = e4m3(v * f32(448/absmax_c)).
- *   - P: one block is one query row by SAGE_BN keys; with m the block's largest
- *     score in log2 units (float32), the block's codes are
- *     e4m3(2^fmaf(acc, c, f32(log2(448)) - m)) where c = f32(f32(s_q*s_k) *
- *     f32(sm_scale*log2 e)), so the largest element codes to 448.  Level 1 is
- *     the block's P8.V8 product, exact products summed in FP32 by the matrix
- *     core; level 2 adds it, weighted by 2^(m - reference max), into FP32
- *     registers.  The row sum is the same weighted sum of the quantized P.
+ *   - Softmax in FP32: each integer score acc (exact) becomes float32 exactly
+ *     and, in log2 units, f32(acc * c) with c = f32(f32(s_q*s_k) *
+ *     f32(sm_scale*log2 e)).
+ *   - P: one block is one query row by SAGE_BN keys; with m the block's
+ *     largest f32(acc * c), the block's codes are
+ *     e4m3(2^fmaf(acc, c, f32(f32(log2(448)) - m))), so the largest element
+ *     codes to 448.  Level 1 is the block's P8.V8 product, exact products
+ *     summed in FP32 by the matrix core; level 2 adds it, weighted by
+ *     2^(m - reference max), into FP32 registers.  The row sum is the same
+ *     weighted sum of the quantized P.
  *   - P.V format (sage_qkv_quant.pv_format).  SAGE_PV_E4M3 is the above.
  *     SAGE_PV_F16 is the SageAttention article's own P.V (paragraph on the P, V
  *     product: P and V stay FP16): V is its binary16 rounding (round to nearest
@@ -46,10 +49,8 @@
  *     Q, K of SageAttention2 (the SageAttention2 summary; the Berkeley brief's
  *     comparison table): the INT8 scheme with 7 in place of 127 (codes in
  *     [-7, 7], scale absmax/7), stored one code per byte and multiplied on
- *     the INT8 matrix core (gfx950 has no INT4 one), at INT8 speed.  Its
- *     scores are converted from the integer accumulator instead of the
- *     1.5*2^23-seeded float read, whose float32 rounding (about one integer
- *     step of c) would matter at INT4 scales.  Decode caches are INT8 only.
+ *     the INT8 matrix core (gfx950 has no INT4 one), at INT8 speed.  Decode
+ *     caches are INT8 only.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library

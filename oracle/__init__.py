@@ -70,7 +70,7 @@ def _load():
         lib.oracle_quantize.argtypes = [P, P, P, i, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
         lib.oracle_quantize_q.argtypes = [P, i, i, i, i, i, i, P, P]
         lib.oracle_quantize_kv.argtypes = [P, P, i, i, i, i, i, i, i, P, P, P, P, P]
-        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, i, i, f,
+        lib.oracle_attn_q.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, i, f,
                                       dd, P, l, P, P, P, P]
         lib.oracle_attn_f64.argtypes = [P, P, P, i, i, i, i, i, i, i, dd, P, l, P]
         lib.oracle_num_threads.restype = i
@@ -186,7 +186,6 @@ def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
     positions) for the given flattened rows (None = all), in the P.V format
     qz["pv"] was made for.  Returns (out, lo, hi, flagged), float64 [nrows, d]."""
     f16 = qz.get("pv", "e4m3") == "f16"
-    seeded = qz.get("qk_bits", 8) == 8
     v_codes = qz["v_f16"] if f16 else qz["v_fp8"]
     v_scale = None if f16 else qz["v_scale"]
     B, Hq, Hkv, Nq, Nk, d = qz["B"], qz["Hq"], qz["Hkv"], qz["Nq"], qz["Nk"], qz["d"]
@@ -202,7 +201,7 @@ def attn_q(qz: dict, causal: bool, sm_scale: float, rows=None, bn: int = BN,
     hi = np.empty((nrows, d), np.float64) if interval else None
     flagged = np.empty(nrows, np.int64) if interval else None
     _load().oracle_attn_q(_ptr(qz["q_i8"]), _ptr(qz["q_scale"]), _ptr(qz["k_i8"]),
-                          _ptr(qz["k_scale"]), _ptr(v_codes), _ptr(v_scale), int(f16), int(seeded),
+                          _ptr(qz["k_scale"]), _ptr(v_codes), _ptr(v_scale), int(f16),
                           B, Hq, Hkv, Nq, Nk, d, qz["bq"], qz["bk"], bn, int(causal),
                           float(sm_scale), float(tau), _ptr(rows), nrows,
                           _ptr(out), _ptr(lo), _ptr(hi), _ptr(flagged))

@@ -25,28 +25,25 @@
  *   - The 4-bit Q, K of SageAttention2 (INT4; the Berkeley brief's comparison
  *     table) are the same with 7 in place of 127: codes in [-7, 7], scale
  *     absmax/7.  The codes are stored one per byte and multiplied like the
- *     INT8 codes.  Their scores are evaluated without the 1.5*2^23 offset
- *     below (seeded = 0: F = acc, u = 0): the float32 rounding of that offset
- *     is about one integer step of c, negligible at INT8 scales but not at
- *     INT4 scales, which are about 330 times larger.
+ *     INT8 codes.
  *   - E4M3 is OCP E4M3FN (bias 7, max 448, subnormal step 2^-9), RNE,
  *     saturating at +-448; V codes are e4m3(v * (448/absmax_c)) in float32.
+ *   - The softmax runs in FP32 (the method's online softmax): the integer
+ *     score acc (exact, |acc| < 2^24) is converted to float32 exactly and
+ *     multiplied by the score factor c = f32(f32(s_q * s_k) * f32(sm_scale *
+ *     log2 e)), one float32 rounding: s = f32(acc * c), in log2 units.
  *   - The P block is one query row by `bn` keys.  Its scale is the block
- *     maximum over 448: with mt the block's largest score (log2 units,
- *     float32), P8 = e4m3(2^x), x ~ acc*c + log2(448) - mt, so the largest
- *     element codes to exactly 448, and the block enters the second
- *     accumulation level with weight 2^(mt - M), M the row maximum.  The row
- *     sum l is the same two-level sum over the quantised P, so the quantised
- *     weights are normalised exactly.  See oracle_attn_q.
- *   - The score enters float32 as F = 1.5*2^23 + acc, which is exact: the
- *     matrix core's INT32 accumulator is seeded with that constant's bit
- *     pattern and read as a float32, which saves a conversion per score.  The
- *     exponent argument x and the block maximum mt are then defined by the
- *     float32 operations written in oracle_attn_q, so that both sides take the
- *     P8 decision on the same number; only 2^x itself is evaluated
- *     differently (float64 here).  Codes whose 2^x lies within a relative
- *     `tau` of a rounding midpoint have two correct values; the oracle
- *     returns the interval spanned by both choices.
+ *     maximum over 448 (the Berkeley brief's softmax-domain scaling): with mt
+ *     the block's largest s (float32), P8 = e4m3(2^x) with x = f32(acc * c +
+ *     f32(f32(log2 448) - mt)) (one fused multiply-add), so the largest
+ *     element codes to 448, and the block enters the second accumulation
+ *     level with weight 2^(mt - M), M the row maximum.  The row sum l is the
+ *     same two-level sum over the quantised P, so the quantised weights are
+ *     normalised exactly.  See oracle_attn_q.  The P8 decision is taken on
+ *     this float32 x; only 2^x itself is evaluated in float64 here.  Codes
+ *     whose 2^x lies within a relative `tau` of a rounding midpoint have two
+ *     correct values (an FP32 exp2 may round either way); the oracle returns
+ *     the interval spanned by both choices.
  *
  * The binary16 P.V mode (SageAttention article, paragraph on the P, V product:
  * P and V stay FP16 there, with an FP16 accumulator).  The matrix cores this
@@ -278,18 +275,14 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  *
  *   acc_j = sum_c q_i8[i,c] * k_i8[j,c]                       (exact integer)
  *   c_j   = f32( f32(sq * sk[j/bk]) * f32(sm_scale*log2 e) )   (float32)
- *   F_j   = 1.5*2^23 + acc_j (exact in float32), u_j = f32(1.5*2^23 * c_j)
- *   s_j   = fmaf(F_j, c_j, -u_j)       (= acc_j * c_j up to float32 rounding)
+ *   s_j   = f32(acc_j * c_j)                                   (float32, log2 units)
  *   blocks t of bn keys; m_t = max of s_j over the block's allowed keys
- *   x_j   = fmaf(F_j, c_j, f32(f32(f32(log2 448) - m_t) - u_j))
+ *   x_j   = fmaf(acc_j, c_j, f32(f32(log2 448) - m_t))
  *   y_j   = 2^x_j (float64);  P8_j = e4m3(y_j)   (the block maximum codes to 448)
  *   level 1: A_t[c] = sum_{j in t} P8_j * V8[j,c];  R_t = sum_{j in t} P8_j
  *   level 2: with M = max_t m_t and w_t = 2^(m_t - M) (float64),
  *            O[c] = sum_t w_t A_t[c],  l = sum_t w_t R_t
  *   out[c] = O[c] * sv[c] / l
- *
- * seeded = 0 (the 4-bit Q, K variant) evaluates the scores without the offset:
- * F_j = acc_j and u_j = 0 in every formula above.
  *
  * pv_f16 = 1 selects the binary16 P.V mode: v_codes holds binary16 codes of V
  * (uint16), v_scale may be NULL (sv = 1), f32(log2 448) above is replaced by 0
@@ -304,7 +297,7 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  */
 void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                    const float* k_scale, const void* v_codes, const float* v_scale, int pv_f16,
-                   int seeded, int B, int Hq, int Hkv, int Nq, int Nk, int d, int bq, int bk, int bn,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int bq, int bk, int bn,
                    int causal, float sm_scale, double tau, const int64_t* rows, long nrows,
                    double* out, double* out_lo, double* out_hi, int64_t* flagged) {
     const long qnd = (long)Nq * d, nd = (long)Nk * d;
@@ -314,8 +307,6 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
     const float qk = (float)((double)sm_scale * 1.4426950408889634); /* log2(e) */
     /* the P block scale: the block maximum maps to 448 (E4M3) or to 1 (binary16) */
     const float l448 = pv_f16 ? 0.0f : (float)log2(448.0);
-    const float seed = seeded ? 12582912.0f : 0.0f; /* 1.5 * 2^23 */
-    const int32_t seed_int = seeded ? 12582912 : 0;
     /* decoded value of every code of the P.V format, and its largest finite
      * positive code */
     const int ncode = pv_f16 ? 65536 : 256;
@@ -331,8 +322,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
     {
         int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
         float* cj = (float*)malloc(sizeof(float) * (size_t)N);
-        float* Fj = (float*)malloc(sizeof(float) * (size_t)N);
-        float* uj = (float*)malloc(sizeof(float) * (size_t)N);
+        float* aj = (float*)malloc(sizeof(float) * (size_t)N);
         float* mblk = (float*)malloc(sizeof(float) * (size_t)(N / bn + 2));
         double* A = (double*)malloc(sizeof(double) * (size_t)d);
         double* O = (double*)malloc(sizeof(double) * (size_t)d);
@@ -363,8 +353,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 acc[j] = s;
                 float sqk = sq * skh[j / bk];
                 cj[j] = sqk * qk;
-                Fj[j] = (float)(seed_int + s);
-                uj[j] = seed * cj[j];
+                aj[j] = (float)s; /* exact: |acc| < 2^24 */
             }
             /* per-block maximum score: the P scale of the block */
             float M = -INFINITY;
@@ -372,7 +361,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 int j0 = t * bn, j1 = j0 + bn - 1 < jmax ? j0 + bn - 1 : jmax;
                 float mt = -INFINITY;
                 for (int j = j0; j <= j1; ++j) {
-                    float s = fmaf(Fj[j], cj[j], -uj[j]);
+                    float s = aj[j] * cj[j];
                     if (s > mt) mt = s;
                 }
                 mblk[t] = mt;
@@ -389,7 +378,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 double R = 0.0;
                 for (int c = 0; c < d; ++c) A[c] = 0.0;
                 for (int j = j0; j <= j1; ++j) {
-                    float x = fmaf(Fj[j], cj[j], bias - uj[j]);
+                    float x = fmaf(aj[j], cj[j], bias);
                     double y = exp2((double)x);
                     int code = pv_f16 ? (int)oracle_f16_encode(y) : (int)oracle_e4m3_encode(y);
                     double p = dec[code];
@@ -443,8 +432,7 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
         }
         free(acc);
         free(cj);
-        free(Fj);
-        free(uj);
+        free(aj);
         free(mblk);
         free(A);
         free(O);

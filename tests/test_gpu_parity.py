@@ -115,7 +115,7 @@ def test_parity_reduced_workloads(sage, orc, recipe, granularity, pv):
 @pytest.mark.parametrize("recipe", [1, 2, 3, 4, 5])
 def test_parity_int4_qk(sage, orc, recipe, granularity):
     """The 4-bit (INT4) Q, K variant on every recipe at N = 700: codes in
-    [-7, 7] bit-exact, scores without the float offset."""
+    [-7, 7] bit-exact, scores taken exactly as for INT8."""
     w0 = workloads.WORKLOADS[recipe]
     w = w0.resized(B=2, Hq=2 * (w0.Hq // w0.Hkv), Hkv=2, N=700)
     pv = "f16" if recipe == 2 else "e4m3"
@@ -142,6 +142,34 @@ def test_parity_edge_lengths(sage, orc, N, d, causal):
                                       seed=N * 7 + d + causal, scale=1.5)
     out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d), granularity, pv, qk_bits)
     oz = quantize_as(orc, q, k, v, granularity, pv, qk_bits)
+    check_prep(orc, quant, oz)
+    check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 1 / math.sqrt(d), None)
+
+
+@pytest.mark.parametrize("kind", ["scale100", "planted_outliers"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
+def test_parity_large_score_factors(sage, orc, kind, d, causal, pv):
+    """Scores whose float32 evaluation is delicate: |Q|, |K| around 100
+    (every row dominated by a few keys, scores in the thousands), and
+    heavy-tail inputs with a +-50 element planted in every Q and K scale
+    block (score factor c of every block about 0.02-0.03 against small
+    typical codes).  Checked against the plain FP32 exponent of the oracle."""
+    N = 700
+    if kind == "scale100":
+        q, k, v = workloads.random_inputs(1, 4, 2, N, d, "bf16", seed=900 + d + causal, scale=100.0)
+    else:
+        w = workloads.WORKLOADS[5].resized(B=1, Hq=4, Hkv=2, N=N, d=d)
+        q, k, v = workloads.generate(w, seed=910 + d + causal)
+        rng = np.random.Generator(np.random.PCG64(920 + d))
+        for t, r0 in ((q, 128), (k, 64)):
+            for h in range(t.shape[1]):
+                for r in range(0, N, r0):
+                    t[0, h, r, int(rng.integers(d))] = float(rng.choice([-50.0, 50.0]))
+    _say(f"case large scores kind={kind} d={d} causal={causal} pv={pv}")
+    out, quant = run_gpu(sage, q, k, v, causal, 1 / math.sqrt(d), "block", pv)
+    oz = quantize_as(orc, q, k, v, "block", pv)
     check_prep(orc, quant, oz)
     check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 1 / math.sqrt(d), None)
 
@@ -230,49 +258,95 @@ def test_parity_split_tail(sage, orc, pv):
     check_attn(orc, _rows_of(out, rows, w.d), oz, False, w.sm_scale, rows)
 
 
-@pytest.mark.parametrize("index,granularity,pv,qk_bits", [
-    (1, "block", "e4m3", 8), (2, "block", "e4m3", 8), (3, "block", "e4m3", 8), (4, "block", "e4m3", 8),
-    (5, "block", "e4m3", 8), (3, "thread", "e4m3", 8), (4, "thread", "e4m3", 8), (5, "thread", "e4m3", 8),
-    (2, "block", "f16", 8), (3, "block", "f16", 8), (4, "block", "f16", 8), (5, "block", "f16", 8),
-    (5, "thread", "f16", 8), (3, "thread", "e4m3", 4), (4, "thread", "f16", 4)])
+# The method's accuracy against float64 attention on the original inputs, on
+# the rows each full-size case checks.  The pages print no accuracy figure
+# (their tables did not survive extraction): these floors are the CPU oracle's
+# own cos / rel-L1 on exactly these inputs and rows, less a small margin, so a
+# kernel or prep change that loses accuracy fails here.  Where the oracle
+# meets the lines cos >= 0.999 or rel-L1 <= 0.03, the line itself is the bar.
+# (cos at least, rel-L1 at most)
+ACCURACY = {
+    (1, "block", "e4m3", 8): (0.999, 0.040),     # oracle 0.999256, 0.03845
+    (2, "block", "e4m3", 8): (0.999, 0.0425),    # 0.999213, 0.04081
+    (3, "block", "e4m3", 8): (0.999, 0.0385),    # 0.999332, 0.03682
+    (4, "block", "e4m3", 8): (0.9975, 0.086),    # 0.997717, 0.08292
+    (5, "block", "e4m3", 8): (0.9945, 0.073),    # 0.994697, 0.07026
+    (3, "thread", "e4m3", 8): (0.999, 0.0375),   # 0.999366, 0.03599
+    (4, "thread", "e4m3", 8): (0.9980, 0.0425),  # 0.998173, 0.04102
+    (5, "thread", "e4m3", 8): (0.999, 0.038),    # 0.999057, 0.03665
+    (2, "block", "f16", 8): (0.999, 0.03),       # 0.999645, 0.02618
+    (3, "block", "f16", 8): (0.999, 0.03),       # 0.999920, 0.01263
+    (4, "block", "f16", 8): (0.9978, 0.074),     # 0.998049, 0.07137
+    (5, "block", "f16", 8): (0.9948, 0.060),     # 0.995004, 0.05737
+    (5, "thread", "f16", 8): (0.999, 0.03),      # 0.999373, 0.02152
+    (3, "thread", "e4m3", 4): (0.980, 0.20),     # 0.981769, 0.19191
+    (4, "thread", "f16", 4): (0.79, 0.32),       # 0.794744, 0.30783
+}
+
+
+def tile_rows(w, seed=13):
+    """One row of every tile of query rows the attention kernel gives a
+    work-group (128 rows at d = 64, 256 at d = 128), at a seeded position
+    inside the tile (rows past N excluded), as flattened row indices."""
+    rows_per_tile = 128 if w.d == 64 else 256
+    nt = -(-w.N // rows_per_tile)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    heads = np.arange(w.B * w.Hq)[:, None]
+    start = np.arange(nt)[None, :] * rows_per_tile
+    span = np.minimum(rows_per_tile, w.N - start)
+    off = (rng.random((w.B * w.Hq, nt)) * span).astype(np.int64)
+    return (heads * w.N + start + off).ravel().astype(np.int64)
+
+
+@pytest.mark.parametrize("index,granularity,pv,qk_bits", list(ACCURACY))
 def test_parity_full_size_workloads(sage, orc, index, granularity, pv, qk_bits):
     """Each workload at its full size, through sage_attn_fwd as the benchmark
-    times it: the prep outputs are compared in full (bit-exact), the attention
-    output on sampled rows the oracle computes one by one (first and last row
-    of the first and last head, 256 seeded rows, and for the peaked-row recipe
-    some of the x20 rows)."""
+    times it.  The output is filled with NaN first and must come back finite
+    everywhere (every tile and every key share of a split tile wrote its
+    rows).  The prep outputs are compared in full (bit-exact), the attention
+    output on rows the oracle computes one by one: one row of every
+    work-group tile, the first and last row of the first and last head, 256
+    seeded rows, rows of the last head's last tiles (where the tail split
+    happens), and for the peaked-row recipe some of the x20 rows.  The
+    accuracy against float64 attention must stay at the level ACCURACY
+    records."""
     w = workloads.WORKLOADS[index]
     _say(f"case full-size workload {index} {w.name} granularity={granularity} pv={pv} qk_bits={qk_bits}")
     q, k, v = workloads.generate(w)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
-    out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    out = torch.full(qd.shape, float("nan"), dtype=torch.float32, device="cuda")
     ws = sage.workspace_for(qd, kd)
     sage.sage_attn_fwd_ex(qd, kd, vd, out, w.causal, w.sm_scale, sage.options(granularity, pv, qk_bits),
                           ws)
     torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "some output rows were not written"
     z = sage.sage_workspace_carve(ws, ws.numel(), w.B, w.Hq, w.Hkv, w.N, w.d, granularity=granularity,
                                   pv=pv, qk_bits=qk_bits)
     quant = sage.read_quantized(z, ws, w.B, w.Hq, w.Hkv, w.N, w.d)
     del qd, kd, vd
     oz = quantize_as(orc, q, k, v, granularity, pv, qk_bits)
     check_prep(orc, quant, oz)
-    rows = workloads.sample_rows(w, 256, seed=11)
+    rows = np.concatenate([workloads.sample_rows(w, 256, seed=11), tile_rows(w)])
     if not w.causal:
         # rows of the last head's last 100 tiles: where the tiles left over
         # after the last whole round of work-groups are split along the keys
         last = (w.B * w.Hq - 1) * w.N
         lo = max(0, w.N - 100 * 128)
         pick = np.random.Generator(np.random.PCG64(12)).choice(w.N - lo, size=min(32, w.N - lo), replace=False)
-        rows = np.unique(np.concatenate([rows, last + lo + pick, [last + w.N - 1]])).astype(np.int64)
+        rows = np.concatenate([rows, last + lo + pick, [last + w.N - 1]])
     if w.recipe == 4:
         # rows scaled x20 in the first head: the largest |Q| rows
         qn = q[0, 0].float().abs().amax(dim=-1)
         hot = torch.nonzero(qn > 4 * qn.median()).flatten()[:32].numpy().astype(np.int64)
-        rows = np.unique(np.concatenate([rows, hot]))
+        rows = np.concatenate([rows, hot])
+    rows = np.unique(rows).astype(np.int64)
     got = out.reshape(-1, w.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    _say(f"   {len(rows)} rows checked")
     nom = check_attn(orc, got, oz, w.causal, w.sm_scale, rows)
-    # the method's accuracy against full precision (reported, not a parity bar)
+    # the method's accuracy against full precision
     ref = orc.attn_f64(q, k, v, w.causal, w.sm_scale, rows=rows)
     a_gpu, a_orc = orc.accuracy(got, ref), orc.accuracy(nom, ref)
     _say(f"   vs float64: gpu cos={a_gpu['cos']:.6f} relL1={a_gpu['rel_l1']:.4f}; "
          f"oracle cos={a_orc['cos']:.6f} relL1={a_orc['rel_l1']:.4f}")
+    cos_min, rel_max = ACCURACY[(index, granularity, pv, qk_bits)]
+    assert a_gpu["cos"] >= cos_min and a_gpu["rel_l1"] <= rel_max

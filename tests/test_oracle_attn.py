@@ -62,6 +62,14 @@ def _deq_inputs(orc, z):
     return qd, kd, vd
 
 
+def _max_log2_score(qd, kd, sm_scale):
+    """Largest |score| in log2 units over every (query, key) pair of the
+    dequantized operands (kv head h // G for query head h)."""
+    G = qd.shape[1] // kd.shape[1]
+    kr = np.repeat(kd, G, axis=1)
+    return float(np.abs(qd @ kr.transpose(0, 1, 3, 2)).max() * sm_scale * math.log2(math.e))
+
+
 @pytest.mark.parametrize("pv", ["e4m3", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_q_gives_mean_of_dequantized_v(orc, causal, pv):
@@ -121,14 +129,16 @@ def test_blockwise_constant_keys_give_weighted_block_means(orc, causal, pv):
     qd, kd, vd = _deq_inputs(orc, z)
     ref = orc.attn_f64(qd, kd, vd, causal, 0.125)
     assert fl.sum() == 0
-    # the block weights carry the float32 evaluation of the exponent: its
-    # constant offset u = f32(1.5 2^23 c) is rounded, so each block's log2
-    # weight is off by at most ~3 ulp(u); the weighted mean moves by at most
-    # twice that relative error times max|V|
-    c_max = float(z["q_scale"].max()) * float(z["k_scale"].max()) * 0.125 * math.log2(math.e)
-    ulp_u = 2.0 ** (math.floor(math.log2(12582912 * c_max)) - 23)
-    eps = 3 * ulp_u * math.log(2)
-    np.testing.assert_allclose(out, ref, rtol=0, atol=2 * eps * np.abs(vd).max() + 1e-12)
+    # every score of a block is equal, so every code is the block maximum's and
+    # the only error left is the float32 evaluation of the log2 block weights:
+    # c = f32(f32(s_q s_k) f32(sm_scale log2 e)) and m_t = f32(acc c) carry at
+    # most four roundings (relative 2^-24 each), so each m_t, and each
+    # difference m_t - M, is off by at most eps = 8 2^-24 max|m|; the block
+    # weights are off by factors within 2^(+-eps), which moves a convex
+    # combination of the block means by at most 2 (2^eps - 1) max|V|
+    m_max = _max_log2_score(qd, kd, 0.125)
+    eps = 8 * 2.0 ** -24 * (m_max + 1)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=2 * (2.0 ** eps - 1) * np.abs(vd).max() + 1e-12)
 
 
 # ----------------------------------------------------------------------------
@@ -192,18 +202,15 @@ def _online_reference(orc, z, causal, sm_scale, bn):
                         c = np.float32(np.float32(s_q * z["k_scale"][b, g, j // z["bk"]]) * qk)
                         accs.append(acc)
                         cs.append(c)
-                    # the score enters float32 as F = 1.5 2^23 + acc (exact),
-                    # with the constant's product u = f32(1.5 2^23 c) taken
-                    # off; the 4-bit variant takes F = acc, u = 0
-                    seed = 12582912 if z.get("qk_bits", 8) == 8 else 0
-                    Fs = [np.float32(seed + a) for a in accs]
-                    us = [np.float32(np.float32(seed) * c) for c in cs]
-                    mt = max(_fma_f32(F, c, -u) for F, c, u in zip(Fs, cs, us))
+                    # FP32 softmax: the exact integer score times the score
+                    # factor, rounded once; the block's largest such value is
+                    # the P scale (its code is the format's largest, 448 or 1)
+                    mt = max(_round_f32(Fraction(a) * Fraction(float(c))) for a, c in zip(accs, cs))
+                    bias = np.float32(l448 - mt)
                     a_blk = np.zeros(d)
                     r_blk = 0.0
-                    for j, F, c, u in zip(blk, Fs, cs, us):
-                        bias = np.float32(np.float32(l448 - mt) - u)
-                        y = 2.0 ** float(_fma_f32(F, c, bias))
+                    for j, a, c in zip(blk, accs, cs):
+                        y = 2.0 ** float(_fma_f32(np.float32(a), c, bias))
                         p = p_code(y)
                         a_blk += p * vrow[b, g, j]
                         r_blk += p
@@ -231,6 +238,33 @@ def test_closed_form_equals_online_recurrence_tiny(orc, N, causal, d, G, pv, qk_
     ref = _online_reference(orc, z, causal, 1 / math.sqrt(d), bn=4)
     ok = fl == 0
     np.testing.assert_allclose(out[ok], ref[ok], rtol=1e-12, atol=1e-13)
+    assert np.all(lo[~ok] <= ref[~ok] + 1e-12) and np.all(ref[~ok] <= hi[~ok] + 1e-12)
+
+
+@pytest.mark.parametrize("pv", ["e4m3", "f16"])
+@pytest.mark.parametrize("N", [7, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_closed_form_equals_online_recurrence_heavy_tails(orc, N, causal, pv):
+    """The same check on the heavy-tail recipe (Student-t(3)), with one
+    element of +-50 planted in every Q and K scale block: the large block
+    absmax against small typical codes makes the score factor c of every
+    block about 0.02-0.03, where the float32 evaluation of each exponent must
+    still be the plain one (f32(acc) c plus one rounded bias) for the codes
+    and block weights to agree."""
+    w = workloads.WORKLOADS[5].resized(B=1, Hq=2, Hkv=1, N=N)
+    q, k, v = workloads.generate(w, seed=300 + N)
+    rng = np.random.Generator(np.random.PCG64(N))
+    for t, r0 in ((q, 4), (k, 2)):
+        for h in range(t.shape[1]):
+            for r in range(0, N, r0):
+                t[0, h, r, int(rng.integers(w.d))] = float(rng.choice([-50.0, 50.0]))
+    z = orc.quantize(q, k, v, bq=4, bk=2, pv=pv)
+    c = np.outer(z["q_scale"].ravel(), z["k_scale"].ravel()) * w.sm_scale * math.log2(math.e)
+    assert c.min() > 0.015
+    out, lo, hi, fl = orc.attn_q(z, causal, w.sm_scale, bn=4)
+    ref = _online_reference(orc, z, causal, w.sm_scale, bn=4)
+    ok = fl == 0
+    np.testing.assert_allclose(out[ok], ref[ok], rtol=1e-12, atol=1e-12)
     assert np.all(lo[~ok] <= ref[~ok] + 1e-12) and np.all(ref[~ok] <= hi[~ok] + 1e-12)
 
 
@@ -264,12 +298,13 @@ def test_f16_pv_within_p_rounding_of_dequantized_reference(orc, recipe):
     """The binary16 P.V mode against float64 attention on the dequantized Q,
     K-smoothed and binary16 V.  Two errors remain: P16_j = y_j (1 + e_j) with
     |e_j| <= 2^-11 for y_j >= 2^-14 and |P16_j - y_j| <= 2^-25 below; and the
-    float32 evaluation of the exponent, whose constant offset u = f32(1.5 2^23
-    c) and bias are rounded, which moves each log2 weight by at most ~3
-    ulp(u).  Each weight is thus off by a factor within 1 +- r,
-    r = (1 + 2^-11) 2^(3 ulp(u)) - 1, and (the row sum being at least 1, the
-    code of the row maximum) the output is within
-    2 max|V| (r / (1 - r) + n 2^-25) of the exact weighted mean."""
+    float32 evaluation of the log2 weights (the score factor c, the block
+    maximum m and the exponent x each carry a few roundings of relative size
+    2^-24), which moves each log2 weight by at most eps = 16 2^-24 (max|m| +
+    1).  Each weight is thus off by a factor within 1 +- r,
+    r = (1 + 2^-11) 2^eps - 1, and (the row sum being at least 1, the code of
+    the row maximum) the output is within 2 max|V| (r / (1 - r) + n 2^-25) of
+    the exact weighted mean."""
     w0 = workloads.WORKLOADS[recipe]
     w = w0.resized(B=1, Hq=w0.Hq // w0.Hkv * 2, Hkv=2, N=700)
     q, k, v = workloads.generate(w, seed=recipe)
@@ -279,9 +314,8 @@ def test_f16_pv_within_p_rounding_of_dequantized_reference(orc, recipe):
     qd, kd, vd = _deq_inputs(orc, z)
     ref = orc.attn_f64(qd, kd, vd, w.causal, w.sm_scale, rows=rows)
     vmax = np.abs(vd).max()
-    c_max = float(z["q_scale"].max()) * float(z["k_scale"].max()) * w.sm_scale * math.log2(math.e)
-    ulp_u = 2.0 ** (math.floor(math.log2(12582912 * c_max)) - 23)
-    r = (1 + 2.0 ** -11) * 2.0 ** (3 * ulp_u) - 1
+    eps = 16 * 2.0 ** -24 * (_max_log2_score(qd, kd, w.sm_scale) + 1)
+    r = (1 + 2.0 ** -11) * 2.0 ** eps - 1
     bound = 2 * vmax * (r / (1 - r) + w.N * 2.0 ** -25)
     assert np.abs(out - ref).max() <= bound
     assert np.all(lo <= out) and np.all(out <= hi)
