@@ -12,12 +12,13 @@
 //      With keys on the M side every lane holds 64 scores of ONE query row,
 //      and the other 64 sit in the lane 32 apart: a row maximum is in-lane
 //      work plus one permlane32 swap;
-//   3. online softmax in FP32.  Each score enters float32 exactly: the INT32
-//      accumulator is seeded with the bit pattern of 1.5*2^23, so a tile read
-//      as float32 holds 1.5*2^23 + acc, and one v_mfma_f32_16x16x1_4b_f32 per
-//      tile (A = 1, B = -1.5*2^23) subtracts the constant from all 16 values
-//      of a lane at once -- exactly, both operands lying in [2^23, 2^24) --
-//      on the otherwise idle matrix pipe instead of 64 vector conversions.
+//   3. online softmax in FP32.  Each score enters float32 exactly (see
+//      ScoreConv): at d = 64 by one conversion per score; at d = 128, where
+//      the matrix pipe has room and the vector ALU does not, on the matrix
+//      pipe: the accumulator is seeded with a float32 bit pattern, so a tile
+//      read as float32 is an exact affine image of the integer scores, and
+//      one v_mfma_f32_16x16x1_4b_f32 per tile removes the offset from all 16
+//      values of a lane at once, exactly.
 //      Block maximum m = f32(max acc * c) per K-scale group (on the integer
 //      patterns, which order like the scores), and
 //      P8 = e4m3(2^fmaf(acc, c, f32(log2(448) - m))), so the block's largest
@@ -56,11 +57,41 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyRescale = 8.0f;
-// The seed of the Q.K^T accumulator: 1.5 * 2^23 and its float32 bit pattern.
-// With |acc| < 2^22 (127^2 * 128 < 2^21), the pattern kSeedBits + acc is the
-// float32 kSeed + acc.
-constexpr float kSeed = 12582912.0f;
-constexpr int kSeedBits = 0x4B400000;
+
+// How the INT32 scores of a tile become float32, exactly, per head dimension.
+// Every ScoreConv<D> yields F = kF * acc for each integer score acc, with the
+// factor applied to the score factor instead (c' = kF^-1 * c, exact: kF is a
+// power of two up to sign), so F * c' = acc * c in every product.
+//  d = 64: no seed; F = f32(acc) by v_cvt_f32_i32 (kF = 1).  A masked score
+//          (INT32_MIN) becomes -2^31, which no real score reaches.
+//  d = 128: the accumulator is seeded with the pattern 0xCBC80000, the
+//          float32 -1.5625 * 2^24; with |acc| < 2^21 (127^2 * 128 < 2^21) the
+//          pattern + acc stays in that binade and reads as the float32
+//          -(1.5625 * 2^24) - 2 acc.  v_mfma_f32_16x16x1_4b_f32 with A = B =
+//          5120 (5120^2 = 1.5625 * 2^24, one register for both operands)
+//          adds the constant back to all 16 values of a lane: F = -2 acc,
+//          exact, the two terms sharing their binade (kF = -2).  A masked
+//          score (INT32_MIN, read as -0.0) becomes +1.5625 * 2^24.
+//  The integer patterns order like the scores in both cases, so the row
+//  maximum is taken on them.
+template <int D> struct ScoreConv;
+template <> struct ScoreConv<64> {
+    static constexpr int kSeedBits = 0;
+    static constexpr float kInvF = 1.0f;           // c' = kInvF * c
+    static constexpr float kMasked = -2147483648.0f;
+    static __device__ __forceinline__ v16f to_f32(const v16i& s) { return __builtin_convertvector(s, v16f); }
+    static __device__ __forceinline__ float max_to_f32(int m) { return (float)m; }
+};
+template <> struct ScoreConv<128> {
+    static constexpr int kSeedBits = (int)0xCBC80000u;
+    static constexpr float kSeed = 26214400.0f;    // 5120^2 = -(the seed's value)
+    static constexpr float kInvF = -0.5f;
+    static constexpr float kMasked = 26214400.0f;
+    static __device__ __forceinline__ v16f to_f32(const v16i& s) {
+        return __builtin_amdgcn_mfma_f32_16x16x1f32(5120.0f, 5120.0f, __builtin_bit_cast(v16f, s), 0, 0, 0);
+    }
+    static __device__ __forceinline__ float max_to_f32(int m) { return __builtin_bit_cast(float, m) + kSeed; }
+};
 
 // XOR swizzle of the 16-byte chunks of one K-tile row (d bytes long): the 16
 // lanes of one LDS read phase (16 consecutive rows, same chunk) land on 16
@@ -190,9 +221,7 @@ __device__ inline int max_across_halves(int x) {
 
 // S^T = K Q^T of one key block for one wave (32 query rows), INT32, on
 // v_mfma_i32_32x32x32_i8.  Tile t, element v: key 32t + 8(v/4) + 4h + v%4.
-// The accumulator is seeded with the bit pattern of 1.5*2^23, so each result
-// read as a float32 is exactly 1.5*2^23 + acc (|acc| < 2^22); the patterns
-// order like the integer scores.
+// The accumulator starts from ScoreConv<D>::kSeedBits.
 template <int D>
 __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, const v4i (&qf)[D / 32],
                                              int h, int r32, v16i (&S)[4]) {
@@ -202,7 +231,7 @@ __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, con
         const int kr = 32 * t + r32;
         v16i acc;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = kSeedBits;
+        for (int v = 0; v < 16; ++v) acc[v] = ScoreConv<D>::kSeedBits;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const v4i kf = *reinterpret_cast<const v4i*>(lk + kr * D + (((2 * ks + h) ^ kswz<D>(kr)) << 4));
@@ -210,16 +239,6 @@ __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, con
         }
         S[t] = acc;
     }
-}
-
-// The exact float32 values of a tile of seeded scores: every output element
-// of v_mfma_f32_16x16x1_4b_f32 is C + A*B with A = 1 and B = -1.5*2^23 in
-// every lane, so each of the lane's 16 values becomes (1.5*2^23 + acc) -
-// 1.5*2^23 = acc, exact (the two terms share their exponent).  A masked score
-// (pattern INT32_MIN, read as -0.0) becomes -1.5*2^23, which no real score
-// reaches.
-__device__ __forceinline__ v16f scores_to_f32(const v16i& s) {
-    return __builtin_amdgcn_mfma_f32_16x16x1f32(1.0f, -kSeed, __builtin_bit_cast(v16f, s), 0, 0, 0);
 }
 
 // The rest of one key block for one wave, from its scores S: masking, online
@@ -238,6 +257,10 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
                                                  float& lsum, v16f (&O)[D / 32]) {
     constexpr int CT = D / 32;
     constexpr int TPG = 4 / KSPLIT;  // tiles per scale group
+    typedef ScoreConv<D> SC;
+    float cf[KSPLIT];  // the factors of the converted scores F (F * cf = acc * c)
+#pragma unroll
+    for (int g = 0; g < KSPLIT; ++g) cf[g] = c[g] * SC::kInvF;
 
     // ---- block maxima, one per K-scale group
     if (MASKED) {
@@ -260,17 +283,16 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
 #pragma unroll
             for (int v = (tt == 0 ? 1 : 0); v < 16; ++v) M = max(M, S[g * TPG + tt][v]);
         M = max_across_halves(M);
-        // f32(acc_max * c): the pattern read as float32, less the seed
-        // (exact), times c, one rounding -- the largest f32(acc * c) of the
+        // f32(acc_max * c), one rounding: the largest f32(acc * c) of the
         // group, since c >= 0
-        float m = (__builtin_bit_cast(float, M) - kSeed) * c[g];
+        float m = SC::max_to_f32(M) * cf[g];
         if (MASKED && M == INT32_MIN) m = -INFINITY;
         mt = fmaxf(mt, m);
     }
-    // the scores as float32, on the matrix pipe (see scores_to_f32)
+    // the scores as float32 (see ScoreConv)
     v16f F[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) F[t] = scores_to_f32(S[t]);
+    for (int t = 0; t < 4; ++t) F[t] = SC::to_f32(S[t]);
 
     // ---- lazy update of the reference maximum
     {
@@ -306,7 +328,7 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
         for (int s = 0; s < 8; ++s) {
             if (pass == 0) {
                 const int t = s >> 1, base = 8 * (s & 1);
-                const float ct = c[t / TPG];
+                const float ct = cf[t / TPG];
                 v4i quad;
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
@@ -315,7 +337,7 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
                     for (int i = 0; i < 4; ++i) {
                         const int v = base + 4 * g + i;
                         y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[t][v], ct, bias));
-                        if (MASKED && F[t][v] == -kSeed) y[i] = 0.0f;
+                        if (MASKED && F[t][v] == SC::kMasked) y[i] = 0.0f;
                     }
                     if (PV16) {
                         // round to nearest even, two values per conversion
