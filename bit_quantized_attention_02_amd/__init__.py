@@ -45,13 +45,14 @@ class sage_qkv_quant(ctypes.Structure):
                 ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v16", "v_scale", "v_inv",
                  "k_part", "v_part", "sync")] + [("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32),
                                                  ("pv_format", ctypes.c_int32), ("qk_bits", ctypes.c_int32),
-                                                 ("tail_part", ctypes.c_void_p), ("tail_rows", ctypes.c_int64)]
+                                                 ("tail_part", ctypes.c_void_p), ("tail_rows", ctypes.c_int64)] + \
+               [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "N", "d")]
 
 
 class sage_kv_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("k_i8", "k_scale", "k_mean", "v", "v_scale", "v_inv", "k_part", "v_part", "sync")] + \
-               [("k_block", ctypes.c_int32), ("pv_format", ctypes.c_int32)]
+               [(n, ctypes.c_int32) for n in ("k_block", "pv_format", "B", "Hkv", "Nk", "d")]
 
 
 class sage_options(ctypes.Structure):

@@ -450,8 +450,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     constexpr size_t lds = decode_lds<D, PV16>();
     if (a.nchunk > kMaxChunks) return hipErrorInvalidValue;  // not reached: see decode_plan
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_decode<In, D, KSPLIT, CAUSAL, PV16>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        static LaunchFacts facts;
+        int slots = 0;
+        hipError_t e = facts.settle((const void*)attn_decode<In, D, KSPLIT, CAUSAL, PV16>, 64, lds, &slots);
         if (e != hipSuccess) return e;
     }
     const long long grid = (long long)a.B * a.Hkv * a.nchunk * a.row_tiles;

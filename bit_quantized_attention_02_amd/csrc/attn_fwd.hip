@@ -326,9 +326,11 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WPS = attn_waves_per_simd<D, KSPLIT, CAUSAL>();
     constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
     a.nqt = a.Np / (32 * WAVES);
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const void* fn = (const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>;
+    static LaunchFacts facts;
+    int slots = 0;
+    {
+        hipError_t e = facts.settle(fn, 64 * WAVES, lds, &slots);
         if (e != hipSuccess) return e;
     }
     const int total = a.B * a.Hq * a.nqt;
@@ -338,45 +340,34 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     // equally long) are split along the keys over the otherwise idle slots.
     a.tiles_main = total;
     a.tail_split = 1;
-    if (!CAUSAL && a.part_o != nullptr) {
-        int dev = 0, cus = 0, per_cu = 0;
-        const bool known =
-            hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, (const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>, 64 * WAVES,
-                lds) == hipSuccess;
-        if (!known) (void)hipGetLastError();  // a failed query only means no split
-        if (known) {
-            const int slots = cus * per_cu;
-            const int nkb = (a.N + SAGE_BN - 1) / SAGE_BN;
-            const int tail = slots > 0 && total > slots ? total % slots : 0;
-            if (tail > 0) {
-                // The leftover tiles as `split` shares each run in
-                // ceil(tail * split / slots) waves of 1/split of a tile's
-                // time: take the split with the shortest, if it beats the
-                // whole tiles' one wave, within the partials' room.
-                int best = 1;
-                long long best_num = 1, best_den = 1;  // time as a fraction of a tile's
-                for (int split = 2; split <= kMaxTailSplit && split <= nkb; ++split) {
-                    if ((long long)tail * split * ROWS > a.tail_rows) break;
-                    const long long waves = ((long long)tail * split + slots - 1) / slots;
-                    if (waves * best_den < best_num * split) {
-                        best = split;
-                        best_num = waves;
-                        best_den = split;
-                    }
+    if (!CAUSAL && a.part_o != nullptr && slots > 0) {
+        const int nkb = (a.N + SAGE_BN - 1) / SAGE_BN;
+        const int tail = total > slots ? total % slots : 0;
+        if (tail > 0) {
+            // The leftover tiles as `split` shares each run in
+            // ceil(tail * split / slots) waves of 1/split of a tile's
+            // time: take the split with the shortest, if it beats the
+            // whole tiles' one wave, within the partials' room.
+            int best = 1;
+            long long best_num = 1, best_den = 1;  // time as a fraction of a tile's
+            for (int split = 2; split <= kMaxTailSplit && split <= nkb; ++split) {
+                if ((long long)tail * split * ROWS > a.tail_rows) break;
+                const long long waves = ((long long)tail * split + slots - 1) / slots;
+                if (waves * best_den < best_num * split) {
+                    best = split;
+                    best_num = waves;
+                    best_den = split;
                 }
-                if (best > 1) {
-                    a.tiles_main = total - tail;
-                    a.tail_split = best;
-                }
+            }
+            if (best > 1) {
+                a.tiles_main = total - tail;
+                a.tail_split = best;
             }
         }
     }
     const int grid = a.tiles_main + (total - a.tiles_main) * a.tail_split;
-    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>), dim3(grid),
-                       dim3(64 * WAVES), lds, st, a);
+    hipLaunchKernelGGL((attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>), dim3(grid), dim3(64 * WAVES), lds,
+                       st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.tail_split == 1) return e;
     const long long threads = (long long)(total - a.tiles_main) * ROWS * (D / 4);

@@ -20,6 +20,43 @@ int prep_sync_words(const Shape& s);
 
 using sage::Shape;
 
+#include <mutex>
+
+// Serialises the first launch of a kernel on a device; later launches read
+// the settled facts without locking.
+static std::mutex g_launch_facts_mu;
+
+hipError_t sage::LaunchFacts::settle(const void* fn, int threads, size_t lds, int* slots_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices && ready[dev].load(std::memory_order_acquire)) {
+        *slots_out = slots[dev];
+        return hipSuccess;
+    }
+    std::lock_guard<std::mutex> lock(g_launch_facts_mu);
+    if (dev >= 0 && dev < kMaxDevices && ready[dev].load(std::memory_order_relaxed)) {
+        *slots_out = slots[dev];
+        return hipSuccess;
+    }
+    if (lds > 65536) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    int cus = 0, per_cu = 0;
+    const bool known =
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) == hipSuccess;
+    if (!known) (void)hipGetLastError();  // an unknown count only means "no split"
+    const int n = known ? cus * per_cu : 0;
+    *slots_out = n;
+    if (dev >= 0 && dev < kMaxDevices) {
+        slots[dev] = n;
+        ready[dev].store(1, std::memory_order_release);
+    }
+    return hipSuccess;
+}
+
 static int check_shape(int B, int Hq, int Hkv, int N, int d) {
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return SAGE_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
@@ -92,8 +129,9 @@ static bool k_block_ok(int k_block) { return k_block == SAGE_BK || k_block == SA
 // Bytes per V element of a KV cache: E4M3 codes, or binary16.
 static size_t cache_v_bytes(int pv_format) { return pv_format == SAGE_PV_F16 ? 2 : 1; }
 
-static int check_cache(const sage_kv_cache* z) {
+static int check_cache(const sage_kv_cache* z, int B, int Hkv, int Nk, int d) {
     if (!z) return SAGE_ERR_INVALID_ARG;
+    if (z->B != B || z->Hkv != Hkv || z->Nk != Nk || z->d != d) return SAGE_ERR_INVALID_ARG;
     if (!k_block_ok(z->k_block) || !pv_format_ok(z->pv_format)) return SAGE_ERR_UNSUPPORTED;
     if (!z->k_i8 || !z->k_scale || !z->k_mean || !z->v || !z->v_scale || !z->v_inv || !z->k_part ||
         !z->v_part || !z->sync)
@@ -135,8 +173,11 @@ static DecodeLayout decode_layout(int B, int Hq, int Hkv, int Nq, int Nk, int d)
     return L;
 }
 
-static int check_quant(const sage_qkv_quant* z) {
+// The views are read and written by the sizes a call is passed: they must be
+// the sizes the struct was carved for.
+static int check_quant(const sage_qkv_quant* z, int B, int Hq, int Hkv, int N, int d) {
     if (!z) return SAGE_ERR_INVALID_ARG;
+    if (z->B != B || z->Hq != Hq || z->Hkv != Hkv || z->N != N || z->d != d) return SAGE_ERR_INVALID_ARG;
     if (!granularity_ok(z->q_block, z->k_block) || !pv_format_ok(z->pv_format) ||
         !qk_bits_ok(z->qk_bits))
         return SAGE_ERR_UNSUPPORTED;
@@ -183,6 +224,11 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     out->k_block = SAGE_BK;
     out->pv_format = SAGE_PV_E4M3;
     out->qk_bits = SAGE_QK_INT8;
+    out->B = B;
+    out->Hq = Hq;
+    out->Hkv = Hkv;
+    out->N = N;
+    out->d = d;
     return SAGE_OK;
 }
 
@@ -193,7 +239,7 @@ int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B,
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
     if (!q || !k || !v || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
         return SAGE_ERR_INVALID_ARG;
-    rc = check_quant(dst);
+    rc = check_quant(dst, B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
     const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
     hipError_t e = sage::launch_prep(q, k, v, dtype, s, dst, (hipStream_t)stream);
@@ -207,7 +253,7 @@ int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq
     if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
     if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
     if (!out || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
-    rc = check_quant(src);
+    rc = check_quant(src, B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
     const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
     // the exponent factor and log2 of the P block maximum's code (448 for
@@ -288,6 +334,10 @@ int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, 
     out->sync = (int32_t*)(base + L.sync);
     out->k_block = k_block;
     out->pv_format = pv_format;
+    out->B = B;
+    out->Hkv = Hkv;
+    out->Nk = Nk;
+    out->d = d;
     return SAGE_OK;
 }
 
@@ -297,7 +347,7 @@ int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, in
     if (rc != SAGE_OK) return rc;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
     if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return SAGE_ERR_INVALID_ARG;
-    rc = check_cache(cache);
+    rc = check_cache(cache, B, Hkv, Nk, d);
     if (rc != SAGE_OK) return rc;
     const Shape s = sage::make_shape(B, Hkv, Hkv, Nk, d);
     const sage::KVViews kv = {cache->k_i8,   cache->k_scale, cache->k_mean, cache->v,
@@ -324,7 +374,7 @@ int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float
     if (causal && Nq > Nk) return SAGE_ERR_INVALID_ARG;
     if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
-    rc = check_cache(cache);
+    rc = check_cache(cache, B, Hkv, Nk, d);
     if (rc != SAGE_OK) return rc;
     const DecodeLayout L = decode_layout(B, Hq, Hkv, Nq, Nk, d);
     if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return SAGE_ERR_WORKSPACE;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/sage.h"
 
 namespace sage {
@@ -70,6 +72,19 @@ __host__ __device__ inline int v_key_position(int j) {
     const int a = (j >> 2) & 3;
     return (j & ~15) | ((((a & 1) << 1) | (a >> 1)) << 2) | (j & 3);
 }
+
+// Launch facts of one kernel on one device, settled once per (kernel, device)
+// and read on every later launch without a driver call: the dynamic-LDS limit
+// raised where a kernel needs more than 64 KB, and the number of its
+// work-groups the device holds at once (CU count times resident work-groups
+// per CU; 0 if the runtime cannot say).  `fn` is the kernel's host stub; each
+// kernel instantiation passes its own LaunchFacts object.
+struct LaunchFacts {
+    static constexpr int kMaxDevices = 64;
+    std::atomic<int> ready[kMaxDevices];
+    int slots[kMaxDevices];
+    hipError_t settle(const void* fn, int threads, size_t lds, int* slots_out);
+};
 
 // ---------------------------------------------------------------- device
 #if defined(__HIPCC__)

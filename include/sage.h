@@ -156,6 +156,9 @@ typedef struct {
     int32_t qk_bits;   /* SAGE_QK_INT8 (set by sage_workspace_carve) or SAGE_QK_INT4; likewise */
     float* tail_part;   /* may be NULL */
     int64_t tail_rows;  /* rows of tail_part (0 with NULL) */
+    int32_t B, Hq, Hkv, N, d; /* the shape the views were carved for (set by
+                                 sage_workspace_carve); the quantize and attention
+                                 calls return SAGE_ERR_INVALID_ARG for other sizes */
 } sage_qkv_quant;
 
 /* Method options of sage_attn_fwd_ex. */
@@ -195,14 +198,24 @@ int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B,
  * Attention on already-quantized operands: out = softmax(Q K^T sm_scale) V as
  * the method computes it, FP32 output [B, Hq, N, d].  causal = 1 applies the
  * square, top-left aligned mask j <= i.  sm_scale must be finite and > 0.
- * `src` must have been carved for these B, Hq, Hkv, N, d and filled by
- * sage_quantize: its buffers are read by these sizes, which the struct does
- * not record.
+ * `src` must have been carved for these B, Hq, Hkv, N, d (checked against the
+ * shape it records: SAGE_ERR_INVALID_ARG otherwise) and filled by
+ * sage_quantize.
  */
 int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq, int Hkv, int N,
                             int d, int causal, float sm_scale, void* stream);
 
-/* Both steps: sage_quantize into `workspace`, then sage_attn_fwd_quantized. */
+/*
+ * The whole forward pass in one call: sage_quantize into `workspace`, then
+ * sage_attn_fwd_quantized.  This is the operator that replaces a model's
+ * native attention (the SageAttention article presents the method as a
+ * plug-and-play replacement needing no retraining; the Berkeley brief's
+ * experiment steps, "落地实验标准步骤", begin by swapping the attention
+ * kernel): it takes the native operator's operands -- fp16/bf16 Q, K, V in
+ * [B, H, N, d], the causal flag and the softmax scale -- and returns its
+ * output, in FP32.  The caller supplies the device workspace
+ * (sage_workspace_bytes) so that the call never allocates.
+ */
 int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                   int N, int d, int causal, float sm_scale, int dtype, void* workspace,
                   size_t ws_bytes, void* stream);
@@ -258,6 +271,10 @@ typedef struct {
     int32_t* sync;
     int32_t k_block;   /* SAGE_BK or SAGE_BK_THREAD */
     int32_t pv_format; /* SAGE_PV_E4M3 or SAGE_PV_F16 */
+    int32_t B, Hkv, Nk, d; /* the shape the cache was carved for (set by
+                              sage_kv_cache_carve); sage_kv_quantize and
+                              sage_attn_decode return SAGE_ERR_INVALID_ARG for
+                              other sizes */
 } sage_kv_cache;
 
 /* Bytes of a KV cache for [B, Hkv, Nk, d] in this P.V format (0 when the
@@ -293,7 +310,7 @@ size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d
  * sum, unnormalised output; a third FP32 accumulation level) are merged by a
  * second kernel in `workspace` (device memory, 256-byte aligned) when there is
  * more than one chunk.  `cache` must have been carved and quantized for these
- * B, Hkv, Nk, d: it is read by these sizes, which the struct does not record.
+ * B, Hkv, Nk, d (checked against the shape it records).
  */
 int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
                      int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,

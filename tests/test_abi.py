@@ -312,6 +312,37 @@ def test_kv_cache_and_decode_entry_points_validate_on_the_host(sage):
     assert dec(c=ctypes.byref(bad2)) == sage.SAGE_ERR_UNSUPPORTED
 
 
+def test_carved_structs_record_their_shape_and_calls_check_it(sage):
+    """A workspace or cache carved for one shape is refused, before any HIP
+    call, by a call passed another: every view is read and written by the
+    sizes passed, so a mismatch would reach past the carved buffers."""
+    L = sage._lib
+    fake = 1 << 40
+    f = ctypes.c_float
+    shape = (2, 4, 2, 300, 64)
+    rc, z = _carve(sage, fake, sage.sage_workspace_bytes(*shape), shape)
+    assert rc == 0 and (z.B, z.Hq, z.Hkv, z.N, z.d) == shape
+    zp = ctypes.byref(z)
+    for other in ((1, 4, 2, 300, 64), (2, 8, 2, 300, 64), (2, 4, 1, 300, 64), (2, 4, 2, 301, 64),
+                  (2, 4, 2, 300, 128)):
+        assert L.sage_quantize(fake, fake, fake, 0, *other, zp, None) == sage.SAGE_ERR_INVALID_ARG, other
+        assert L.sage_attn_fwd_quantized(zp, fake, *other, 0, f(0.125), None) == sage.SAGE_ERR_INVALID_ARG, other
+    c = sage.sage_kv_cache_carve(fake, sage.sage_kv_cache_bytes(2, 2, 300, 64), 2, 2, 300, 64)
+    assert (c.B, c.Hkv, c.Nk, c.d) == (2, 2, 300, 64)
+    cp = ctypes.byref(c)
+    wsb = sage.sage_decode_workspace_bytes(2, 8, 2, 1, 300, 64)
+    for B, Hkv, Nk, d in ((1, 2, 300, 64), (2, 1, 300, 64), (2, 2, 299, 64), (2, 2, 300, 128)):
+        assert L.sage_kv_quantize(fake, fake, 0, B, Hkv, Nk, d, cp, None) == sage.SAGE_ERR_INVALID_ARG
+        Hq = 4 * Hkv
+        n = sage.sage_decode_workspace_bytes(B, Hq, Hkv, 1, Nk, d)
+        assert L.sage_attn_decode(fake, 0, cp, fake, B, Hq, Hkv, 1, Nk, d, 1, f(0.125), fake, n,
+                                  None) == sage.SAGE_ERR_INVALID_ARG
+    # the struct's own shape is accepted up to the first HIP call: a short
+    # workspace is the first error found
+    assert L.sage_attn_decode(fake, 0, cp, fake, 2, 8, 2, 1, 300, 64, 1, f(0.125), fake, wsb - 1,
+                              None) == sage.SAGE_ERR_WORKSPACE
+
+
 def test_binding_rejects_tensors_the_sizes_do_not_describe(sage):
     """The C calls take B, Hq, Hkv, N, d from Q and K alone; the binding
     refuses a V, output, cache query or workspace that those sizes do not
