@@ -364,9 +364,10 @@ size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d
     return decode_layout(B, Hq, Hkv, Nq, Nk, d).total;
 }
 
-int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
-                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
-                     void* workspace, size_t ws_bytes, void* stream) {
+// Validation shared by the two decode entry points (host only, no HIP call).
+static int check_decode_call(const void* q, int dtype, const sage_kv_cache* cache, const float* out,
+                             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                             float sm_scale) {
     int rc = check_decode_shape(B, Hq, Hkv, Nq, Nk, d);
     if (rc != SAGE_OK) return rc;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
@@ -374,16 +375,28 @@ int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float
     if (causal && Nq > Nk) return SAGE_ERR_INVALID_ARG;
     if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
-    rc = check_cache(cache, B, Hkv, Nk, d);
+    return check_cache(cache, B, Hkv, Nk, d);
+}
+
+static hipError_t run_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out,
+                             char* base, const DecodeLayout& L, int B, int Hq, int Hkv, int Nq,
+                             int Nk, int d, int causal, float sm_scale, void* stream) {
+    const float qk = (float)((double)sm_scale * 1.4426950408889634);
+    const float l448 = cache->pv_format == SAGE_PV_F16 ? 0.0f : (float)log2(448.0);
+    return sage::launch_decode(q, dtype, cache, out, (float*)(base + L.part_o),
+                               (float*)(base + L.part_ml), B, Hq, Hkv, Nq, Nk, d, causal, qk, l448,
+                               (hipStream_t)stream);
+}
+
+int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_decode_call(q, dtype, cache, out, B, Hq, Hkv, Nq, Nk, d, causal, sm_scale);
     if (rc != SAGE_OK) return rc;
     const DecodeLayout L = decode_layout(B, Hq, Hkv, Nq, Nk, d);
     if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return SAGE_ERR_WORKSPACE;
-    const float qk = (float)((double)sm_scale * 1.4426950408889634);
-    const float l448 = cache->pv_format == SAGE_PV_F16 ? 0.0f : (float)log2(448.0);
-    char* base = (char*)workspace;
-    hipError_t e = sage::launch_decode(q, dtype, cache, out, (float*)(base + L.part_o),
-                                       (float*)(base + L.part_ml), B, Hq, Hkv, Nq, Nk, d, causal, qk,
-                                       l448, (hipStream_t)stream);
+    hipError_t e = run_decode(q, dtype, cache, out, (char*)workspace, L, B, Hq, Hkv, Nq, Nk, d, causal,
+                              sm_scale, stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
