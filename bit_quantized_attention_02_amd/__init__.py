@@ -26,6 +26,7 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ER
 SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_BQ, SAGE_BK, SAGE_BN, SAGE_NPAD = 128, 64, 128, 256
 SAGE_MAX_N = 1 << 20  # longest sequence (N, Nk, Nq) the library accepts
+SAGE_DECODE_SCRATCH_BYTES = 17039360  # the library's own decode scratch, per GPU
 SAGE_BQ_THREAD, SAGE_BK_THREAD = 1, 32
 SAGE_PV_E4M3, SAGE_PV_F16 = 0, 1
 SAGE_QK_INT8, SAGE_QK_INT4 = 8, 4
@@ -80,6 +81,8 @@ _lib.sage_decode_workspace_bytes.restype = _S
 _lib.sage_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.sage_attn_decode.argtypes = [_P, _I, ctypes.POINTER(sage_kv_cache), _P, _I, _I, _I, _I, _I, _I,
                                   _I, _F, _P, _S, _P]
+_lib.sage_attn_decode_noalloc.argtypes = [_P, _I, ctypes.POINTER(sage_kv_cache), _P, _I, _I, _I, _I, _I,
+                                          _I, _I, _F, _P]
 _lib.sage_get_config.argtypes = [ctypes.POINTER(sage_config)]
 _lib.sage_v_key_position.argtypes = [_I]
 _lib.sage_status_string.restype = ctypes.c_char_p
@@ -88,7 +91,7 @@ _lib.sage_status_string.argtypes = [_I]
 EXPORTED = ["sage_workspace_bytes", "sage_workspace_carve", "sage_quantize",
             "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_attn_fwd_granular", "sage_attn_fwd_ex",
             "sage_kv_cache_bytes", "sage_kv_cache_carve", "sage_kv_quantize",
-            "sage_decode_workspace_bytes", "sage_attn_decode", "sage_get_config",
+            "sage_decode_workspace_bytes", "sage_attn_decode", "sage_attn_decode_noalloc", "sage_get_config",
             "sage_v_key_position", "sage_status_string"]
 
 
@@ -279,6 +282,20 @@ def sage_attn_decode(q: torch.Tensor, cache: sage_kv_cache, out: torch.Tensor, H
     _check(_lib.sage_attn_decode(_ptr(q), _dtype_code(q), ctypes.byref(cache), _ptr(out), B, Hq, Hkv,
                                  Nq, Nk, d, int(causal), float(sm_scale), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sage_attn_decode_noalloc(q: torch.Tensor, cache: sage_kv_cache, out: torch.Tensor, Hkv: int, Nk: int,
+                             causal: bool, sm_scale: float, stream=None) -> None:
+    """sage_attn_decode without a workspace: the library's own per-GPU
+    scratch holds the key split's partials (no allocation; calls that overlap
+    on one GPU race)."""
+    if q.dim() != 4:
+        raise ValueError("Q must be 4-D [B, Hq, Nq, d]")
+    _check_out(q, out, q.shape)
+    _check_device(q, q)
+    B, Hq, Nq, d = q.shape
+    _check(_lib.sage_attn_decode_noalloc(_ptr(q), _dtype_code(q), ctypes.byref(cache), _ptr(out), B, Hq,
+                                         Hkv, Nq, Nk, d, int(causal), float(sm_scale), _stream(stream)))
 
 
 # ------------------------------------------------------------------ helpers

@@ -364,6 +364,36 @@ size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d
     return decode_layout(B, Hq, Hkv, Nq, Nk, d).total;
 }
 
+// ---- The scratch of sage_attn_decode_noalloc: the decode key split's
+// per-chunk partials (part_o then part_ml, as in a decode workspace) in a
+// file-scope device array, one copy per GPU.  Its host-side name is only a
+// stand-in; the device address of each GPU's copy is looked up once, with that
+// device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SAGE_DECODE_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static std::atomic<void*> g_scratch_ptr[sage::LaunchFacts::kMaxDevices];
+
+static int scratch_of_current_device(char** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_HIP;
+    if (dev < 0 || dev >= sage::LaunchFacts::kMaxDevices) return SAGE_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return SAGE_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = (char*)p;
+    return SAGE_OK;
+}
+
 // Validation shared by the two decode entry points (host only, no HIP call).
 static int check_decode_call(const void* q, int dtype, const sage_kv_cache* cache, const float* out,
                              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
@@ -397,6 +427,21 @@ int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float
     if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return SAGE_ERR_WORKSPACE;
     hipError_t e = run_decode(q, dtype, cache, out, (char*)workspace, L, B, Hq, Hkv, Nq, Nk, d, causal,
                               sm_scale, stream);
+    return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_attn_decode_noalloc(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
+                             int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
+                             void* stream) {
+    int rc = check_decode_call(q, dtype, cache, out, B, Hq, Hkv, Nq, Nk, d, causal, sm_scale);
+    if (rc != SAGE_OK) return rc;
+    const DecodeLayout L = decode_layout(B, Hq, Hkv, Nq, Nk, d);
+    if (L.total > (size_t)SAGE_DECODE_SCRATCH_BYTES) return SAGE_ERR_WORKSPACE;
+    char* base = nullptr;
+    rc = scratch_of_current_device(&base);
+    if (rc != SAGE_OK) return rc;
+    hipError_t e = run_decode(q, dtype, cache, out, base, L, B, Hq, Hkv, Nq, Nk, d, causal, sm_scale,
+                              stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

@@ -316,6 +316,26 @@ int sage_attn_decode(const void* q, int dtype, const sage_kv_cache* cache, float
                      int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * sage_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, runtimes that forbid hipMalloc.  The
+ * same arguments without the workspace: the per-chunk partials of the key
+ * split go to a scratch array the library itself holds in device memory, one
+ * copy per GPU, SAGE_DECODE_SCRATCH_BYTES long, kept until the process ends.
+ * The call allocates nothing (the first call on a device looks the array's
+ * address up, once).  Every shape sage_attn_decode accepts fits the array
+ * (the key split never makes more than 32 x 1024 row-chunk partials); a shape
+ * that would not returns SAGE_ERR_WORKSPACE.  Results equal sage_attn_decode's
+ * bit for bit (same kernels, same partial layout).
+ * All calls on one GPU share its array: calls that overlap on one GPU (two
+ * streams, or two host threads without ordering) race and give undefined
+ * output; serialize them (one stream, or events).
+ */
+#define SAGE_DECODE_SCRATCH_BYTES 17039360 /* 32 * 1024 * (128 + 2) floats, 256-byte regions */
+int sage_attn_decode_noalloc(const void* q, int dtype, const sage_kv_cache* cache, float* out, int B,
+                             int Hq, int Hkv, int Nq, int Nk, int d, int causal, float sm_scale,
+                             void* stream);
+
 /* Block sizes and format constants the library was compiled with. */
 int sage_get_config(sage_config* c);
 

@@ -343,6 +343,42 @@ def test_carved_structs_record_their_shape_and_calls_check_it(sage):
                               None) == sage.SAGE_ERR_WORKSPACE
 
 
+def test_noalloc_decode_scratch_holds_every_split_and_validates_on_the_host(sage):
+    """The library's own decode scratch (SAGE_DECODE_SCRATCH_BYTES) holds the
+    partials of every key split the decode plan makes: swept over batch,
+    heads, query rows, cached keys and d, no decode workspace is larger.  Bad
+    arguments are refused before any HIP call, as for sage_attn_decode."""
+    worst = 0
+    for B in (1, 2, 3, 8, 64):
+        for Hkv, G in ((1, 1), (1, 8), (2, 4), (8, 4), (8, 16), (32, 1)):
+            for Nq in (1, 2, 7, 16, 33, 100):
+                for Nk in (Nq, 128, 300, 4096, 32768, 1 << 20):
+                    if Nk < Nq:
+                        continue
+                    for d in (64, 128):
+                        n = sage.sage_decode_workspace_bytes(B, Hkv * G, Hkv, Nq, Nk, d)
+                        assert 0 < n <= sage.SAGE_DECODE_SCRATCH_BYTES, (B, Hkv * G, Hkv, Nq, Nk, d, n)
+                        worst = max(worst, n)
+    assert worst > sage.SAGE_DECODE_SCRATCH_BYTES // 2
+    L = sage._lib
+    fake = 1 << 40
+    f = ctypes.c_float
+    c = sage.sage_kv_cache_carve(fake, sage.sage_kv_cache_bytes(1, 2, 300, 64), 1, 2, 300, 64)
+    cp = ctypes.byref(c)
+
+    def dec(q=fake, dt=0, cc=cp, out=fake, B=1, Hq=8, Hkv=2, Nq=1, Nk=300, d=64, causal=1, sm=0.125):
+        return L.sage_attn_decode_noalloc(q, dt, cc, out, B, Hq, Hkv, Nq, Nk, d, causal, f(sm), None)
+
+    assert dec(q=None) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(out=fake + 4) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(cc=None) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(dt=2) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(Nq=301) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(sm=float("nan")) == sage.SAGE_ERR_INVALID_ARG
+    assert dec(B=2) == sage.SAGE_ERR_INVALID_ARG  # not the cache's shape
+    assert dec(Hq=7) == sage.SAGE_ERR_UNSUPPORTED
+
+
 def test_binding_rejects_tensors_the_sizes_do_not_describe(sage):
     """The C calls take B, Hq, Hkv, N, d from Q and K alone; the binding
     refuses a V, output, cache query or workspace that those sizes do not
