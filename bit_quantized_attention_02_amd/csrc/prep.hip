@@ -299,13 +299,52 @@ __device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* 
         s_last = __hip_atomic_fetch_add(cnt + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                  nchunk - 1;
     __syncthreads();
-    if (!s_last || tid >= D) return;
+    if (!s_last) return;  // (uniform over the work-group)
+    // The reduction over the head's chunks: LPC lanes per channel, each
+    // loading every LPC-th chunk's partials with its loads in flight
+    // together, then a fixed-order combination of the lanes through LDS.
+    // (The float64 sums of 16-bit inputs are exact here, as above, so the
+    // grouping does not change the result.)
+    constexpr int LPC = kThreads / D;
+    static_assert(LPC <= StatsSmem<D>::RPI, "the lanes' sums fit the stats buffers");
+    {
+        const int ch = tid % D, lane = tid / D;
+        double t = 0.0;
+        float m = 0.0f;
+        constexpr int U = 8;
+        const long long base = (long long)bg * nchunk * D + ch;
+        int c = lane;
+        for (; c + (U - 1) * LPC < nchunk; c += U * LPC) {
+            double pk[U];
+            float pv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                pk[u] = __hip_atomic_load(k_part + base + (long long)(c + u * LPC) * D, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                pv[u] = __hip_atomic_load(v_part + base + (long long)(c + u * LPC) * D, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                t += pk[u];
+                m = fmaxf(m, pv[u]);
+            }
+        }
+        for (; c < nchunk; c += LPC) {
+            t += __hip_atomic_load(k_part + base + (long long)c * D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            m = fmaxf(m, __hip_atomic_load(v_part + base + (long long)c * D, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+        }
+        ssum[lane][ch] = t;
+        smax[lane][ch] = m;
+    }
+    __syncthreads();
+    if (tid >= D) return;
     double t = 0.0;
     float m = 0.0f;
-    for (int c = 0; c < nchunk; ++c) {
-        const long long o = ((long long)bg * nchunk + c) * D + tid;
-        t += __hip_atomic_load(k_part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        m = fmaxf(m, __hip_atomic_load(v_part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    for (int l = 0; l < LPC; ++l) {
+        t += ssum[l][tid];
+        m = fmaxf(m, smax[l][tid]);
     }
     const long long o = (long long)bg * D + tid;
     k_mean[o] = (float)(t / (double)s.N);
