@@ -6,7 +6,7 @@ already resident in HBM: the prep kernels (K mean, smoothing, INT8 Q/K, FP8 V)
 followed by the fused attention kernel, i.e. one sage_attn_fwd call.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu]
-                    [--granularity block|thread] [--pv e4m3|f16]
+                    [--granularity block|thread|token] [--pv e4m3|f16]
 
 Prints one JSON line.  `value` is TOPS = 4*B*Hq*N^2*d / t (halved for causal)
 for the whole step; `roofline` prices the attention kernel alone (its average
@@ -37,8 +37,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=3,
                    help="1..5; 3 is the non-causal N=17550 video-diffusion shape")
-    p.add_argument("--granularity", choices=("block", "thread"), default="block",
-                   help="Q/K scale granularity: block (128 rows / 64 keys) or thread (per row / 32 keys)")
+    p.add_argument("--granularity", choices=("block", "thread", "token"), default="block",
+                   help="Q/K scale granularity: block (128 rows / 64 keys), thread (per row / 32 keys) or "
+                        "token (per row / per key; not for the decode cache)")
     p.add_argument("--pv", choices=("e4m3", "f16"), default="e4m3",
                    help="P.V format: e4m3 (FP8 P and V, the default) or f16 (binary16 P and V)")
     p.add_argument("--qk-bits", type=int, choices=(8, 4), default=8,

@@ -27,11 +27,12 @@ SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_BQ, SAGE_BK, SAGE_BN, SAGE_NPAD = 128, 64, 128, 256
 SAGE_MAX_N = 1 << 20  # longest sequence (N, Nk, Nq) the library accepts
 SAGE_DECODE_SCRATCH_BYTES = 17039360  # the library's own decode scratch, per GPU
-SAGE_BQ_THREAD, SAGE_BK_THREAD = 1, 32
+SAGE_BQ_THREAD, SAGE_BK_THREAD, SAGE_BK_TOKEN = 1, 32, 1
 SAGE_PV_E4M3, SAGE_PV_F16 = 0, 1
 SAGE_QK_INT8, SAGE_QK_INT4 = 8, 4
-# (q_block, k_block) of the two quantization granularities
-GRANULARITY = {"block": (SAGE_BQ, SAGE_BK), "thread": (SAGE_BQ_THREAD, SAGE_BK_THREAD)}
+# (q_block, k_block) of the quantization granularities
+GRANULARITY = {"block": (SAGE_BQ, SAGE_BK), "thread": (SAGE_BQ_THREAD, SAGE_BK_THREAD),
+               "token": (SAGE_BQ_THREAD, SAGE_BK_TOKEN)}
 # P.V formats: FP8 E4M3 P and V, or binary16 P and V (both accumulated in FP32)
 PV_FORMAT = {"e4m3": SAGE_PV_E4M3, "f16": SAGE_PV_F16}
 
@@ -321,8 +322,8 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
          granularity: str = "block", pv: str = "e4m3", qk_bits: int = 8) -> torch.Tensor:
     """Drop-in attention: [B,Hq,N,d] fp16/bf16 Q and [B,Hkv,N,d] K,V on the GPU
     -> FP32 [B,Hq,N,d], on the current stream.  granularity: "block" (one Q
-    scale per 128 rows, one K scale per 64 keys) or "thread" (per row, per 32
-    keys); pv: "e4m3" (FP8 P and V) or "f16" (binary16 P and V); qk_bits: 8
+    scale per 128 rows, one K scale per 64 keys), "thread" (per row, per 32
+    keys) or "token" (per row, per key); pv: "e4m3" (FP8 P and V) or "f16" (binary16 P and V); qk_bits: 8
     (INT8 Q, K) or 4 (INT4 values)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])

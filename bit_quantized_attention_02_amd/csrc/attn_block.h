@@ -74,6 +74,14 @@ constexpr float kLazyRescale = 8.0f;
 //          score (INT32_MIN, read as -0.0) becomes +1.5625 * 2^24.
 //  The integer patterns order like the scores in both cases, so the row
 //  maximum is taken on them.
+// Score factors passed to the block body: one per K-scale group (KSPLIT of
+// 2 or 4 per block), or, with one K scale per key (KSPLIT == SAGE_BN), the
+// row's Q scale and f32(sm_scale * log2 e), the keys' scales coming from LDS.
+template <int KSPLIT>
+constexpr int score_factors() {
+    return KSPLIT == SAGE_BN ? 2 : KSPLIT;
+}
+
 template <int D> struct ScoreConv;
 template <> struct ScoreConv<64> {
     static constexpr int kSeedBits = 0;
@@ -248,19 +256,35 @@ __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, con
 // E4M3 code bytes (a KV cache), converted to binary16 -- exactly -- as each
 // fragment is read.
 // KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
-// 32-key tile).  c[g] is the score factor f32(f32(s_q * s_k) * f32(sm_scale *
-// log2 e)) of scale group g; tile t belongs to group t / (4 / KSPLIT).
+// 32-key tile; SAGE_BN: one per key).  For 2 or 4, c[g] is the score factor
+// f32(f32(s_q * s_k) * f32(sm_scale * log2 e)) of scale group g; tile t
+// belongs to group t / (4 / KSPLIT).  For SAGE_BN, c = {s_q, f32(sm_scale *
+// log2 e)} and the block's 128 key scales are at lks in LDS; each key's
+// factor is formed as f32(f32(s_q * s_k) * c[1]) where it is needed.
 template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false>
 __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __restrict__ lv, int T,
-                                                 int row, int N, const float (&c)[KSPLIT], float l448,
-                                                 int h, int r32, const v8h& rsel, float& mref,
-                                                 float& lsum, v16f (&O)[D / 32]) {
+                                                 int row, int N, const float (&c)[score_factors<KSPLIT>()],
+                                                 float l448, int h, int r32, const v8h& rsel, float& mref,
+                                                 float& lsum, v16f (&O)[D / 32],
+                                                 const float* __restrict__ lks = nullptr) {
     constexpr int CT = D / 32;
-    constexpr int TPG = 4 / KSPLIT;  // tiles per scale group
+    constexpr bool PER_KEY = KSPLIT == SAGE_BN;
+    constexpr int NG = PER_KEY ? 1 : KSPLIT;  // scale groups held in registers
+    constexpr int TPG = 4 / NG;               // tiles per scale group
     typedef ScoreConv<D> SC;
-    float cf[KSPLIT];  // the factors of the converted scores F (F * cf = acc * c)
+    float cf[NG];  // the factors of the converted scores F (F * cf = acc * c)
+    if constexpr (!PER_KEY) {
 #pragma unroll
-    for (int g = 0; g < KSPLIT; ++g) cf[g] = c[g] * SC::kInvF;
+        for (int g = 0; g < KSPLIT; ++g) cf[g] = c[g] * SC::kInvF;
+    }
+    // per key: the factor of key 32t + 8i + 4h + j (element 4i + j of tile
+    // t), (s_q * s_k) * f32(sm_scale log2 e * kInvF), the last product exact
+    // up to the power of two kInvF
+    const float qkf = PER_KEY ? c[1] * SC::kInvF : 0.0f;
+    auto key_factor = [&](int t, int i, int j) -> float {
+        const v4f ks = *reinterpret_cast<const v4f*>(lks + 32 * t + 8 * i + 4 * h);
+        return (c[0] * ks[j]) * qkf;
+    };
 
     // ---- block maxima, one per K-scale group
     if (MASKED) {
@@ -275,24 +299,44 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
             }
     }
     float mt = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < KSPLIT; ++g) {
-        int M = S[g * TPG][0];
-#pragma unroll
-        for (int tt = 0; tt < TPG; ++tt)
-#pragma unroll
-            for (int v = (tt == 0 ? 1 : 0); v < 16; ++v) M = max(M, S[g * TPG + tt][v]);
-        M = max_across_halves(M);
-        // f32(acc_max * c), one rounding: the largest f32(acc * c) of the
-        // group, since c >= 0
-        float m = SC::max_to_f32(M) * cf[g];
-        if (MASKED && M == INT32_MIN) m = -INFINITY;
-        mt = fmaxf(mt, m);
-    }
-    // the scores as float32 (see ScoreConv)
     v16f F[4];
+    if constexpr (PER_KEY) {
+        // the scores as float32 first, then the largest f32(acc * c_key)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) F[t] = SC::to_f32(S[t]);
+        for (int t = 0; t < 4; ++t) F[t] = SC::to_f32(S[t]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float f = F[t][4 * i + j];
+                    const float sc = f * key_factor(t, i, j);
+                    if (!MASKED || f != SC::kMasked) mt = fmaxf(mt, sc);
+                }
+        // (the other half of the row's keys sit in the lane 32 apart)
+        const auto both = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mt), __builtin_bit_cast(int, mt),
+                                                           false, false);
+        mt = fmaxf(__builtin_bit_cast(float, (int)both[0]), __builtin_bit_cast(float, (int)both[1]));
+    } else {
+#pragma unroll
+        for (int g = 0; g < KSPLIT; ++g) {
+            int M = S[g * TPG][0];
+#pragma unroll
+            for (int tt = 0; tt < TPG; ++tt)
+#pragma unroll
+                for (int v = (tt == 0 ? 1 : 0); v < 16; ++v) M = max(M, S[g * TPG + tt][v]);
+            M = max_across_halves(M);
+            // f32(acc_max * c), one rounding: the largest f32(acc * c) of the
+            // group, since c >= 0
+            float m = SC::max_to_f32(M) * cf[g];
+            if (MASKED && M == INT32_MIN) m = -INFINITY;
+            mt = fmaxf(mt, m);
+        }
+        // the scores as float32 (see ScoreConv)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) F[t] = SC::to_f32(S[t]);
+    }
 
     // ---- lazy update of the reference maximum
     {
@@ -328,7 +372,7 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
         for (int s = 0; s < 8; ++s) {
             if (pass == 0) {
                 const int t = s >> 1, base = 8 * (s & 1);
-                const float ct = cf[t / TPG];
+                const float ct = PER_KEY ? 0.0f : cf[t / TPG];
                 v4i quad;
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
@@ -336,7 +380,8 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int v = base + 4 * g + i;
-                        y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[t][v], ct, bias));
+                        const float cv = PER_KEY ? key_factor(t, v >> 2, v & 3) : ct;
+                        y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[t][v], cv, bias));
                         if (MASKED && F[t][v] == SC::kMasked) y[i] = 0.0f;
                     }
                     if (PV16) {
@@ -397,13 +442,13 @@ template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = fals
 __device__ __forceinline__ void attn_block(const uint8_t* __restrict__ lk,
                                            const void* __restrict__ lv,
                                            const v4i (&qf)[D / 32], int T, int row, int N,
-                                           const float (&c)[KSPLIT], float l448, int h, int r32,
-                                           const v8h& rsel, float& mref, float& lsum,
-                                           v16f (&O)[D / 32]) {
+                                           const float (&c)[score_factors<KSPLIT>()], float l448, int h,
+                                           int r32, const v8h& rsel, float& mref, float& lsum,
+                                           v16f (&O)[D / 32], const float* __restrict__ lks = nullptr) {
     v16i S[4];
     block_scores<D>(lk, qf, h, r32, S);
     block_softmax_pv<D, KSPLIT, CAUSAL, PV16, MASKED, V8>(S, lv, T, row, N, c, l448, h, r32, rsel,
-                                                          mref, lsum, O);
+                                                          mref, lsum, O, lks);
 }
 
 }  // namespace sage

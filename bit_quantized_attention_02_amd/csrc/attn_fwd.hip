@@ -11,8 +11,9 @@
 
 namespace sage {
 
-static_assert(SAGE_BQ == 128 && SAGE_BQ_THREAD == 1 && SAGE_BK == 64 && SAGE_BK_THREAD == 32,
-              "the launch maps the two granularities to q_shift 7/0 and 2/4 K scales per block");
+static_assert(SAGE_BQ == 128 && SAGE_BQ_THREAD == 1 && SAGE_BK == 64 && SAGE_BK_THREAD == 32 &&
+                  SAGE_BK_TOKEN == 1,
+              "the launch maps the granularities to q_shift 7/0 and 2/4/128 K scales per block");
 
 constexpr int kMaxTailSplit = 8;  // key shares of a split tail tile, at most
 
@@ -48,6 +49,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     uint8_t* const lk1 = smem + SAGE_BN * D;
     uint16_t* const lv0 = reinterpret_cast<uint16_t*>(smem + 2 * SAGE_BN * D);
     uint16_t* const lv1 = lv0 + D * SAGE_BN;
+    // with one K scale per key, each block's 128 scales ride with its tiles
+    constexpr bool PER_KEY = KSPLIT == SAGE_BN;
+    float* const ls0 = reinterpret_cast<float*>(lv1 + D * SAGE_BN);
+    float* const ls1 = ls0 + SAGE_BN;
 
     const int lane = threadIdx.x & 63;
     // The wave index is uniform; held in a scalar register at d = 64, the
@@ -130,10 +135,41 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     // The K scales of a block are loaded one block ahead, before that block's
     // tile copy is issued: vector-memory waits count in issue order, so a
     // scale load issued after the copy would make its wait cover the copy too.
-    typedef float kvec __attribute__((ext_vector_type(KSPLIT)));
-    kvec kscale = *reinterpret_cast<const kvec*>(ksc + KSPLIT * T0);
+    // (per key the scales go through LDS instead; see load_s)
+    constexpr int NKS = PER_KEY ? 1 : KSPLIT;
+    typedef float kvec __attribute__((ext_vector_type(NKS)));
+    auto load_kscale = [&](int t) -> kvec {
+        if constexpr (PER_KEY) {
+            (void)t;
+            return kvec{};
+        } else {
+            return *reinterpret_cast<const kvec*>(ksc + KSPLIT * t);
+        }
+    };
+    kvec kscale = load_kscale(T0);
     const TileLoader<D, WAVES> tiles(kbase, vbase, a.Np, wave, lane);
+    // the 128 per-key scales of block t into LDS: one float per lane of the
+    // first two waves, written straight to LDS by the buffer load
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)ksc, (short)0, PER_KEY ? a.Np * 4 : 0, 0x00020000);
+    auto load_s = [&](int t, float* ls) {
+        if (PER_KEY && wave < 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                srs, (__attribute__((address_space(3))) void*)(ls + 64 * wave), 4, lane * 4,
+                t * SAGE_BN * 4 + wave * 256, 0, 0);
+    };
+    // the score factors of a block (see score_factors)
+    auto factors = [&](float (&c)[score_factors<KSPLIT>()]) {
+        if constexpr (PER_KEY) {
+            c[0] = sq;
+            c[1] = a.qk;
+        } else {
+#pragma unroll
+            for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
+        }
+    };
     tiles.load(T0, lk0, lv0, wave);
+    load_s(T0, ls0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -148,13 +184,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     auto full_block = [&](int T, auto odd_c) {
         constexpr bool ODD = decltype(odd_c)::value;
         const bool more = T + 1 < T1;
-        const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
-        if (more) tiles.load(T + 1, ODD ? lk0 : lk1, ODD ? lv0 : lv1, wave);
-        float c[KSPLIT];
-#pragma unroll
-        for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-        attn_block<D, KSPLIT, CAUSAL, PV16, false>(ODD ? lk1 : lk0, ODD ? lv1 : lv0, qf, T, row,
-                                                                 a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
+        const kvec knext = load_kscale(more ? T + 1 : T);
+        if (more) {
+            tiles.load(T + 1, ODD ? lk0 : lk1, ODD ? lv0 : lv1, wave);
+            load_s(T + 1, ODD ? ls0 : ls1);
+        }
+        float c[score_factors<KSPLIT>()];
+        factors(c);
+        attn_block<D, KSPLIT, CAUSAL, PV16, false>(ODD ? lk1 : lk0, ODD ? lv1 : lv0, qf, T, row, a.N, c, a.l448,
+                                                   h, r32, rsel, mref, lsum, O, ODD ? ls1 : ls0);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -173,13 +211,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
         for (; T < nA1; ++T) {
             const bool odd = (T - T0) & 1;
             const bool more = T + 1 < T1;
-            const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
-            if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
-            float c[KSPLIT];
-#pragma unroll
-            for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
-            attn_block<D, KSPLIT, CAUSAL, PV16, false>(
-                odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
+            const kvec knext = load_kscale(more ? T + 1 : T);
+            if (more) {
+                tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
+                load_s(T + 1, odd ? ls0 : ls1);
+            }
+            float c[score_factors<KSPLIT>()];
+            factors(c);
+            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
+                                                       a.l448, h, r32, rsel, mref, lsum, O, odd ? ls1 : ls0);
             kscale = knext;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
@@ -188,19 +228,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     for (; T < T1; ++T) {
         const bool odd = (T - T0) & 1;
         const bool more = T + 1 < T1;
-        const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
-        if (more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
-        float c[KSPLIT];
-#pragma unroll
-        for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
+        const kvec knext = load_kscale(more ? T + 1 : T);
+        if (more) {
+            tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, wave);
+            load_s(T + 1, odd ? ls0 : ls1);
+        }
+        float c[score_factors<KSPLIT>()];
+        factors(c);
         // (without causality only the ragged last block is left here: one
         // body, whose registers then need no spilling at d = 128)
         if (CAUSAL && T < n_full)
-            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
-                                                       a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, PV16, false>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
+                                                       a.l448, h, r32, rsel, mref, lsum, O, odd ? ls1 : ls0);
         else if (T <= wave_last)
-            attn_block<D, KSPLIT, CAUSAL, PV16, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row,
-                                                      a.N, c, a.l448, h, r32, rsel, mref, lsum, O);
+            attn_block<D, KSPLIT, CAUSAL, PV16, true>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, row, a.N, c,
+                                                      a.l448, h, r32, rsel, mref, lsum, O, odd ? ls1 : ls0);
         kscale = knext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -317,6 +359,10 @@ SAGE_ATTN_INST_PV(128, 2, false)
 SAGE_ATTN_INST_PV(128, 2, true)
 SAGE_ATTN_INST_PV(128, 4, false)
 SAGE_ATTN_INST_PV(128, 4, true)
+SAGE_ATTN_INST_PV(64, SAGE_BN, false)
+SAGE_ATTN_INST_PV(64, SAGE_BN, true)
+SAGE_ATTN_INST_PV(128, SAGE_BN, false)
+SAGE_ATTN_INST_PV(128, SAGE_BN, true)
 #undef SAGE_ATTN_INST_PV
 #undef SAGE_ATTN_INST
 
@@ -324,7 +370,7 @@ template <int D, int KSPLIT, bool CAUSAL, bool PV16>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t st) {
     constexpr int WAVES = attn_waves<D>();
     constexpr int WPS = attn_waves_per_simd<D, KSPLIT, CAUSAL>();
-    constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2;
+    constexpr size_t lds = 2 * SAGE_BN * D + 2 * D * SAGE_BN * 2 + (KSPLIT == SAGE_BN ? 2 * SAGE_BN * 4 : 0);
     a.nqt = a.Np / (32 * WAVES);
     const void* fn = (const void*)attn_fwd<D, KSPLIT, CAUSAL, PV16, WAVES, WPS>;
     static LaunchFacts facts;
@@ -411,12 +457,17 @@ hipError_t launch_attn(const sage_qkv_quant* z, float* out, const Shape& s, int 
     a.q_shift = z->q_block == SAGE_BQ ? 7 : 0;  // SAGE_BQ = 128, SAGE_BQ_THREAD = 1
     a.qk = qk;
     a.l448 = l448;
-    const bool fine_k = z->k_block == SAGE_BK_THREAD;  // 4 K scales per block, else 2
+    // K scales per block: 2 (SAGE_BK), 4 (SAGE_BK_THREAD) or one per key (SAGE_BK_TOKEN)
     const bool pv16 = z->pv_format == SAGE_PV_F16;
     // (INT4 codes go through the same kernels: their scores are as exact)
-    if (s.d == 64)
-        return fine_k ? launch_attn_d<64, 4>(a, causal, pv16, st) : launch_attn_d<64, 2>(a, causal, pv16, st);
-    return fine_k ? launch_attn_d<128, 4>(a, causal, pv16, st) : launch_attn_d<128, 2>(a, causal, pv16, st);
+    if (s.d == 64) {
+        if (z->k_block == SAGE_BK_TOKEN) return launch_attn_d<64, SAGE_BN>(a, causal, pv16, st);
+        return z->k_block == SAGE_BK_THREAD ? launch_attn_d<64, 4>(a, causal, pv16, st)
+                                            : launch_attn_d<64, 2>(a, causal, pv16, st);
+    }
+    if (z->k_block == SAGE_BK_TOKEN) return launch_attn_d<128, SAGE_BN>(a, causal, pv16, st);
+    return z->k_block == SAGE_BK_THREAD ? launch_attn_d<128, 4>(a, causal, pv16, st)
+                                        : launch_attn_d<128, 2>(a, causal, pv16, st);
 }
 
 }  // namespace sage

@@ -101,9 +101,9 @@ static Layout layout(const Shape& s, bool with_q = true, size_t v_bytes = sizeof
     L.q_i8 = with_q ? take((size_t)s.q_elems()) : 0;
     L.k_i8 = take((size_t)s.kv_elems());
     L.v16 = take((size_t)s.kv_elems() * v_bytes);
-    // scales sized for the finer of the two granularities
+    // scales sized for the finest granularity
     L.q_scale = with_q ? take(Bq * (s.Np / SAGE_BQ_THREAD) * sizeof(float)) : 0;
-    L.k_scale = take(Bkv * (s.Np / SAGE_BK_THREAD) * sizeof(float));
+    L.k_scale = take(Bkv * (s.Np / SAGE_BK_TOKEN) * sizeof(float));
     L.k_mean = take(Bkv * s.d * sizeof(float));
     L.v_scale = take(Bkv * s.d * sizeof(float));
     L.v_inv = take(Bkv * s.d * sizeof(float));
@@ -118,7 +118,7 @@ static Layout layout(const Shape& s, bool with_q = true, size_t v_bytes = sizeof
 
 static bool granularity_ok(int q_block, int k_block) {
     return (q_block == SAGE_BQ && k_block == SAGE_BK) ||
-           (q_block == SAGE_BQ_THREAD && k_block == SAGE_BK_THREAD);
+           (q_block == SAGE_BQ_THREAD && (k_block == SAGE_BK_THREAD || k_block == SAGE_BK_TOKEN));
 }
 
 static bool pv_format_ok(int f) { return f == SAGE_PV_E4M3 || f == SAGE_PV_F16; }
@@ -466,7 +466,7 @@ const char* sage_status_string(int status) {
         case SAGE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad flag or size)";
         case SAGE_ERR_UNSUPPORTED:
             return "unsupported shape or option (d must be 64 or 128, Hq % Hkv == 0, N <= 2^20; "
-                   "(q_block, k_block) = (128, 64) or (1, 32); P.V format E4M3 (0) or binary16 (1); "
+                   "(q_block, k_block) = (128, 64), (1, 32) or (1, 1); P.V format E4M3 (0) or binary16 (1); "
                    "Q, K codes of 8 or 4 bits)";
         case SAGE_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
         case SAGE_ERR_HIP: return "HIP launch failed";

@@ -24,7 +24,11 @@
  *     flash tile of the SageAttention article) and thread-level (one Q scale
  *     per query row -- each lane of the attention kernel owns one row -- and
  *     one K scale per 32-key matrix-core tile; the Berkeley brief's checklist
- *     item on thread-level block quantization).  sage_qkv_quant.q_block and
+ *     item on thread-level block quantization); and token granularity (one
+ *     Q scale per query row and one K scale per key, the finest the scheme
+ *     allows: the attention kernel forms each key's score factor where it
+ *     needs it, at a cost in vector work, for the rows whose large |Q| the
+ *     coarser K groups quantize too coarsely).  sage_qkv_quant.q_block and
  *     .k_block select it.
  *   - FP8: OCP E4M3FN (max 448), round to nearest even.  V: one scale per
  *     channel, code = e4m3(v * f32(448/absmax_c)).
@@ -87,6 +91,7 @@ extern "C" {
 #define SAGE_MAX_N (1 << 20)
 #define SAGE_BQ_THREAD 1  /* query rows per Q scale, thread-level granularity */
 #define SAGE_BK_THREAD 32 /* keys per K scale, thread-level granularity */
+#define SAGE_BK_TOKEN 1   /* keys per K scale, token granularity (one scale per key) */
 #define SAGE_PV_E4M3 0    /* P and V as FP8 E4M3 (the default) */
 #define SAGE_PV_F16 1     /* P and V as binary16 */
 #define SAGE_QK_INT8 8    /* Q, K codes: INT8 (the default) */
@@ -116,7 +121,7 @@ typedef struct {
  *   q_i8    int8 [B, Hq, N_p, d]            row-major, d innermost
  *   q_scale f32  [B, Hq, N_p / bq]
  *   k_i8    int8 [B, Hkv, N_p, d]           codes of K - k_mean
- *   k_scale f32  [B, Hkv, N_p / bk]
+ *   k_scale f32  [B, Hkv, N_p / bk]          (room for bk = 1)
  *   k_mean  f32  [B, Hkv, d]
  *   v16     binary16 [B, Hkv, N_p / SAGE_BN, d, SAGE_BN]: the V operand of
  *           P.V.  With SAGE_PV_E4M3, the E4M3 codes of V, each stored as the
@@ -150,7 +155,8 @@ typedef struct {
     float* v_part;
     int32_t* sync;
     int32_t q_block; /* query rows per Q scale: SAGE_BQ (set by sage_workspace_carve) or SAGE_BQ_THREAD */
-    int32_t k_block; /* keys per K scale: SAGE_BK (set by sage_workspace_carve) or SAGE_BK_THREAD */
+    int32_t k_block; /* keys per K scale: SAGE_BK (set by sage_workspace_carve), SAGE_BK_THREAD or
+                        SAGE_BK_TOKEN */
     int32_t pv_format; /* SAGE_PV_E4M3 (set by sage_workspace_carve) or SAGE_PV_F16; the
                           attention call must see the value the quantize call saw */
     int32_t qk_bits;   /* SAGE_QK_INT8 (set by sage_workspace_carve) or SAGE_QK_INT4; likewise */
@@ -164,7 +170,7 @@ typedef struct {
 /* Method options of sage_attn_fwd_ex. */
 typedef struct {
     int32_t q_block;   /* SAGE_BQ or SAGE_BQ_THREAD */
-    int32_t k_block;   /* SAGE_BK or SAGE_BK_THREAD (paired with q_block as above) */
+    int32_t k_block;   /* SAGE_BK, SAGE_BK_THREAD or SAGE_BK_TOKEN (paired with q_block as above) */
     int32_t pv_format; /* SAGE_PV_E4M3 or SAGE_PV_F16 */
     int32_t qk_bits;   /* SAGE_QK_INT8 or SAGE_QK_INT4 */
 } sage_options;
@@ -175,9 +181,9 @@ size_t sage_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /* Split `workspace` (device memory, 256-byte aligned, ws_bytes long) into the
  * views above, with the per-block granularity (q_block = SAGE_BQ, k_block =
- * SAGE_BK) and E4M3 P.V; the caller may then switch both block sizes to
- * SAGE_BQ_THREAD and SAGE_BK_THREAD (the workspace holds the scales of
- * either) and pv_format to SAGE_PV_F16.  The quantize and attention calls
+ * SAGE_BK) and E4M3 P.V; the caller may then switch the block sizes to
+ * (SAGE_BQ_THREAD, SAGE_BK_THREAD) or (SAGE_BQ_THREAD, SAGE_BK_TOKEN) (the
+ * workspace holds the scales of any of them) and pv_format to SAGE_PV_F16.  The quantize and attention calls
  * given the struct read these fields; any other values make them return
  * SAGE_ERR_UNSUPPORTED.  Host-only; no HIP call. */
 int sage_workspace_carve(void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
@@ -222,8 +228,9 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
 
 /* sage_attn_fwd (E4M3 P.V) with the quantization granularity chosen by the caller:
  * (q_block, k_block) = (SAGE_BQ, SAGE_BK) is sage_attn_fwd itself,
- * (SAGE_BQ_THREAD, SAGE_BK_THREAD) the thread-level granularity; any other
- * pair returns SAGE_ERR_UNSUPPORTED. */
+ * (SAGE_BQ_THREAD, SAGE_BK_THREAD) the thread-level granularity,
+ * (SAGE_BQ_THREAD, SAGE_BK_TOKEN) the token granularity; any other pair
+ * returns SAGE_ERR_UNSUPPORTED. */
 int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* out, int B, int Hq,
                            int Hkv, int N, int d, int causal, float sm_scale, int dtype,
                            int q_block, int k_block, void* workspace, size_t ws_bytes,

@@ -89,12 +89,12 @@ def _rows_of(out, rows, d):
 
 
 def quantize_as(orc, q, k, v, granularity, pv="e4m3", qk_bits=8):
-    bq, bk = {"block": (128, 64), "thread": (1, 32)}[granularity]
+    bq, bk = {"block": (128, 64), "thread": (1, 32), "token": (1, 1)}[granularity]
     return orc.quantize(q, k, v, bq=bq, bk=bk, pv=pv, qk_bits=qk_bits)
 
 
 @pytest.mark.parametrize("pv", ["e4m3", "f16"])
-@pytest.mark.parametrize("granularity", ["block", "thread"])
+@pytest.mark.parametrize("granularity", ["block", "thread", "token"])
 @pytest.mark.parametrize("recipe", [1, 2, 3, 4, 5])
 def test_parity_reduced_workloads(sage, orc, recipe, granularity, pv):
     """Each workload's recipe at a size the oracle covers in full: several
@@ -134,7 +134,7 @@ def test_parity_int4_qk(sage, orc, recipe, granularity):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_parity_edge_lengths(sage, orc, N, d, causal):
-    granularity = "thread" if N in (17, 129, 300) else "block"
+    granularity = "thread" if N in (17, 129, 300) else ("token" if N in (2, 127, 255) else "block")
     pv = "f16" if N in (2, 64, 129, 256) else "e4m3"
     qk_bits = 4 if N in (1, 127, 129) else 8
     _say(f"case N={N} d={d} causal={causal} granularity={granularity} pv={pv} qk_bits={qk_bits}")
@@ -281,6 +281,10 @@ ACCURACY = {
     (5, "thread", "f16", 8): (0.999, 0.03),      # 0.999373, 0.02152
     (3, "thread", "e4m3", 4): (0.980, 0.20),     # 0.981769, 0.19191
     (4, "thread", "f16", 4): (0.79, 0.32),       # 0.794744, 0.30783
+    (4, "token", "e4m3", 8): (0.9983, 0.0405),   # 0.998536, 0.03887
+    (4, "token", "f16", 8): (0.9987, 0.03),      # 0.998888, 0.01790
+    (5, "token", "f16", 8): (0.999, 0.03),       # 0.999470, 0.01911
+    (2, "token", "e4m3", 8): (0.999, 0.0355),    # 0.999422, 0.03391
 }
 
 

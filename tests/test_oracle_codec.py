@@ -151,11 +151,12 @@ def test_int8_blocks_round_half_even_within_half_step(orc, N, d, qk_bits, qmax):
 
 
 @pytest.mark.parametrize("qk_bits,qmax", [(8, 127), (4, 7)])
-@pytest.mark.parametrize("bq,bk", [(1, 32), (128, 64)])
-def test_scale_groups_of_both_granularities(orc, bq, bk, qk_bits, qmax):
+@pytest.mark.parametrize("bq,bk", [(1, 32), (128, 64), (1, 1)])
+def test_scale_groups_of_every_granularity(orc, bq, bk, qk_bits, qmax):
     """Q scales per bq rows and K scales per bk keys, each the group's absmax /
-    qmax with numpy's rint on the float32 product, for the per-block and the
-    thread-level (per-row Q, 32-key K) granularities; ragged last groups."""
+    qmax with numpy's rint on the float32 product, for the per-block, the
+    thread-level (per-row Q, 32-key K) and the token (per-row Q, per-key K)
+    granularities; ragged last groups."""
     N, d = 70, 64
     q, k, v = workloads.random_inputs(1, 2, 2, N, d, "bf16", seed=bq + bk, scale=2.0)
     z = orc.quantize(q, k, v, bq=bq, bk=bk, qk_bits=qk_bits)
