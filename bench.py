@@ -58,7 +58,8 @@ def parse():
                         "cache on decode workload 6 or 7 (one JSON line of its own, HBM-bound)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="instead of the benchmark, run a plain device-to-device copy of BYTES "
-                        "bytes 5 times: a known-size reference for hardware byte counters")
+                        "bytes 7 times (2 untimed, 5 timed with HIP events): a known-size reference for "
+                        "hardware byte counters and the achievable copy bandwidth")
     return p.parse_args()
 
 
@@ -343,10 +344,11 @@ def main():
     if args.copy_probe:
         src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
-        for _ in range(5):
+        for _ in range(2):
             dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 5}), flush=True)
+        ms = timed(lambda: dst.copy_(src), 5, torch)
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 7, "ms_per_copy": round(ms, 4),
+                          "copy_TBps": round(2 * args.copy_probe / (ms * 1e-3) / 1e12, 3)}), flush=True)
         return
 
     w = workloads.WORKLOADS[args.workload]
