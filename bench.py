@@ -375,9 +375,7 @@ def main():
     ms_prep = timed(lambda: sage.sage_quantize(qd, kd, vd, z), args.steps, torch)
     ms_attn = timed(lambda: sage.sage_attn_fwd_quantized(z, out, w.B, w.Hq, w.Hkv, w.N, w.d,
                                                          w.causal, w.sm_scale), args.steps, torch)
-    traffic_wl, traffic = measured_traffic(args.granularity, args.pv, args.qk_bits)
-    if traffic_wl != w.name:
-        traffic = None
+    _, traffic = measured_traffic(args.granularity, args.pv, args.qk_bits, workload=w.name)
     tops = w.ops / (ms_step * 1e-3) / 1e12
     attn_tops = w.ops / (ms_attn * 1e-3) / 1e12
     elems = (w.B * w.Hq + 2 * w.B * w.Hkv) * w.N * w.d
