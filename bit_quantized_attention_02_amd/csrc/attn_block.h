@@ -75,11 +75,12 @@ constexpr float kLazyRescale = 8.0f;
 //  The integer patterns order like the scores in both cases, so the row
 //  maximum is taken on them.
 // Score factors passed to the block body: one per K-scale group (KSPLIT of
-// 2 or 4 per block), or, with one K scale per key (KSPLIT == SAGE_BN), the
-// row's Q scale and f32(sm_scale * log2 e), the keys' scales coming from LDS.
+// 2 or 4 per block), c = f32(f32(s_q * f32(sm_scale * log2 e)) * s_k), or,
+// with one K scale per key (KSPLIT == SAGE_BN), the row's part f32(s_q *
+// f32(sm_scale * log2 e)) alone, the keys' scales coming from LDS.
 template <int KSPLIT>
 constexpr int score_factors() {
-    return KSPLIT == SAGE_BN ? 2 : KSPLIT;
+    return KSPLIT == SAGE_BN ? 1 : KSPLIT;
 }
 
 template <int D> struct ScoreConv;
@@ -257,10 +258,10 @@ __device__ __forceinline__ void block_scores(const uint8_t* __restrict__ lk, con
 // fragment is read.
 // KSPLIT: K scales per block of SAGE_BN keys (2: one per 64 keys; 4: one per
 // 32-key tile; SAGE_BN: one per key).  For 2 or 4, c[g] is the score factor
-// f32(f32(s_q * s_k) * f32(sm_scale * log2 e)) of scale group g; tile t
-// belongs to group t / (4 / KSPLIT).  For SAGE_BN, c = {s_q, f32(sm_scale *
-// log2 e)} and the block's 128 key scales are at lks in LDS; each key's
-// factor is formed as f32(f32(s_q * s_k) * c[1]) where it is needed.
+// f32(f32(s_q * f32(sm_scale * log2 e)) * s_k) of scale group g; tile t
+// belongs to group t / (4 / KSPLIT).  For SAGE_BN, c[0] is the row's part
+// f32(s_q * f32(sm_scale * log2 e)) and the block's 128 key scales are at
+// lks in LDS; each key's factor f32(c[0] * s_k) is formed where it is needed.
 template <int D, int KSPLIT, bool CAUSAL, bool PV16, bool MASKED, bool V8 = false>
 __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __restrict__ lv, int T,
                                                  int row, int N, const float (&c)[score_factors<KSPLIT>()],
@@ -278,12 +279,12 @@ __device__ __forceinline__ void block_softmax_pv(v16i (&S)[4], const void* __res
         for (int g = 0; g < KSPLIT; ++g) cf[g] = c[g] * SC::kInvF;
     }
     // per key: the factor of key 32t + 8i + 4h + j (element 4i + j of tile
-    // t), (s_q * s_k) * f32(sm_scale log2 e * kInvF), the last product exact
-    // up to the power of two kInvF
-    const float qkf = PER_KEY ? c[1] * SC::kInvF : 0.0f;
+    // t), f32(row part * s_k) times the power of two kInvF (exact), one
+    // product per key
+    const float rowf = PER_KEY ? c[0] * SC::kInvF : 0.0f;
     auto key_factor = [&](int t, int i, int j) -> float {
         const v4f ks = *reinterpret_cast<const v4f*>(lks + 32 * t + 8 * i + 4 * h);
-        return (c[0] * ks[j]) * qkf;
+        return rowf * ks[j];
     };
 
     // ---- block maxima, one per K-scale group

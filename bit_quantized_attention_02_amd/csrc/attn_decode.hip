@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
             const kvec knext = *reinterpret_cast<const kvec*>(ksc + KSPLIT * (more ? T + 1 : T));
             float c[KSPLIT];
 #pragma unroll
-            for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * kscale[gg]) * a.qk;
+            for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * a.qk) * kscale[gg];
             v16i S[4];
             block_scores<D>(lk0, qf, h, r32, S);
             if (more) {
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64) void attn_decode(DecodeArgs a) {
         if (NBUF == 2 && more) tiles.load(T + 1, odd ? lk0 : lk1, odd ? lv0 : lv1, 0);
         float c[KSPLIT];
 #pragma unroll
-        for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * kscale[gg]) * a.qk;
+        for (int gg = 0; gg < KSPLIT; ++gg) c[gg] = (sq * a.qk) * kscale[gg];
         if (T < first_masked)
             attn_block<D, KSPLIT, CAUSAL, PV16, false, V8>(odd ? lk1 : lk0, odd ? lv1 : lv0, qf, T, pos,
                                                            a.Nk, c, a.l448, h, r32, rsel, mref, lsum, O);

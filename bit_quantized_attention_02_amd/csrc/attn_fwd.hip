@@ -160,12 +160,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     };
     // the score factors of a block (see score_factors)
     auto factors = [&](float (&c)[score_factors<KSPLIT>()]) {
+        const float sqq = sq * a.qk;  // the row's part of every factor
         if constexpr (PER_KEY) {
-            c[0] = sq;
-            c[1] = a.qk;
+            c[0] = sqq;
         } else {
 #pragma unroll
-            for (int g = 0; g < KSPLIT; ++g) c[g] = (sq * kscale[g]) * a.qk;
+            for (int g = 0; g < KSPLIT; ++g) c[g] = sqq * kscale[g];
         }
     };
     tiles.load(T0, lk0, lv0, wave);

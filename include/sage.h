@@ -33,8 +33,9 @@
  *   - FP8: OCP E4M3FN (max 448), round to nearest even.  V: one scale per
  *     channel, code = e4m3(v * f32(448/absmax_c)).
  *   - Softmax in FP32: each integer score acc (exact) becomes float32 exactly
- *     and, in log2 units, f32(acc * c) with c = f32(f32(s_q*s_k) *
- *     f32(sm_scale*log2 e)).
+ *     and, in log2 units, f32(acc * c) with c = f32(f32(s_q *
+ *     f32(sm_scale*log2 e)) * s_k) (the row's part formed first, so that a
+ *     per-key factor costs one product per key).
  *   - P: one block is one query row by SAGE_BN keys; with m the block's
  *     largest f32(acc * c), the block's codes are
  *     e4m3(2^fmaf(acc, c, f32(f32(log2(448)) - m))), so the largest element

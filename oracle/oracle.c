@@ -274,7 +274,7 @@ void oracle_quantize(const float* q, const float* k, const float* v,
  * j <= i + Nk - Nq (causal) or all j < Nk:
  *
  *   acc_j = sum_c q_i8[i,c] * k_i8[j,c]                       (exact integer)
- *   c_j   = f32( f32(sq * sk[j/bk]) * f32(sm_scale*log2 e) )   (float32)
+ *   c_j   = f32( f32(sq * f32(sm_scale*log2 e)) * sk[j/bk] )   (float32)
  *   s_j   = f32(acc_j * c_j)                                   (float32, log2 units)
  *   blocks t of bn keys; m_t = max of s_j over the block's allowed keys
  *   x_j   = fmaf(acc_j, c_j, f32(f32(log2 448) - m_t))
@@ -351,8 +351,8 @@ void oracle_attn_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                 const int8_t* kr = kh + (long)j * d;
                 for (int c = 0; c < d; ++c) s += (int32_t)qrow[c] * (int32_t)kr[c];
                 acc[j] = s;
-                float sqk = sq * skh[j / bk];
-                cj[j] = sqk * qk;
+                float sqq = sq * qk;
+                cj[j] = sqq * skh[j / bk];
                 aj[j] = (float)s; /* exact: |acc| < 2^24 */
             }
             /* per-block maximum score: the P scale of the block */

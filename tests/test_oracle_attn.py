@@ -131,7 +131,7 @@ def test_blockwise_constant_keys_give_weighted_block_means(orc, causal, pv):
     assert fl.sum() == 0
     # every score of a block is equal, so every code is the block maximum's and
     # the only error left is the float32 evaluation of the log2 block weights:
-    # c = f32(f32(s_q s_k) f32(sm_scale log2 e)) and m_t = f32(acc c) carry at
+    # c = f32(f32(s_q f32(sm_scale log2 e)) s_k) and m_t = f32(acc c) carry at
     # most four roundings (relative 2^-24 each), so each m_t, and each
     # difference m_t - M, is off by at most eps = 8 2^-24 max|m|; the block
     # weights are off by factors within 2^(+-eps), which moves a convex
@@ -199,7 +199,7 @@ def _online_reference(orc, z, causal, sm_scale, bn):
                     for j in blk:
                         acc = int(np.dot(z["q_i8"][b, h, i].astype(np.int64),
                                          z["k_i8"][b, g, j].astype(np.int64)))
-                        c = np.float32(np.float32(s_q * z["k_scale"][b, g, j // z["bk"]]) * qk)
+                        c = np.float32(np.float32(s_q * qk) * z["k_scale"][b, g, j // z["bk"]])
                         accs.append(acc)
                         cs.append(c)
                     # FP32 softmax: the exact integer score times the score
