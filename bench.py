@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--pv", choices=("e4m3", "f16"), default="e4m3",
                    help="P.V format: e4m3 (FP8 P and V, the default) or f16 (binary16 P and V)")
     p.add_argument("--qk-bits", type=int, choices=(8, 4), default=8,
-                   help="Q, K codes: INT8 (the default) or the INT4 values of the 4-bit variant")
+                   help="Q, K codes: INT8 (the default) or INT4-valued codes on the INT8 matrix core "
+                        "(the 4-bit numerics as an accuracy option, at INT8 speed)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
     p.add_argument("--contrast", action="store_true",

@@ -303,7 +303,7 @@ def sage_attn_decode_noalloc(q: torch.Tensor, cache: sage_kv_cache, out: torch.T
 
 def options(granularity: str = "block", pv: str = "e4m3", qk_bits: int = 8) -> sage_options:
     """sage_options from the names of a granularity and a P.V format, and the
-    Q, K code width (8, or 4 for the INT4 variant)."""
+    Q, K code width (8, or 4 for INT4-valued codes: an accuracy option at INT8 speed)."""
     qb, kb = GRANULARITY[granularity]
     return sage_options(qb, kb, PV_FORMAT[pv], qk_bits)
 
@@ -324,7 +324,7 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     -> FP32 [B,Hq,N,d], on the current stream.  granularity: "block" (one Q
     scale per 128 rows, one K scale per 64 keys), "thread" (per row, per 32
     keys) or "token" (per row, per key); pv: "e4m3" (FP8 P and V) or "f16" (binary16 P and V); qk_bits: 8
-    (INT8 Q, K) or 4 (INT4 values)."""
+    (INT8 Q, K) or 4 (INT4-valued codes on the INT8 matrix core, an accuracy option)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     _check_qkv(q, k, v)

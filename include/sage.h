@@ -50,12 +50,13 @@
  *     f16(2^fmaf(acc, c, -m)), so the block's largest element is exactly 1.
  *     The article accumulates in FP16; the binary16 matrix cores here
  *     accumulate in FP32 only, so both levels stay FP32.
- *   - Q, K code width (sage_qkv_quant.qk_bits).  SAGE_QK_INT4 is the 4-bit
- *     Q, K of SageAttention2 (the SageAttention2 summary; the Berkeley brief's
- *     comparison table): the INT8 scheme with 7 in place of 127 (codes in
- *     [-7, 7], scale absmax/7), stored one code per byte and multiplied on
- *     the INT8 matrix core (gfx950 has no INT4 one), at INT8 speed.  Decode
- *     caches are INT8 only.
+ *   - Q, K code width (sage_qkv_quant.qk_bits).  SAGE_QK_INT4 gives the
+ *     numerics of SageAttention2's 4-bit Q, K (the SageAttention2 summary;
+ *     the Berkeley brief's comparison table) as an accuracy option, not a
+ *     faster path: the INT8 scheme with 7 in place of 127 (codes in [-7, 7],
+ *     scale absmax/7), stored one code per byte and multiplied on the INT8
+ *     matrix core (gfx950 has no INT4 one), at INT8 speed.  Decode caches are
+ *     INT8 only.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
