@@ -29,6 +29,14 @@
 
 namespace sage {
 
+// Channels of V one prep_pack work-group transposes: all of them at d = 64;
+// at d = 128 two work-groups take 64 each, so that the LDS tile (16 KB)
+// leaves room for twice as many resident work-groups.
+template <int D>
+__host__ __device__ constexpr int pack_v_channels() {
+    return D < 64 ? D : 64;
+}
+
 // The arrival counters of the statistics, one per kv head.
 __host__ __device__ inline int sync_words(const Shape& s) { return s.B * s.Hkv; }
 
@@ -169,19 +177,20 @@ __device__ inline void q_rows(const uint16_t* __restrict__ q, const Shape& s, in
         const int row = min(t * R + e / CPR, s.N - 1), col = (e % CPR) * 8;
         u[c] = *reinterpret_cast<const uint4*>(q + src_head + (long long)row * D + col);
     }
-    float x[NCH][8], am[NCH];
+    // The values are unpacked twice (for the absmax, then for the codes)
+    // rather than kept as floats across the group maximum: at d = 128 that
+    // halves the registers, and the occupancy doubles.
+    float am[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
         const int row = t * R + e / CPR;
-        unpack8<In>(u[c], x[c]);
-        if (row >= s.N) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[c][i] = 0.0f;
-        }
+        float x[8];
+        unpack8<In>(u[c], x);
         am[c] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) am[c] = fmaxf(am[c], fabsf(x[c][i]));
+        for (int i = 0; i < 8; ++i) am[c] = fmaxf(am[c], fabsf(x[i]));
+        if (row >= s.N) am[c] = 0.0f;
     }
     group_absmax<CPR, R, NCH>(am, bq, rmax, gmax);
     const long long sbase = (long long)bh * (s.Np / bq);
@@ -192,7 +201,13 @@ __device__ inline void q_rows(const uint16_t* __restrict__ q, const Shape& s, in
         const float a = am[c];
         if (e % CPR == 0 && row % bq == 0) q_scale[sbase + row / bq] = a / qmax;
         const float inv = a > 0.0f ? qmax / a : 0.0f;
-        *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = int8_codes(x[c], inv, qmax);
+        float x[8];
+        unpack8<In>(u[c], x);
+        if (row >= s.N) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+        }
+        *reinterpret_cast<uint2*>(q_i8 + dst_head + (long long)row * D + col) = int8_codes(x, inv, qmax);
     }
 }
 
@@ -378,11 +393,12 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     const float* __restrict__ k_mean, const float* __restrict__ v_inv,
     int8_t* __restrict__ k_i8, float* __restrict__ k_scale, void* __restrict__ v_out, int v_store) {
     constexpr int CPR = D / 8;
+    constexpr int VC = pack_v_channels<D>();  // channels per V work-group
     __shared__ float rmax[64], gmax[64];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * SAGE_BN];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[VC * SAGE_BN];
     const int tid = threadIdx.x;
     const int nkb = s.Np / 64, nvb = s.Np / SAGE_BN;
-    const int per_head = nkb + nvb;
+    const int per_head = nkb + nvb * (D / VC);
     // reverse head order relative to the statistics
     const int bg = s.B * s.Hkv - 1 - (int)(blockIdx.x / per_head);
     const int j = blockIdx.x % per_head;
@@ -440,13 +456,15 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
         return;
     }
 
-    // V block T: 128 keys x D channels, transposed through LDS.
-    const int T = j - nkb;
-    constexpr int NCH = SAGE_BN * CPR / kThreads;
-    static_assert(kThreads % CPR == 0, "a thread keeps its column in every chunk");
+    // V block T, channels [c0, c0 + VC): 128 keys x VC channels, transposed
+    // through LDS.
+    const int T = (j - nkb) / (D / VC), c0 = (j - nkb) % (D / VC) * VC;
+    constexpr int CPRV = VC / 8;  // 16-byte chunks of a key's slice
+    constexpr int NCH = SAGE_BN * CPRV / kThreads;
+    static_assert(kThreads % CPRV == 0, "a thread keeps its column in every chunk");
     float inv[8];
     if (v_store != kVF16) {
-        const float4* ip = reinterpret_cast<const float4*>(v_inv + (long long)bg * D + (tid % CPR) * 8);
+        const float4* ip = reinterpret_cast<const float4*>(v_inv + (long long)bg * D + c0 + (tid % CPRV) * 8);
         const float4 i0 = ip[0], i1 = ip[1];
         inv[0] = i0.x, inv[1] = i0.y, inv[2] = i0.z, inv[3] = i0.w;
         inv[4] = i1.x, inv[5] = i1.y, inv[6] = i1.z, inv[7] = i1.w;
@@ -455,13 +473,13 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
-        const int row = min(T * SAGE_BN + e / CPR, s.N - 1), col = (e % CPR) * 8;
+        const int row = min(T * SAGE_BN + e / CPRV, s.N - 1), col = c0 + (e % CPRV) * 8;
         u[c] = *reinterpret_cast<const uint4*>(v + src_head + (long long)row * D + col);
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
-        const int key = e / CPR, col = (e % CPR) * 8;
+        const int key = e / CPRV, col = (e % CPRV) * 8;  // col: within the slice
         const int row = T * SAGE_BN + key;
         float x[8];
         unpack8<In>(u[c], x);
@@ -470,19 +488,20 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
             for (int i = 0; i < 8; ++i) x[i] = 0.0f;
         }
         if (v_store == kVF16)
-            v_f16_to_tile<D>(x, col, v_key_position(key), vt);
+            v_f16_to_tile<VC>(x, col, v_key_position(key), vt);
         else if (v_store == kVE4M3Byte)
-            v_codes_to_tile8<D>(x, inv, col, v_key_position(key),
+            v_codes_to_tile8<VC>(x, inv, col, v_key_position(key),
                                 reinterpret_cast<uint8_t*>(vt));
         else
-            v_codes_to_tile<D>(x, inv, col, v_key_position(key), vt);
+            v_codes_to_tile<VC>(x, inv, col, v_key_position(key), vt);
     }
     __syncthreads();
-    const long long tile = ((long long)bg * nvb + T) * (long long)(D * SAGE_BN);
+    // the slice's channels are a contiguous part of the block's [D][128] tile
+    const long long tile = ((long long)bg * nvb + T) * (long long)(D * SAGE_BN) + (long long)c0 * SAGE_BN;
     if (v_store == kVE4M3Byte)
-        store_v_tile<D, 1>(vt, static_cast<uint8_t*>(v_out) + tile, tid);
+        store_v_tile<VC, 1>(vt, static_cast<uint8_t*>(v_out) + tile, tid);
     else
-        store_v_tile<D, 2>(vt, static_cast<uint16_t*>(v_out) + tile, tid);
+        store_v_tile<VC, 2>(vt, static_cast<uint16_t*>(v_out) + tile, tid);
 }
 
 // Clears the arrival counters of prep_qstats (one per kv head), before it.
@@ -507,7 +526,7 @@ static hipError_t launch_prep_all(const void* q, const void* k, const void* v, c
                        q_scale, z.k_part, z.v_part, z.sync, z.k_mean, z.v_scale, z.v_inv, pv16);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int per_head = s.Np / 64 + s.Np / SAGE_BN;
+    const int per_head = s.Np / 64 + s.Np / SAGE_BN * (D / pack_v_channels<D>());
     hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
                        (const uint16_t*)k, (const uint16_t*)v, s, z.k_block, z.qmax, z.k_mean, z.v_inv,
                        z.k_i8, z.k_scale, z.v, z.v_store);

@@ -65,7 +65,8 @@ static int check_shape(int B, int Hq, int Hkv, int N, int d) {
     const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
     // work-group counts must fit a 1-D grid
     if ((long long)B * Hq * (s.Np / SAGE_BQ) >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
-    if ((long long)B * Hkv * (s.Np / SAGE_BK + s.Np / SAGE_BN) >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
+    // (prep_pack: K row blocks of 64, V blocks of 128 keys in up to two channel slices)
+    if ((long long)B * Hkv * (s.Np / SAGE_BK + 2 * (s.Np / SAGE_BN)) >= (1LL << 31)) return SAGE_ERR_UNSUPPORTED;
     return SAGE_OK;
 }
 
