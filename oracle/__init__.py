@@ -48,11 +48,18 @@ def build(force: bool = False) -> str:
     return LIB
 
 
+# A sanitizer build of oracle.c (tests/test_host_sanitizers.py) is loaded in
+# place of liboracle.so when this variable names its file.
+SANITIZED_LIB_ENV = "SAGE_ORACLE_SANITIZED_LIB"
+
+
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(LIB)
+        path = os.environ.get(SANITIZED_LIB_ENV)
+        if not path:
+            path = build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i, f, dd, l = ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_long
         lib.oracle_e4m3_decode.restype = dd
