@@ -1,4 +1,4 @@
-"""Stream semantics of the boundary: every call runs on the stream it is given
+"""Stream semantics and determinism of the boundary: every call runs on the stream it is given
 (torch's current stream by default), in that stream's order, and can be
 captured into a graph.
 
@@ -9,6 +9,7 @@ captured into a graph.
   into a graph, give on every replay the bytes of an eager call on the inputs
   the replay reads; between replays the program does eager work of its own
   and synchronizes, and the static inputs are rewritten in place.
+- Repeated calls on the same inputs give the same bytes.
 """
 import math
 import sys
@@ -143,3 +144,35 @@ def test_graph_replays_of_the_no_allocation_decode(sage):
         torch.cuda.synchronize()
         _say(f"   replay {rep}")
         assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("index,granularity,pv", [(3, "block", "e4m3"), (4, "block", "e4m3"),
+                                                  (5, "thread", "f16"), (4, "token", "e4m3")])
+def test_repeated_calls_give_identical_bytes(sage, index, granularity, pv):
+    """Five calls on the same inputs return the same bytes: with double-buffered
+    LDS tiles, cross-work-group statistics and split tail tiles, a race would
+    show up as run-to-run differences."""
+    # 48 heads of 17 tiles at d = 64: more tiles than the chip holds at once,
+    # so the leftover round is split along the keys
+    H = 48 if index == 3 else 4
+    w, q, k, v = _problem(index, 2100, 91 + index, B=1, Hq=H, Hkv=H if index != 4 else 1)
+    _say(f"case determinism workload-{index} recipe N=2100 Hq={H} {granularity} {pv}")
+    opts = sage.options(granularity, pv, 8)
+    ws = sage.workspace_for(q, k)
+    first = _attn(sage, w, q, k, v, ws, opts)
+    for _ in range(4):
+        again = _attn(sage, w, q, k, v, ws, opts)
+        torch.cuda.synchronize()
+        assert torch.equal(again, first)
+
+
+def test_repeated_decode_gives_identical_bytes(sage):
+    w, q, k, v = _problem(4, 20000, 99, B=2, Hq=8, Hkv=2, Nq=2)
+    _say("case determinism decode: Nq=2 against 20000 cached keys")
+    cache = sage.KVCache(k, v)
+    sm = 1 / math.sqrt(w.d)
+    first = cache.attend(q, causal=True, sm_scale=sm)
+    for _ in range(4):
+        again = cache.attend(q, causal=True, sm_scale=sm)
+        torch.cuda.synchronize()
+        assert torch.equal(again, first)
