@@ -249,8 +249,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     }
 
     // ---- epilogue: out = O * s_V / l.  O[ct][v] is channel 32ct + 8(v/4) + 4h + v%4.
-    if (row >= a.N) return;
     if (chunk >= 0) {
+        if (row >= a.N) return;
         // a split tile's share: unnormalised O, reference max, row sum
         const long long p = ((long long)(logical - main_tiles) * ROWS + (row - q0)) * a.tail_split + chunk;
         float* po = a.part_o + p * D;
@@ -267,20 +267,62 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
     }
     const float* sv = a.v_scale + (long long)bg * D;
     const float inv_l = 1.0f / lsum;
-    float* op = a.out + ((long long)bh * a.N + row) * D;
+    if constexpr (D == 64) {
+        // each lane stores its row's values directly (turning them around
+        // through LDS as below costs the block loop registers at d = 64,
+        // whose long tiles make the epilogue a small part of the time)
+        if (row >= a.N) return;
+        float* op = a.out + ((long long)bh * a.N + row) * D;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ch = 32 * ct + 8 * i + 4 * h;
-            const float4 s4 = *reinterpret_cast<const float4*>(sv + ch);
-            float4 o;
-            o.x = O[ct][4 * i + 0] * s4.x * inv_l;
-            o.y = O[ct][4 * i + 1] * s4.y * inv_l;
-            o.z = O[ct][4 * i + 2] * s4.z * inv_l;
-            o.w = O[ct][4 * i + 3] * s4.w * inv_l;
-            *reinterpret_cast<float4*>(op + ch) = o;
+            for (int i = 0; i < 4; ++i) {
+                const int ch = 32 * ct + 8 * i + 4 * h;
+                const float4 s4 = *reinterpret_cast<const float4*>(sv + ch);
+                float4 o;
+                o.x = O[ct][4 * i + 0] * s4.x * inv_l;
+                o.y = O[ct][4 * i + 1] * s4.y * inv_l;
+                o.z = O[ct][4 * i + 2] * s4.z * inv_l;
+                o.w = O[ct][4 * i + 3] * s4.w * inv_l;
+                *reinterpret_cast<float4*>(op + ch) = o;
+            }
+        return;
+    }
+    // d = 128: each wave turns its 32 rows around through an LDS region of
+    // its own (the tile buffers are free after the last block's barrier), 64
+    // channels at a time, so that each store instruction writes whole rows'
+    // 256-byte runs instead of a lane's scattered 16-byte pieces: the short
+    // causal tiles end sooner.  Rows are padded to 68 floats, so the 16
+    // lanes of a 16-byte write phase land on distinct banks.
+    constexpr int RS = 68;
+    float* const lo = reinterpret_cast<float*>(smem) + wave * 32 * RS;
+    float* const ob = a.out + (long long)bh * a.N * D;
+#pragma unroll
+    for (int pass = 0; pass < CT / 2; ++pass) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ct = 2 * pass + cc;
+                const int ch = 32 * ct + 8 * i + 4 * h;
+                const float4 s4 = *reinterpret_cast<const float4*>(sv + ch);
+                float4 o;
+                o.x = O[ct][4 * i + 0] * s4.x * inv_l;
+                o.y = O[ct][4 * i + 1] * s4.y * inv_l;
+                o.z = O[ct][4 * i + 2] * s4.z * inv_l;
+                o.w = O[ct][4 * i + 3] * s4.w * inv_l;
+                *reinterpret_cast<float4*>(lo + r32 * RS + ch - 64 * pass) = o;
+            }
+        // (a wave's LDS accesses run in order: these reads see the writes
+        // above, and the next pass's writes come after them)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = lane + 64 * k, rr = c >> 4, c4 = c & 15;
+            const float4 o = *reinterpret_cast<const float4*>(lo + rr * RS + 4 * c4);
+            if (rbase + rr < a.N)
+                *reinterpret_cast<float4*>(ob + (long long)(rbase + rr) * D + 64 * pass + 4 * c4) = o;
         }
+    }
 }
 
 // d = 64: 4-wave work-groups (48 KB of LDS each) whose waves interleave on
