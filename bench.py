@@ -47,10 +47,10 @@ def parse():
                         "(the 4-bit numerics as an accuracy option, at INT8 speed)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows in the CPU sample (0 = auto)")
-    p.add_argument("--contrast", action="store_true",
-                   help="also time torch's scaled_dot_product_attention (flash backend only) in the "
-                        "input dtype on the same inputs: the native attention this path replaces; "
-                        "and a naive unfused 16-bit attention of our own (hipBLASLt products)")
+    p.add_argument("--no-contrast", action="store_true",
+                   help="skip the 16-bit contrast: torch's scaled_dot_product_attention (flash backend "
+                        "only) in the input dtype on the same inputs, the native attention this path "
+                        "replaces, and a naive unfused 16-bit attention of our own (hipBLASLt products)")
     p.add_argument("--prep-flush", action="store_true",
                    help="also time the prep step alone with a 512 MB write between launches, so the "
                         "last-level cache holds none of its inputs")
@@ -404,7 +404,7 @@ def main():
         ms_pf = prep_flushed(sage, qd, kd, vd, z, max(args.steps, 20), torch)
         line["prep"]["flushed_median_ms"] = round(ms_pf, 4)
         line["prep"]["flushed_alg_GBps"] = round(3.0 * elems / (ms_pf * 1e-3) / 1e9, 1)
-    if args.contrast:
+    if not args.no_contrast:
         line["contrast"] = contrast_sdpa(w, qd, kd, vd, args.steps, torch)
         line["contrast_naive"] = contrast_naive(w, qd, kd, vd, args.steps, torch)
     if not args.no_cpu:
