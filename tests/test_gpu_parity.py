@@ -146,6 +146,36 @@ def test_parity_edge_lengths(sage, orc, N, d, causal):
     check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, 1 / math.sqrt(d), None)
 
 
+def _sweep_cases():
+    rng = np.random.default_rng(20261204)
+    cases = []
+    for i in range(24):
+        G = int(rng.choice([1, 2, 3, 8, 16]))
+        Hkv = int(rng.integers(1, 3)) if G < 8 else 1
+        cases.append((i, int(rng.integers(1, 4)), G * Hkv, Hkv, int(rng.integers(1, 640)),
+                      int(rng.choice([64, 128])), bool(rng.integers(0, 2)),
+                      str(rng.choice(["block", "thread", "token"])), str(rng.choice(["e4m3", "f16"]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"s{c[0]}")
+def test_parity_shape_sweep(sage, orc, case):
+    """Seeded random shapes: 1, 2, 3, 8 or 16 q heads per kv head, one to three
+    batches, any N below 640, both head sizes and masks, every granularity and
+    P.V format.  Their small tile counts are rarely multiples of the eight
+    XCDs, so the work-group numbering's uneven ranges are exercised."""
+    i, B, Hq, Hkv, N, d, causal, granularity, pv = case
+    dtype = "f16" if i % 2 else "bf16"
+    _say(f"case sweep {i}: shape={(B, Hq, Hkv, N, d)} causal={causal} granularity={granularity} "
+         f"pv={pv} dtype={dtype}")
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, dtype, seed=3000 + i, scale=1.5)
+    sm = 1 / math.sqrt(d)
+    out, quant = run_gpu(sage, q, k, v, causal, sm, granularity, pv)
+    oz = quantize_as(orc, q, k, v, granularity, pv)
+    check_prep(orc, quant, oz)
+    check_attn(orc, out.reshape(-1, d).cpu().numpy(), oz, causal, sm, None)
+
+
 @pytest.mark.parametrize("kind", ["scale100", "planted_outliers"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
