@@ -19,7 +19,7 @@
  * Spec details the pages leave open (the CPU oracle under oracle/ follows the
  * same ones):
  *   - INT8: symmetric, +-127, code = rne(x * f32(127/absmax)) in float32; an
- *     all-zero block has scale 0.  Two granularities: per block (the default:
+ *     all-zero block has scale 0.  Three granularities: per block (the default:
  *     one Q scale per SAGE_BQ query rows, one K scale per SAGE_BK keys, the
  *     flash tile of the SageAttention article) and thread-level (one Q scale
  *     per query row -- each lane of the attention kernel owns one row -- and
