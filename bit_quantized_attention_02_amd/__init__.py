@@ -62,6 +62,12 @@ class sage_options(ctypes.Structure):
                 ("qk_bits", ctypes.c_int32)]
 
 
+class sage_strides(ctypes.Structure):
+    """Element strides (batch, head, token) of a [B, H, N, d] input whose d
+    elements are contiguous."""
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib.sage_workspace_bytes.restype = _S
 _lib.sage_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
@@ -74,6 +80,11 @@ _lib.sage_attn_fwd_granular.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, 
                                         _S, _P]
 _lib.sage_attn_fwd_ex.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                   ctypes.POINTER(sage_options), _P, _S, _P]
+_SP = ctypes.POINTER(sage_strides)
+_lib.sage_quantize_strided.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _SP, _SP, _SP,
+                                       ctypes.POINTER(sage_qkv_quant), _P]
+_lib.sage_attn_fwd_strided.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                       ctypes.POINTER(sage_options), _SP, _SP, _SP, _P, _S, _P]
 _lib.sage_kv_cache_bytes.restype = _S
 _lib.sage_kv_cache_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.sage_kv_cache_carve.argtypes = [_P, _S, _I, _I, _I, _I, _I, _I, ctypes.POINTER(sage_kv_cache)]
@@ -91,6 +102,7 @@ _lib.sage_status_string.argtypes = [_I]
 
 EXPORTED = ["sage_workspace_bytes", "sage_workspace_carve", "sage_quantize",
             "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_attn_fwd_granular", "sage_attn_fwd_ex",
+            "sage_quantize_strided", "sage_attn_fwd_strided",
             "sage_kv_cache_bytes", "sage_kv_cache_carve", "sage_kv_quantize",
             "sage_decode_workspace_bytes", "sage_attn_decode", "sage_attn_decode_noalloc", "sage_get_config",
             "sage_v_key_position", "sage_status_string"]
@@ -142,9 +154,35 @@ def _check_device(ref: torch.Tensor, *ts) -> None:
             raise ValueError(f"tensors must be contiguous and on {ref.device}")
 
 
-def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out=None) -> None:
+def _strides(t: torch.Tensor):
+    """None for a contiguous [B, H, N, d] tensor; else its element strides as
+    sage_strides, when its d elements are contiguous and every row starts
+    16 bytes apart in multiples (strides of 8 elements), as the library
+    requires of inputs read through strides."""
+    if t.is_contiguous():
+        return None
+    st = t.stride()
+    if st[3] != 1 and t.shape[3] > 1:
+        raise ValueError(f"the last dimension (d) must be contiguous; strides {st}")
+    if any(x < 0 or x % 8 for x in st[:3]) or t.data_ptr() % 16:
+        raise ValueError(f"strides {st[:3]} must be non-negative multiples of 8 elements, "
+                         "from a 16-byte aligned start")
+    return sage_strides(st[0], st[1], st[2])
+
+
+def _check_inputs(ref: torch.Tensor, *ts) -> None:
+    """Q, K, V: on ref's GPU, contiguous or readable through their strides."""
+    for t in ts:
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError(f"tensors must be on {ref.device}")
+        _strides(t)
+
+
+def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out=None, strided: bool = False) -> None:
     """Q [B, Hq, N, d], K and V [B, Hkv, N, d] of one dtype, out FP32 of Q's
-    shape, all contiguous on one GPU."""
+    shape, all contiguous on one GPU; with `strided`, Q, K and V may instead
+    have their d elements contiguous and row strides of 8 elements (the calls
+    that read them through their strides)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("Q, K, V must be 4-D [B, H, N, d]")
     if k.shape != v.shape or (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]):
@@ -154,7 +192,11 @@ def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out=None) -> N
         raise TypeError(f"Q, K, V must share one dtype; got {q.dtype}, {k.dtype}, {v.dtype}")
     if out is not None and (out.shape != q.shape or out.dtype != torch.float32):
         raise ValueError(f"out must be float32 of shape {tuple(q.shape)}")
-    _check_device(q, k, v, out)
+    if strided:
+        _check_inputs(q, q, k, v)
+        _check_device(q, out)
+    else:
+        _check_device(q, k, v, out)
 
 
 def _check_out(ref: torch.Tensor, out: torch.Tensor, shape) -> None:
@@ -199,10 +241,16 @@ def sage_workspace_carve(workspace: torch.Tensor | int | None, ws_bytes: int, B:
 
 def sage_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dst: sage_qkv_quant,
                   stream=None) -> None:
-    _check_qkv(q, k, v)
+    _check_qkv(q, k, v, strided=True)
     B, Hq, Hkv, N, d = _shape(q, k)
-    _check(_lib.sage_quantize(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, N, d,
-                              ctypes.byref(dst), _stream(stream)))
+    st = [_strides(t) for t in (q, k, v)]
+    if all(x is None for x in st):
+        _check(_lib.sage_quantize(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, N, d,
+                                  ctypes.byref(dst), _stream(stream)))
+    else:
+        _check(_lib.sage_quantize_strided(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, N, d,
+                                          *(None if x is None else ctypes.byref(x) for x in st),
+                                          ctypes.byref(dst), _stream(stream)))
 
 
 def sage_attn_fwd_quantized(src: sage_qkv_quant, out: torch.Tensor, B: int, Hq: int, Hkv: int,
@@ -237,12 +285,20 @@ def sage_attn_fwd_granular(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ou
 def sage_attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                      causal: bool, sm_scale: float, opts: sage_options, workspace: torch.Tensor,
                      stream=None) -> None:
-    _check_qkv(q, k, v, out)
+    _check_qkv(q, k, v, out, strided=True)
     _check_device(q, workspace)
     B, Hq, Hkv, N, d = _shape(q, k)
-    _check(_lib.sage_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, int(causal),
-                                 float(sm_scale), _dtype_code(q), ctypes.byref(opts), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    st = [_strides(t) for t in (q, k, v)]
+    if all(x is None for x in st):
+        _check(_lib.sage_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, int(causal),
+                                     float(sm_scale), _dtype_code(q), ctypes.byref(opts), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+    else:
+        _check(_lib.sage_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, int(causal),
+                                          float(sm_scale), _dtype_code(q), ctypes.byref(opts),
+                                          *(None if x is None else ctypes.byref(x) for x in st),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
 
 
 def sage_kv_cache_bytes(B: int, Hkv: int, Nk: int, d: int, pv: str = "e4m3") -> int:
@@ -321,13 +377,15 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
          sm_scale: float | None = None, workspace: torch.Tensor | None = None,
          granularity: str = "block", pv: str = "e4m3", qk_bits: int = 8) -> torch.Tensor:
     """Drop-in attention: [B,Hq,N,d] fp16/bf16 Q and [B,Hkv,N,d] K,V on the GPU
-    -> FP32 [B,Hq,N,d], on the current stream.  granularity: "block" (one Q
+    -> FP32 [B,Hq,N,d], on the current stream.  Q, K and V may be views, e.g.
+    the transpose(1, 2) of [B,N,H,d] tensors: they are read through their
+    strides, not copied.  granularity: "block" (one Q
     scale per 128 rows, one K scale per 64 keys), "thread" (per row, per 32
     keys) or "token" (per row, per key); pv: "e4m3" (FP8 P and V) or "f16" (binary16 P and V); qk_bits: 8
     (INT8 Q, K) or 4 (INT4-valued codes on the INT8 matrix core, an accuracy option)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
-    _check_qkv(q, k, v)
+    _check_qkv(q, k, v, strided=True)
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = workspace_for(q, k)

@@ -155,7 +155,7 @@ __device__ inline void store_v_tile(const void* vt, void* dst, int tid) {
 // ------------------------------------------------------------ Q
 // Work-group qb codes 128 rows of a q head; one scale per bq rows (128 or 1).
 // rmax and gmax are 128 floats of LDS each.
-template <typename In, int D>
+template <typename In, int D, bool STR>
 __device__ inline void q_rows(const uint16_t* __restrict__ q, const Shape& s, int bq, float qmax,
                               int8_t* __restrict__ q_i8, float* __restrict__ q_scale, int qb,
                               float* rmax, float* gmax) {
@@ -166,7 +166,9 @@ __device__ inline void q_rows(const uint16_t* __restrict__ q, const Shape& s, in
     const int nwg = s.Np / R;
     // rows [t*R, t*R+R) of head bh; rows >= N are zero padding
     const int bh = qb / nwg, t = qb % nwg;
-    const long long src_head = (long long)bh * s.N * D;
+    // (STR: Q read through its strides; otherwise contiguous, with constant offsets)
+    const long long src_head = STR ? Shape::head_start(s.qs, bh, s.Hq) : (long long)bh * s.N * D;
+    const long long qn = STR ? s.qs.n : D;
     const long long dst_head = (long long)bh * s.Np * D;
     // all of this thread's loads first (rows past N read row N-1 and are
     // zeroed), so they are in flight together
@@ -175,7 +177,7 @@ __device__ inline void q_rows(const uint16_t* __restrict__ q, const Shape& s, in
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
         const int row = min(t * R + e / CPR, s.N - 1), col = (e % CPR) * 8;
-        u[c] = *reinterpret_cast<const uint4*>(q + src_head + (long long)row * D + col);
+        u[c] = *reinterpret_cast<const uint4*>(q + src_head + (long long)row * qn + col);
     }
     // The values are unpacked twice (for the absmax, then for the codes)
     // rather than kept as floats across the group maximum: at d = 128 that
@@ -222,7 +224,7 @@ struct StatsSmem {
     int last;
 };
 
-template <typename In, int D>
+template <typename In, int D, bool STR>
 __device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                 const Shape& s, double* __restrict__ k_part,
                                 float* __restrict__ v_part, int* __restrict__ cnt,
@@ -237,7 +239,20 @@ __device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* 
     const int nchunk = s.part_chunks();
     const int bg = wg / nchunk, chunk = wg % nchunk;
     const int cg = tid % CPR, rr = tid / CPR;
+    // contiguous inputs: one offset serves K and V; otherwise each its own
     const long long head = (long long)bg * s.N * D;
+    const long long khead = STR ? Shape::head_start(s.ks, bg, s.Hkv) + cg * 8 : 0;
+    const long long vhead = STR ? Shape::head_start(s.vs, bg, s.Hkv) + cg * 8 : 0;
+    auto kv_load = [&](long long row, uint4& kk, uint4* vv) {
+        if constexpr (STR) {
+            kk = *reinterpret_cast<const uint4*>(k + khead + row * s.ks.n);
+            if (vv) *vv = *reinterpret_cast<const uint4*>(v + vhead + row * s.vs.n);
+        } else {
+            const long long off = head + row * D + cg * 8;
+            kk = *reinterpret_cast<const uint4*>(k + off);
+            if (vv) *vv = *reinterpret_cast<const uint4*>(v + off);
+        }
+    };
     const int r0 = chunk * kStatRows;
     const int r1 = min(s.N, r0 + kStatRows);
     double sum[8];
@@ -254,11 +269,7 @@ __device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* 
     for (; r + (U - 1) * RPI < r1; r += U * RPI) {
         uint4 uk[U], uv[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const long long off = head + (long long)(r + j * RPI) * D + cg * 8;
-            uk[j] = *reinterpret_cast<const uint4*>(k + off);
-            if (!pv16) uv[j] = *reinterpret_cast<const uint4*>(v + off);
-        }
+        for (int j = 0; j < U; ++j) kv_load(r + j * RPI, uk[j], pv16 ? nullptr : &uv[j]);
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             float fk[8];
@@ -274,14 +285,15 @@ __device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* 
         }
     }
     for (; r < r1; r += RPI) {
-        const long long off = head + (long long)r * D + cg * 8;
+        uint4 uk1, uv1;
+        kv_load(r, uk1, pv16 ? nullptr : &uv1);
         float fk[8];
-        unpack8<In>(*reinterpret_cast<const uint4*>(k + off), fk);
+        unpack8<In>(uk1, fk);
 #pragma unroll
         for (int i = 0; i < 8; ++i) sum[i] += (double)fk[i];
         if (!pv16) {
             float fv[8];
-            unpack8<In>(*reinterpret_cast<const uint4*>(v + off), fv);
+            unpack8<In>(uv1, fv);
 #pragma unroll
             for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(fv[i]));
         }
@@ -371,7 +383,7 @@ __device__ inline void kv_stats(const uint16_t* __restrict__ k, const uint16_t* 
 // so they overlap.  Work-groups [0, nstats) take the statistics (the longer
 // ones, dispatched first), the rest the Q row blocks (nq of them, 0 for a KV
 // cache).  The arrival counters are cleared by clear_words beforehand.
-template <typename In, int D>
+template <typename In, int D, bool STR>
 __global__ __launch_bounds__(kThreads) void prep_qstats(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     Shape s, int bq, float qmax, int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
@@ -382,12 +394,12 @@ __global__ __launch_bounds__(kThreads) void prep_qstats(
     const int nstats = s.B * s.Hkv * s.part_chunks();
     const int wg = blockIdx.x;
     if (wg < nstats)
-        kv_stats<In, D>(k, v, s, k_part, v_part, cnt, k_mean, v_scale, v_inv, pv16, wg, stats_smem);
+        kv_stats<In, D, STR>(k, v, s, k_part, v_part, cnt, k_mean, v_scale, v_inv, pv16, wg, stats_smem);
     else
-        q_rows<In, D>(q, s, bq, qmax, q_i8, q_scale, wg - nstats, rmax, gmax);
+        q_rows<In, D, STR>(q, s, bq, qmax, q_i8, q_scale, wg - nstats, rmax, gmax);
 }
 
-template <typename In, int D>
+template <typename In, int D, bool STR>
 __global__ __launch_bounds__(kThreads) void prep_pack(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Shape s, int bk, float qmax,
     const float* __restrict__ k_mean, const float* __restrict__ v_inv,
@@ -402,20 +414,21 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
     // reverse head order relative to the statistics
     const int bg = s.B * s.Hkv - 1 - (int)(blockIdx.x / per_head);
     const int j = blockIdx.x % per_head;
-    const long long src_head = (long long)bg * s.N * D;
 
     if (j < nkb) {
         // K rows [t*64, t*64+64): smoothed, one scale per bk rows (64 or 32)
         const int t = j;
         constexpr int R = 64;
         constexpr int NCH = R * CPR / kThreads;
+        const long long src_head = STR ? Shape::head_start(s.ks, bg, s.Hkv) : (long long)bg * s.N * D;
+        const long long kn = STR ? s.ks.n : D;
         const long long dst_head = (long long)bg * s.Np * D;
         uint4 u[NCH];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int e = tid + c * kThreads;
             const int row = min(t * R + e / CPR, s.N - 1), col = (e % CPR) * 8;
-            u[c] = *reinterpret_cast<const uint4*>(k + src_head + (long long)row * D + col);
+            u[c] = *reinterpret_cast<const uint4*>(k + src_head + (long long)row * kn + col);
         }
         // a thread's column is the same in every chunk (kThreads % CPR == 0)
         float mean[8];
@@ -469,12 +482,14 @@ __global__ __launch_bounds__(kThreads) void prep_pack(
         inv[0] = i0.x, inv[1] = i0.y, inv[2] = i0.z, inv[3] = i0.w;
         inv[4] = i1.x, inv[5] = i1.y, inv[6] = i1.z, inv[7] = i1.w;
     }
+    const long long src_head = STR ? Shape::head_start(s.vs, bg, s.Hkv) : (long long)bg * s.N * D;
+    const long long vn = STR ? s.vs.n : D;
     uint4 u[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = tid + c * kThreads;
         const int row = min(T * SAGE_BN + e / CPRV, s.N - 1), col = c0 + (e % CPRV) * 8;
-        u[c] = *reinterpret_cast<const uint4*>(v + src_head + (long long)row * D + col);
+        u[c] = *reinterpret_cast<const uint4*>(v + src_head + (long long)row * vn + col);
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -512,25 +527,42 @@ __global__ __launch_bounds__(kThreads) void clear_words(int* __restrict__ w, int
 // ------------------------------------------------------------ launchers
 // Counter clearing, then the statistics with the Q codes of nq row blocks
 // (none for a KV cache), then the K and V codes.
-template <typename In, int D>
-static hipError_t launch_prep_all(const void* q, const void* k, const void* v, const Shape& s,
-                                  int nq, int bq, float qmax, int8_t* q_i8, float* q_scale,
-                                  const KVViews& z, hipStream_t st) {
+template <typename In, int D, bool STR>
+static hipError_t launch_prep_s(const void* q, const void* k, const void* v, const Shape& s,
+                                int nq, int bq, float qmax, int8_t* q_i8, float* q_scale,
+                                const KVViews& z, hipStream_t st) {
     hipLaunchKernelGGL(clear_words, dim3(1), dim3(kThreads), 0, st, z.sync, sync_words(s));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nstats = s.B * s.Hkv * s.part_chunks();
     const int pv16 = z.v_store == kVF16;
-    hipLaunchKernelGGL((prep_qstats<In, D>), dim3(nstats + nq), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((prep_qstats<In, D, STR>), dim3(nstats + nq), dim3(kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, bq, qmax, q_i8,
                        q_scale, z.k_part, z.v_part, z.sync, z.k_mean, z.v_scale, z.v_inv, pv16);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int per_head = s.Np / 64 + s.Np / SAGE_BN * (D / pack_v_channels<D>());
-    hipLaunchKernelGGL((prep_pack<In, D>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((prep_pack<In, D, STR>), dim3(s.B * s.Hkv * per_head), dim3(kThreads), 0, st,
                        (const uint16_t*)k, (const uint16_t*)v, s, z.k_block, z.qmax, z.k_mean, z.v_inv,
                        z.k_i8, z.k_scale, z.v, z.v_store);
     return hipGetLastError();
+}
+
+static bool is_contiguous(const InStrides& st, int H, int N, int d) {
+    const InStrides c = contiguous_strides(H, N, d);
+    return st.b == c.b && st.h == c.h && st.n == c.n;
+}
+
+// The kernels with constant offsets when every input is contiguous, else the
+// ones that read through the strides.
+template <typename In, int D>
+static hipError_t launch_prep_all(const void* q, const void* k, const void* v, const Shape& s,
+                                  int nq, int bq, float qmax, int8_t* q_i8, float* q_scale,
+                                  const KVViews& z, hipStream_t st) {
+    const bool contiguous = (nq == 0 || is_contiguous(s.qs, s.Hq, s.N, s.d)) &&
+                            is_contiguous(s.ks, s.Hkv, s.N, s.d) && is_contiguous(s.vs, s.Hkv, s.N, s.d);
+    return contiguous ? launch_prep_s<In, D, false>(q, k, v, s, nq, bq, qmax, q_i8, q_scale, z, st)
+                      : launch_prep_s<In, D, true>(q, k, v, s, nq, bq, qmax, q_i8, q_scale, z, st);
 }
 
 template <typename In, int D>

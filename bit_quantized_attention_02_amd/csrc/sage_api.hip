@@ -233,18 +233,43 @@ int sage_workspace_carve(void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int 
     return SAGE_OK;
 }
 
-int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
-                  int N, int d, const sage_qkv_quant* dst, void* stream) {
+// An input layout from the caller's strides (NULL: contiguous).  Every row
+// must start 16 bytes apart from the base in multiples (the prep step reads
+// 16-byte pieces), so each stride is a non-negative multiple of 8 elements.
+static bool take_strides(const sage_strides* st, sage::InStrides* out) {
+    if (!st) return true;
+    if (st->b < 0 || st->h < 0 || st->n < 0 || st->b % 8 || st->h % 8 || st->n % 8) return false;
+    *out = sage::InStrides{st->b, st->h, st->n};
+    return true;
+}
+
+static int quantize_impl(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
+                         int N, int d, const sage_strides* qst, const sage_strides* kst,
+                         const sage_strides* vst, const sage_qkv_quant* dst, void* stream) {
     int rc = check_shape(B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
     if (!q || !k || !v || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
         return SAGE_ERR_INVALID_ARG;
+    Shape s = sage::make_shape(B, Hq, Hkv, N, d);
+    if (!take_strides(qst, &s.qs) || !take_strides(kst, &s.ks) || !take_strides(vst, &s.vs))
+        return SAGE_ERR_INVALID_ARG;
     rc = check_quant(dst, B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
-    const Shape s = sage::make_shape(B, Hq, Hkv, N, d);
     hipError_t e = sage::launch_prep(q, k, v, dtype, s, dst, (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_quantize(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
+                  int N, int d, const sage_qkv_quant* dst, void* stream) {
+    return quantize_impl(q, k, v, dtype, B, Hq, Hkv, N, d, nullptr, nullptr, nullptr, dst, stream);
+}
+
+int sage_quantize_strided(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                          int Hkv, int N, int d, const sage_strides* q_strides,
+                          const sage_strides* k_strides, const sage_strides* v_strides,
+                          const sage_qkv_quant* dst, void* stream) {
+    return quantize_impl(q, k, v, dtype, B, Hq, Hkv, N, d, q_strides, k_strides, v_strides, dst, stream);
 }
 
 int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq, int Hkv, int N,
@@ -266,9 +291,10 @@ int sage_attn_fwd_quantized(const sage_qkv_quant* src, float* out, int B, int Hq
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
-int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
-                     int N, int d, int causal, float sm_scale, int dtype, const sage_options* opts,
-                     void* workspace, size_t ws_bytes, void* stream) {
+static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                         int N, int d, int causal, float sm_scale, int dtype, const sage_options* opts,
+                         const sage_strides* qst, const sage_strides* kst, const sage_strides* vst,
+                         void* workspace, size_t ws_bytes, void* stream) {
     int rc = check_shape(B, Hq, Hkv, N, d);
     if (rc != SAGE_OK) return rc;
     if (!opts) return SAGE_ERR_INVALID_ARG;
@@ -288,9 +314,25 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, in
     z.k_block = opts->k_block;
     z.pv_format = opts->pv_format;
     z.qk_bits = opts->qk_bits;
-    rc = sage_quantize(q, k, v, dtype, B, Hq, Hkv, N, d, &z, stream);
+    rc = quantize_impl(q, k, v, dtype, B, Hq, Hkv, N, d, qst, kst, vst, &z, stream);
     if (rc != SAGE_OK) return rc;
     return sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, causal, sm_scale, stream);
+}
+
+int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                     int N, int d, int causal, float sm_scale, int dtype, const sage_options* opts,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, N, d, causal, sm_scale, dtype, opts, nullptr, nullptr,
+                         nullptr, workspace, ws_bytes, stream);
+}
+
+int sage_attn_fwd_strided(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                          int Hkv, int N, int d, int causal, float sm_scale, int dtype,
+                          const sage_options* opts, const sage_strides* q_strides,
+                          const sage_strides* k_strides, const sage_strides* v_strides,
+                          void* workspace, size_t ws_bytes, void* stream) {
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, N, d, causal, sm_scale, dtype, opts, q_strides, k_strides,
+                         v_strides, workspace, ws_bytes, stream);
 }
 
 int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* out, int B, int Hq,

@@ -15,17 +15,35 @@ constexpr int kThreads = 256;      // prep kernels run 4 waves of 64
 constexpr int kStatRows = 512;     // rows per partial-statistics chunk of the prep step
 constexpr int kVersion = 101;
 
+// Element strides (batch, head, token) of an fp16/bf16 input whose d elements
+// are contiguous; the prep step reads Q, K and V through them.
+struct InStrides {
+    long long b, h, n;
+};
+
 struct Shape {
     int B, Hq, Hkv, N, d;
     int Np;       // N rounded up to SAGE_NPAD
+    InStrides qs, ks, vs;  // input layouts (contiguous [B, H, N, d] by default)
     long long q_elems() const { return (long long)B * Hq * Np * d; }
     long long kv_elems() const { return (long long)B * Hkv * Np * d; }
     __host__ __device__ int part_chunks() const { return (N + kStatRows - 1) / kStatRows; }
+    // where head bh (b * H + h) of an input with H heads starts
+    __host__ __device__ static long long head_start(const InStrides& st, int bh, int H) {
+        return (long long)(bh / H) * st.b + (long long)(bh % H) * st.h;
+    }
 };
 
+inline InStrides contiguous_strides(int H, int N, int d) {
+    return InStrides{(long long)H * N * d, (long long)N * d, d};
+}
+
 inline Shape make_shape(int B, int Hq, int Hkv, int N, int d) {
-    Shape s{B, Hq, Hkv, N, d, 0};
+    Shape s{B, Hq, Hkv, N, d, 0, {}, {}, {}};
     s.Np = (N + SAGE_NPAD - 1) / SAGE_NPAD * SAGE_NPAD;
+    s.qs = contiguous_strides(Hq, N, d);
+    s.ks = contiguous_strides(Hkv, N, d);
+    s.vs = s.ks;
     return s;
 }
 

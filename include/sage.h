@@ -61,7 +61,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or keeps them.  Tensors are contiguous
- *     [B, H, N, d] with d innermost; Q has Hq heads, K and V have Hkv heads,
+ *     [B, H, N, d] with d innermost (the *_strided entry points also read
+ *     Q, K, V in other layouts); Q has Hq heads, K and V have Hkv heads,
  *     query head h reads kv head h / (Hq/Hkv).
  *   - Q, K, V and out must be 16-byte aligned; the workspace 256-byte aligned.
  *   - Supported: d in {64, 128}; N >= 1; B, Hq, Hkv >= 1; Hq % Hkv == 0;
@@ -244,6 +245,43 @@ int sage_attn_fwd_granular(const void* q, const void* k, const void* v, float* o
 int sage_attn_fwd_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                      int N, int d, int causal, float sm_scale, int dtype, const sage_options* opts,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * ---- Inputs in other layouts.  A model's attention operands often come as
+ * [B, N, H, d] (heads after tokens) or as views into one packed QKV tensor;
+ * the operator that replaces its attention (the SageAttention article's
+ * plug-and-play replacement) can read them where they lie instead of having
+ * them copied into [B, H, N, d] first.
+ *
+ * sage_strides: the element strides (batch, head, token) of an fp16/bf16
+ * [B, H, N, d] tensor whose d elements are contiguous.  [B, H, N, d] itself
+ * is {H*N*d, N*d, d}; a [B, N, H, d] tensor is {N*H*d, d, H*d}.  Each
+ * stride must be a non-negative multiple of 8 (every row starts 16-byte
+ * aligned, as the base pointer must be), else SAGE_ERR_INVALID_ARG.  The
+ * library reads element (b, h, n, c) at base + b*s.b + h*s.h + n*s.n + c and
+ * nothing else; the caller guarantees those elements lie in its allocation.
+ * A NULL stride pointer means the contiguous layout.  The output stays FP32
+ * [B, Hq, N, d], contiguous.
+ */
+typedef struct {
+    long long b, h, n;
+} sage_strides;
+
+/* sage_quantize with Q, K and V read through their strides.  The workspace
+ * contents equal sage_quantize's on the same values, byte for byte. */
+int sage_quantize_strided(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                          int Hkv, int N, int d, const sage_strides* q_strides,
+                          const sage_strides* k_strides, const sage_strides* v_strides,
+                          const sage_qkv_quant* dst, void* stream);
+
+/* sage_attn_fwd_ex with Q, K and V read through their strides (opts must not
+ * be NULL).  The output equals sage_attn_fwd_ex's on the same values, bit for
+ * bit. */
+int sage_attn_fwd_strided(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                          int Hkv, int N, int d, int causal, float sm_scale, int dtype,
+                          const sage_options* opts, const sage_strides* q_strides,
+                          const sage_strides* k_strides, const sage_strides* v_strides,
+                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * ---- Short queries against a quantized KV cache (decode).

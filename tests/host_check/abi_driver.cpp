@@ -131,6 +131,29 @@ int main() {
         bad.v16 = nullptr;
         EXPECT(sage_quantize(fake, fake, fake, SAGE_F16, B, Hq, Hkv, N, d, &bad, nullptr) < 0);
     }
+    // ---- strided inputs: bad strides in each slot, and the contiguous calls' checks
+    {
+        const sage_strides bad[] = {{4, 64, 256}, {8, 12, 256}, {-8, 64, 256}, {8, 64, 260}, {1LL << 40 | 4, 64, 256}};
+        const sage_strides good = {(long long)N * Hq * d, d, (long long)Hq * d};
+        sage_options o = {SAGE_BQ, SAGE_BK, SAGE_PV_E4M3, SAGE_QK_INT8};
+        for (const auto& b : bad)
+            for (int slot = 0; slot < 3; ++slot) {
+                const sage_strides* st[3] = {nullptr, nullptr, nullptr};
+                st[slot] = &b;
+                EXPECT(sage_quantize_strided(fake, fake, fake, SAGE_F16, B, Hq, Hkv, N, d, st[0], st[1], st[2], &z,
+                                             nullptr) == SAGE_ERR_INVALID_ARG);
+                EXPECT(sage_attn_fwd_strided(fake, fake, fake, out, B, Hq, Hkv, N, d, 0, sm, SAGE_F16, &o, st[0],
+                                             st[1], st[2], fake, need, nullptr) == SAGE_ERR_INVALID_ARG);
+            }
+        EXPECT(sage_quantize_strided(nullptr, fake, fake, SAGE_F16, B, Hq, Hkv, N, d, &good, nullptr, nullptr, &z,
+                                     nullptr) < 0);
+        EXPECT(sage_quantize_strided(fake, fake, fake, SAGE_F16, B, Hq, Hkv, N, d, &good, nullptr, nullptr,
+                                     nullptr, nullptr) < 0);
+        EXPECT(sage_attn_fwd_strided(fake, fake, fake, out, B, Hq, Hkv, N, d, 0, sm, SAGE_F16, nullptr, &good,
+                                     nullptr, nullptr, fake, need, nullptr) < 0);
+        EXPECT(sage_attn_fwd_strided(fake, fake, fake, nullptr, B, Hq, Hkv, N, d, 0, sm, SAGE_F16, &o, &good,
+                                     &good, nullptr, fake, need, nullptr) < 0);
+    }
     EXPECT(sage_attn_fwd_quantized(nullptr, out, B, Hq, Hkv, N, d, 0, sm, nullptr) < 0);
     EXPECT(sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, -1, sm, nullptr) < 0);
     EXPECT(sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, 0, -1.0f, nullptr) < 0);

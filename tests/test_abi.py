@@ -151,6 +151,54 @@ def test_entry_points_reject_bad_arguments_before_any_hip_call(sage):
     assert L.sage_get_config(None) == sage.SAGE_ERR_INVALID_ARG
 
 
+def test_strided_entry_points_validate_strides_on_the_host(sage):
+    """sage_quantize_strided and sage_attn_fwd_strided take NULL (contiguous)
+    or non-negative strides in multiples of 8 elements; anything else, and the
+    checks the contiguous calls make, return before any HIP call."""
+    import torch
+    L = sage._lib
+    fake = 1 << 40
+    shape = (1, 4, 2, 300, 64)
+    need = sage.sage_workspace_bytes(*shape)
+    rc, z = _carve(sage, fake, need, shape)
+    assert rc == 0
+    zp = ctypes.byref(z)
+    S, f = sage.sage_strides, ctypes.c_float
+    opts = sage.options("block", "e4m3", 8)
+    bad_strides = (S(4, 64, 256), S(8, 12, 256), S(-8, 64, 256), S(8, 64, 260), S(1 << 40 | 4, 64, 256))
+    for bad in bad_strides:
+        for slot in range(3):
+            st = [None, None, None]
+            st[slot] = ctypes.byref(bad)
+            assert L.sage_quantize_strided(fake, fake, fake, 0, 1, 4, 2, 300, 64, *st, zp, None) == \
+                sage.SAGE_ERR_INVALID_ARG
+            assert L.sage_attn_fwd_strided(fake, fake, fake, fake, 1, 4, 2, 300, 64, 0, f(0.125), 0,
+                                           ctypes.byref(opts), *st, fake, need, None) == sage.SAGE_ERR_INVALID_ARG
+    good = ctypes.byref(S(300 * 4 * 64, 64, 4 * 64))
+    assert L.sage_quantize_strided(None, fake, fake, 0, 1, 4, 2, 300, 64, good, None, None, zp, None) == \
+        sage.SAGE_ERR_INVALID_ARG
+    assert L.sage_quantize_strided(fake, fake, fake, 7, 1, 4, 2, 300, 64, good, None, None, zp, None) == \
+        sage.SAGE_ERR_INVALID_ARG
+    assert L.sage_quantize_strided(fake, fake, fake, 0, 1, 4, 2, 300, 96, good, None, None, zp, None) == \
+        sage.SAGE_ERR_UNSUPPORTED
+    assert L.sage_quantize_strided(fake, fake, fake, 0, 1, 4, 2, 300, 64, good, None, None, None, None) == \
+        sage.SAGE_ERR_INVALID_ARG
+    assert L.sage_attn_fwd_strided(fake, fake, fake, fake, 1, 4, 2, 300, 64, 0, f(0.125), 0, None, good,
+                                   None, None, fake, need, None) == sage.SAGE_ERR_INVALID_ARG
+    assert L.sage_attn_fwd_strided(fake, fake, fake, fake, 1, 4, 2, 300, 64, 0, f(0.125), 0,
+                                   ctypes.byref(opts), good, None, None, fake, need - 256, None) == \
+        sage.SAGE_ERR_WORKSPACE
+    # the binding derives the strides from a tensor view, or refuses it
+    x = torch.zeros(2, 16, 8, 64, dtype=torch.float16)  # [B, N, H, d]
+    st = sage._strides(x.transpose(1, 2))
+    assert (st.b, st.h, st.n) == (16 * 8 * 64, 64, 8 * 64)
+    assert sage._strides(x) is None
+    with pytest.raises(ValueError):  # d not contiguous
+        sage._strides(torch.zeros(2, 4, 64, 16, dtype=torch.float16).transpose(2, 3))
+    with pytest.raises(ValueError):  # rows 68 elements apart
+        sage._strides(torch.zeros(2, 4, 16, 68, dtype=torch.float16)[..., :64])
+
+
 def test_granularity_is_validated(sage):
     """Only (128, 64) and (1, 32) are accepted, by the struct-taking calls and
     by sage_attn_fwd_granular; both fit the same workspace."""
