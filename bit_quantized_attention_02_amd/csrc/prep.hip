@@ -25,6 +25,10 @@
 //               visited in the reverse order of the statistics so the second
 //               read of K and V finds the most recent heads still in the
 //               last-level cache.
+// Q, K and V are read as contiguous [B, H, N, d] with constant offsets, or,
+// when the caller passes other strides (a [B, N, H, d] tensor, a slice of a
+// packed QKV tensor), through those strides: a template flag on the kernels,
+// so the contiguous case keeps its offset arithmetic and registers.
 #include "sage_internal.h"
 
 namespace sage {
