@@ -89,6 +89,8 @@ _lib.sage_kv_cache_bytes.restype = _S
 _lib.sage_kv_cache_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.sage_kv_cache_carve.argtypes = [_P, _S, _I, _I, _I, _I, _I, _I, ctypes.POINTER(sage_kv_cache)]
 _lib.sage_kv_quantize.argtypes = [_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(sage_kv_cache), _P]
+_lib.sage_kv_quantize_strided.argtypes = [_P, _P, _I, _I, _I, _I, _I, _SP, _SP, ctypes.POINTER(sage_kv_cache),
+                                          _P]
 _lib.sage_decode_workspace_bytes.restype = _S
 _lib.sage_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.sage_attn_decode.argtypes = [_P, _I, ctypes.POINTER(sage_kv_cache), _P, _I, _I, _I, _I, _I, _I,
@@ -103,7 +105,7 @@ _lib.sage_status_string.argtypes = [_I]
 EXPORTED = ["sage_workspace_bytes", "sage_workspace_carve", "sage_quantize",
             "sage_attn_fwd_quantized", "sage_attn_fwd", "sage_attn_fwd_granular", "sage_attn_fwd_ex",
             "sage_quantize_strided", "sage_attn_fwd_strided",
-            "sage_kv_cache_bytes", "sage_kv_cache_carve", "sage_kv_quantize",
+            "sage_kv_cache_bytes", "sage_kv_cache_carve", "sage_kv_quantize", "sage_kv_quantize_strided",
             "sage_decode_workspace_bytes", "sage_attn_decode", "sage_attn_decode_noalloc", "sage_get_config",
             "sage_v_key_position", "sage_status_string"]
 
@@ -317,12 +319,20 @@ def sage_kv_cache_carve(buf: torch.Tensor | int | None, nbytes: int, B: int, Hkv
 
 
 def sage_kv_quantize(k: torch.Tensor, v: torch.Tensor, cache: sage_kv_cache, stream=None) -> None:
+    """K and V contiguous, or views read through their strides (e.g. a
+    [B, Nk, Hkv, d] cache seen as [B, Hkv, Nk, d])."""
     if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
         raise ValueError("K and V must be [B, Hkv, Nk, d] of one shape and dtype")
-    _check_device(k, k, v)
+    _check_inputs(k, k, v)
     B, Hkv, Nk, d = k.shape
-    _check(_lib.sage_kv_quantize(_ptr(k), _ptr(v), _dtype_code(k), B, Hkv, Nk, d, ctypes.byref(cache),
-                                 _stream(stream)))
+    st = [_strides(t) for t in (k, v)]
+    if all(x is None for x in st):
+        _check(_lib.sage_kv_quantize(_ptr(k), _ptr(v), _dtype_code(k), B, Hkv, Nk, d, ctypes.byref(cache),
+                                     _stream(stream)))
+    else:
+        _check(_lib.sage_kv_quantize_strided(_ptr(k), _ptr(v), _dtype_code(k), B, Hkv, Nk, d,
+                                             *(None if x is None else ctypes.byref(x) for x in st),
+                                             ctypes.byref(cache), _stream(stream)))
 
 
 def sage_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
@@ -401,7 +411,7 @@ class KVCache:
                  pv: str = "e4m3", stream=None):
         if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
             raise ValueError("K and V must be [B, Hkv, Nk, d] of one shape and dtype")
-        _check_device(k, k, v)
+        _check_inputs(k, k, v)
         self.B, self.Hkv, self.Nk, self.d = k.shape
         nbytes = sage_kv_cache_bytes(self.B, self.Hkv, self.Nk, self.d, pv)
         if nbytes == 0:

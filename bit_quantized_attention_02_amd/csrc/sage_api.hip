@@ -384,15 +384,17 @@ int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, 
     return SAGE_OK;
 }
 
-int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
-                     const sage_kv_cache* cache, void* stream) {
+static int kv_quantize_impl(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
+                            const sage_strides* kst, const sage_strides* vst, const sage_kv_cache* cache,
+                            void* stream) {
     int rc = check_shape(B, Hkv, Hkv, Nk, d);
     if (rc != SAGE_OK) return rc;
     if (dtype != SAGE_F16 && dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARG;
     if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return SAGE_ERR_INVALID_ARG;
+    Shape s = sage::make_shape(B, Hkv, Hkv, Nk, d);
+    if (!take_strides(kst, &s.ks) || !take_strides(vst, &s.vs)) return SAGE_ERR_INVALID_ARG;
     rc = check_cache(cache, B, Hkv, Nk, d);
     if (rc != SAGE_OK) return rc;
-    const Shape s = sage::make_shape(B, Hkv, Hkv, Nk, d);
     const sage::KVViews kv = {cache->k_i8,   cache->k_scale, cache->k_mean, cache->v,
                               cache->v_scale, cache->v_inv,  cache->k_part, cache->v_part,
                               cache->sync,   cache->k_block,
@@ -400,6 +402,17 @@ int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, in
                               127.0f};
     hipError_t e = sage::launch_prep_kv(k, v, dtype, s, kv, (hipStream_t)stream);
     return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
+                     const sage_kv_cache* cache, void* stream) {
+    return kv_quantize_impl(k, v, dtype, B, Hkv, Nk, d, nullptr, nullptr, cache, stream);
+}
+
+int sage_kv_quantize_strided(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
+                             const sage_strides* k_strides, const sage_strides* v_strides,
+                             const sage_kv_cache* cache, void* stream) {
+    return kv_quantize_impl(k, v, dtype, B, Hkv, Nk, d, k_strides, v_strides, cache, stream);
 }
 
 size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {

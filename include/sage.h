@@ -341,6 +341,13 @@ int sage_kv_cache_carve(void* buf, size_t bytes, int B, int Hkv, int Nk, int d, 
 int sage_kv_quantize(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
                      const sage_kv_cache* cache, void* stream);
 
+/* sage_kv_quantize with K and V read through their strides (sage_strides;
+ * NULL: contiguous), e.g. a cache kept as [B, Nk, Hkv, d].  The cache bytes
+ * equal sage_kv_quantize's on the same values. */
+int sage_kv_quantize_strided(const void* k, const void* v, int dtype, int B, int Hkv, int Nk, int d,
+                             const sage_strides* k_strides, const sage_strides* v_strides,
+                             const sage_kv_cache* cache, void* stream);
+
 /* Workspace bytes sage_attn_decode needs for this shape (at least 256; 0 when
  * the shape is invalid). */
 size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);

@@ -153,6 +153,18 @@ int main() {
                                      nullptr, nullptr, fake, need, nullptr) < 0);
         EXPECT(sage_attn_fwd_strided(fake, fake, fake, nullptr, B, Hq, Hkv, N, d, 0, sm, SAGE_F16, &o, &good,
                                      &good, nullptr, fake, need, nullptr) < 0);
+        // a KV cache from strided K, V: bad strides, and a cache not carved for the shape
+        const size_t cneed = sage_kv_cache_bytes(B, Hkv, N, d, SAGE_PV_E4M3);
+        sage_kv_cache kc;
+        EXPECT(sage_kv_cache_carve(fake, cneed, B, Hkv, N, d, SAGE_BK, SAGE_PV_E4M3, &kc) == SAGE_OK);
+        for (const auto& b : bad) {
+            EXPECT(sage_kv_quantize_strided(fake, fake, SAGE_F16, B, Hkv, N, d, &b, nullptr, &kc, nullptr) ==
+                   SAGE_ERR_INVALID_ARG);
+            EXPECT(sage_kv_quantize_strided(fake, fake, SAGE_F16, B, Hkv, N, d, nullptr, &b, &kc, nullptr) ==
+                   SAGE_ERR_INVALID_ARG);
+        }
+        EXPECT(sage_kv_quantize_strided(fake, fake, SAGE_F16, B, Hkv, N + 1, d, &good, &good, &kc, nullptr) < 0);
+        EXPECT(sage_kv_quantize_strided(fake, fake, SAGE_F16, B, Hkv, N, d, &good, &good, nullptr, nullptr) < 0);
     }
     EXPECT(sage_attn_fwd_quantized(nullptr, out, B, Hq, Hkv, N, d, 0, sm, nullptr) < 0);
     EXPECT(sage_attn_fwd_quantized(&z, out, B, Hq, Hkv, N, d, -1, sm, nullptr) < 0);

@@ -188,6 +188,19 @@ def test_strided_entry_points_validate_strides_on_the_host(sage):
     assert L.sage_attn_fwd_strided(fake, fake, fake, fake, 1, 4, 2, 300, 64, 0, f(0.125), 0,
                                    ctypes.byref(opts), good, None, None, fake, need - 256, None) == \
         sage.SAGE_ERR_WORKSPACE
+    # sage_kv_quantize_strided: the same stride rule for K and V
+    kneed = sage.sage_kv_cache_bytes(1, 2, 300, 64)
+    kz = sage.sage_kv_cache_carve(fake, kneed, 1, 2, 300, 64)
+    for bad in bad_strides:
+        assert L.sage_kv_quantize_strided(fake, fake, 0, 1, 2, 300, 64, ctypes.byref(bad), None, ctypes.byref(kz),
+                                          None) == sage.SAGE_ERR_INVALID_ARG
+        assert L.sage_kv_quantize_strided(fake, fake, 0, 1, 2, 300, 64, None, ctypes.byref(bad), ctypes.byref(kz),
+                                          None) == sage.SAGE_ERR_INVALID_ARG
+    kgood = ctypes.byref(S(300 * 2 * 64, 64, 2 * 64))
+    assert L.sage_kv_quantize_strided(fake, None, 0, 1, 2, 300, 64, kgood, kgood, ctypes.byref(kz), None) == \
+        sage.SAGE_ERR_INVALID_ARG
+    assert L.sage_kv_quantize_strided(fake, fake, 0, 1, 2, 301, 64, kgood, kgood, ctypes.byref(kz), None) == \
+        sage.SAGE_ERR_INVALID_ARG  # not the shape the cache was carved for
     # the binding derives the strides from a tensor view, or refuses it
     x = torch.zeros(2, 16, 8, 64, dtype=torch.float16)  # [B, N, H, d]
     st = sage._strides(x.transpose(1, 2))

@@ -109,3 +109,28 @@ def test_workload_shape_through_views(sage):
         sage.sage_attn_fwd_ex(qv, kv, vv, out, w.causal, w.sm_scale, opts, ws2)
     side.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_kv_cache_from_views(sage):
+    """A KV cache built from [B, Nk, Hkv, d] views holds the bytes of one built
+    from contiguous copies, and short queries against both agree bit for bit."""
+    B, Hq, Hkv, Nk, Nq, d = 2, 8, 2, 3000, 3, 128
+    _say(f"case KV cache from views: B={B} Hq={Hq} Hkv={Hkv} Nk={Nk} Nq={Nq} d={d}")
+    q, k, v = (t.cuda() for t in workloads.random_inputs(B, Hq, Hkv, Nk, d, "bf16", seed=91, scale=1.5))
+    q = q[:, :, -Nq:].contiguous()
+    a = sage.KVCache(k, v)
+    b = sage.KVCache(_bnhd_view(k), _bnhd_view(v))
+    torch.cuda.synchronize()
+    Np = -(-Nk // sage.SAGE_NPAD) * sage.SAGE_NPAD
+
+    def region(c, name, nbytes):  # one carved array of the cache, as bytes
+        off = getattr(c.z, name) - c.buf.data_ptr()
+        return c.buf[off:off + nbytes]
+    for name, nbytes in (("k_i8", B * Hkv * Np * d), ("k_scale", B * Hkv * (Np // 64) * 4),
+                         ("k_mean", B * Hkv * d * 4), ("v", B * Hkv * Np * d), ("v_scale", B * Hkv * d * 4)):
+        assert torch.equal(region(a, name, nbytes), region(b, name, nbytes)), name
+    sm = 1 / math.sqrt(d)
+    oa = a.attend(q, causal=True, sm_scale=sm)
+    ob = b.attend(q, causal=True, sm_scale=sm)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
