@@ -327,16 +327,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES_PER_SIMD) void attn_fwd(AttnArgs 
 
 // d = 64: 4-wave work-groups (48 KB of LDS each) whose waves interleave on
 // each SIMD: three per CU (168 registers a wave) for the non-causal
-// per-block granularity, whose loop fits those registers without spilling;
-// two per CU (half the register file) otherwise.  d = 128: one 8-wave
-// work-group per CU (96 KB of LDS), two waves per SIMD.
+// per-block and thread-level granularities, whose loops fit those registers
+// (the thread-level one reloads two spilled registers per block); two per CU
+// (half the register file) otherwise.  d = 128: one 8-wave work-group per CU
+// (96 KB of LDS), two waves per SIMD.
 template <int D>
 constexpr int attn_waves() {
     return D == 64 ? 4 : 8;
 }
 template <int D, int KSPLIT, bool CAUSAL>
 constexpr int attn_waves_per_simd() {
-    return D == 64 && KSPLIT == 2 && !CAUSAL ? 3 : 2;
+    return D == 64 && (KSPLIT == 2 || KSPLIT == 4) && !CAUSAL ? 3 : 2;
 }
 
 // Combines the key-split shares of the last partial round's tiles: per query
