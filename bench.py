@@ -33,8 +33,10 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default 50; 2000 with --decode, whose 20-30 us steps need that many "
+                        "for the timed window to outlast the clock's ramp)")
+    p.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 5; 200 with --decode)")
     p.add_argument("--workload", type=int, default=3,
                    help="1..5; 3 is the non-causal N=17550 video-diffusion shape")
     p.add_argument("--granularity", choices=("block", "thread", "token"), default="block",
@@ -330,6 +332,10 @@ def bench_decode(args, sage, workloads, torch):
 
 def main():
     args = parse()
+    if args.steps is None:
+        args.steps = 2000 if args.decode else 50
+    if args.warmup is None:
+        args.warmup = 200 if args.decode else 5
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
